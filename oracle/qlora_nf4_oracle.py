@@ -1,0 +1,401 @@
+"""CPU oracle for the frozen-NF4 linear layer with a LoRA adapter.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this module.  It shares no code, table or constant with the HIP library: the
+NF4 levels, the decision thresholds, the 8-bit float codec and the bf16
+rounding are all derived here from their definitions.
+
+Everything is plain NumPy.  Floating-point steps whose rounding is part of the
+method (the codes and the dequantised weights must match bit for bit) are done
+in float32 exactly as the step states it; the matrix products of the forward
+and backward pass are done in float64 on the exact values of the bf16 inputs.
+
+Sources (titles of the pages this follows; sections named in each function):
+  [PL]  "QLoRA — 650億パラメータのモデルをGPU 1枚で微調整する" (ta-paperlens)
+  [WZ]  LLM book, chapter 26 "LoRA/QLoRA" (waylandz.com)
+  [HF]  "Hugging Face 4ビット量子化とQLoRAリリース" (agentlenshq)
+  [UL]  Ultralytics glossary "QLoRA" (German edition)
+
+Readings where the pages are silent (each is listed in the design doc):
+  * blocks are 64 consecutive elements of the row-major [rows, cols] weight;
+  * the code is the nearest level to RN32(w / c) in exact arithmetic, ties to
+    the lower index; an all-zero block gets code 7 (the level 0);
+  * two codes per byte, element 2i in the low nibble;
+  * double quantisation: one mean mu per tensor (fixed float64 pairwise tree),
+    d = RN32(c - mu), s2 = max |d| per group of 256 blocks, code8 = OCP E4M3
+    round-to-nearest-even of RN32(d / s2) * 256;
+  * dequantisation: c' = RN32(RN32(e4m3(code8) * 2^-8 * s2) + mu),
+    w_hat = bf16_RNE(RN32(q[code] * c')).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import ndtri
+
+BLOCK = 64          # weights per absmax block   [PL] 量子化を1段落で
+DQ_GROUP = 256      # block constants per second-level constant   [PL] 二重量子化
+NF4_ZERO_CODE = 7   # index of the exact 0 level
+
+F32 = np.float32
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# NF4 codebook
+# --------------------------------------------------------------------------
+def nf4_levels() -> np.ndarray:
+    """The 16 NF4 levels as float32, ascending.
+
+    [UL] code example under "So funktioniert QLoRA": eight positive levels are
+    the standard-normal quantiles at 8 evenly spaced probabilities from
+    0.9677083 toward 0.5 (0.5 excluded), seven negative levels are the negated
+    quantiles at 7 evenly spaced probabilities over the same range, an exact 0
+    is added, and the sorted set is divided by its largest value.  [PL] NF4
+    section: dense near zero, an exact zero, endpoints exactly -1 and +1.
+    Evaluated in float64, rounded once to float32.
+    """
+    p_pos = np.linspace(0.9677083, 0.5, 9)[:-1]
+    p_neg = np.linspace(0.9677083, 0.5, 8)[:-1]
+    levels = np.concatenate([-ndtri(p_neg), [0.0], ndtri(p_pos)])
+    levels = np.sort(levels)
+    levels = levels / levels.max()
+    return levels.astype(F32)
+
+
+def nf4_midpoints(levels: np.ndarray | None = None) -> np.ndarray:
+    """Exact midpoints between neighbouring levels, float64 (15 values).
+
+    The sum of two float32 numbers of similar magnitude and the halving are
+    exact in float64, so these are the real-number decision boundaries of the
+    nearest-level rule ([PL] 量子化を1段落で: store the index of the nearest level).
+    """
+    q = (nf4_levels() if levels is None else levels).astype(F64)
+    return (q[:-1] + q[1:]) / 2.0
+
+
+# --------------------------------------------------------------------------
+# (a1) block absmax, (a2) nearest-level encode and packing
+# --------------------------------------------------------------------------
+def block_absmax(w: np.ndarray) -> np.ndarray:
+    """c_b = max |w_i| over each block of 64 consecutive row-major elements.
+
+    [PL] 量子化を1段落で (one high-precision constant per block of 64, the
+    largest absolute value in the block); [UL] code example (one scale per row
+    of 64).  Returns float32 [n / 64].
+    """
+    w = np.asarray(w, dtype=F32).reshape(-1, BLOCK)
+    return np.abs(w).max(axis=1)
+
+
+def nf4_encode(w: np.ndarray, c: np.ndarray, levels: np.ndarray | None = None,
+               chunk_blocks: int = 1 << 16) -> np.ndarray:
+    """NF4 code of every element, uint8 in [0, 15], one per element.
+
+    [PL] 量子化を1段落で: each value is stored as the index of the level nearest
+    to w / c.  The quotient is the float32 IEEE quotient RN32(w / c); the code
+    is the number of exact midpoints strictly below it, i.e. the nearest level
+    with ties going to the lower index.  A block whose constant is 0 holds
+    only zeros and gets the zero level.  Rows are processed in chunks only to
+    bound memory; every element is independent.
+    """
+    w = np.asarray(w, dtype=F32).reshape(-1, BLOCK)
+    c = np.asarray(c, dtype=F32).reshape(-1)
+    mids = nf4_midpoints(levels)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    for s in range(0, w.shape[0], chunk_blocks):
+        wb = w[s:s + chunk_blocks]
+        cb = c[s:s + chunk_blocks]
+        zero = cb == 0
+        safe_c = np.where(zero, F32(1.0), cb).astype(F32)
+        r = (wb / safe_c[:, None]).astype(F32)        # float32 IEEE division
+        r64 = r.astype(F64)
+        code = np.zeros(r.shape, dtype=np.uint8)
+        for m in mids:
+            code += (r64 > F64(m))
+        code[zero] = NF4_ZERO_CODE
+        codes[s:s + chunk_blocks] = code
+    return codes.reshape(-1)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte, element 2i in the low nibble.
+
+    [WZ] 26.6.3: NF4 is kept as 4-bit integers, half a byte per weight.  The
+    order inside the byte is not given on the pages.
+    """
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    assert codes.size % 2 == 0
+    return (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    out = np.empty(packed.size * 2, dtype=np.uint8)
+    out[0::2] = packed & 0x0F
+    out[1::2] = packed >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# (a3) mean of the block constants, (a4) 8-bit float codes per group of 256
+# --------------------------------------------------------------------------
+def pairwise_tree_sum(x: np.ndarray) -> float:
+    """Perfect binary tree of float64 additions over x in index order.
+
+    The input is zero-padded to the next power of two; level by level,
+    element 2j and element 2j+1 are added.  Fixes the rounding order of the
+    mean so that it is reproducible.
+    """
+    v = np.asarray(x, dtype=F64).reshape(-1)
+    if v.size == 0:
+        return 0.0
+    size = 1
+    while size < v.size:
+        size *= 2
+    v = np.concatenate([v, np.zeros(size - v.size, dtype=F64)])
+    while v.size > 1:
+        v = v[0::2] + v[1::2]
+    return float(v[0])
+
+
+def dq_mean(c: np.ndarray) -> np.float32:
+    """mu = RN32(RN64(S / n_b)), S the pairwise tree sum of all constants.
+
+    [PL] 二重量子化, last paragraph: the constants are all positive, so their
+    mean is subtracted before they are quantised to a symmetric 8-bit float.
+    One mean per tensor (the pages do not say per what).
+    """
+    c = np.asarray(c, dtype=F32).reshape(-1)
+    s = pairwise_tree_sum(c)
+    return F32(F64(s) / F64(c.size))
+
+
+def e4m3_value(code: int) -> float:
+    """Real value of an OCP FP8 E4M3 bit pattern (float64, exact); NaN for 0x7F/0xFF.
+
+    Format: 1 sign bit, 4 exponent bits with bias 7, 3 fraction bits; exponent
+    field 0 is subnormal (fraction * 2^-9); 0x7F and 0xFF are NaN; no infinity.
+    """
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0x0F
+    m = code & 0x07
+    if e == 0x0F and m == 0x07:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# the 127 finite non-negative E4M3 values, in code order (which is value order)
+_E4M3_POS = np.array([e4m3_value(k) for k in range(0x7F)], dtype=F64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Vector decode of E4M3 bit patterns to float64 (exact)."""
+    table = np.array([e4m3_value(k) for k in range(256)], dtype=F64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode_rne(x: np.ndarray) -> np.ndarray:
+    """E4M3 bit pattern nearest to each float32 x, ties to the even pattern.
+
+    The nearest finite E4M3 magnitude is found among all 127 of them; on an
+    exact tie the pattern with an even last bit wins (round to nearest even).
+    The sign bit is copied, so -0 and tiny negatives give 0x80.  Inputs must
+    satisfy |x| <= 448 (no saturation or NaN handling is needed here).
+    """
+    x = np.asarray(x, dtype=F32)
+    a = np.abs(x).astype(F64)
+    assert np.all(a <= 448.0), "E4M3 encode: |x| > 448 is out of range"
+    hi = np.searchsorted(_E4M3_POS, a, side="left")      # first value >= a
+    hi = np.minimum(hi, _E4M3_POS.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag = np.where(pick_hi, hi, lo)
+    mag = np.where(_E4M3_POS[hi] == a, hi, mag)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (mag | sign).astype(np.uint8)
+
+
+def double_quantize(c: np.ndarray):
+    """Second-level quantisation of the float32 block constants.
+
+    [PL] 二重量子化: the float32 constants are taken in groups of 256, stored as
+    8-bit floats, with one float32 second-level constant per group, after the
+    mean has been subtracted.  [UL] "Doppelte Quantisierung": 8 bits per block
+    constant in blocks of 256.
+
+    Returns (code8 uint8 [n_b], s2 float32 [n_g], mu float32).
+    """
+    c = np.asarray(c, dtype=F32).reshape(-1)
+    n_b = c.size
+    mu = dq_mean(c)
+    d = (c - mu).astype(F32)                        # RN32(c - mu)
+    n_g = (n_b + DQ_GROUP - 1) // DQ_GROUP
+    s2 = np.zeros(n_g, dtype=F32)
+    code8 = np.zeros(n_b, dtype=np.uint8)
+    for g in range(n_g):
+        dg = d[g * DQ_GROUP:(g + 1) * DQ_GROUP]
+        s = np.abs(dg).max()
+        s2[g] = s
+        if s == 0:
+            code8[g * DQ_GROUP:(g + 1) * DQ_GROUP] = 0x00
+            continue
+        t = (dg / s).astype(F32)                    # RN32(d / s2), in [-1, 1]
+        code8[g * DQ_GROUP:(g + 1) * DQ_GROUP] = e4m3_encode_rne(t * F32(256.0))
+    return code8, s2, mu
+
+
+def block_constants_from_dq(code8: np.ndarray, s2: np.ndarray, mu) -> np.ndarray:
+    """c'_b = RN32(RN32(e4m3(code8_b) * 2^-8 * s2_g) + mu), float32 [n_b].
+
+    Inverse of double_quantize: e4m3 * 2^-8 is exact in float32; the product
+    with s2 and the sum with mu are each rounded once (no fused multiply-add).
+    """
+    code8 = np.asarray(code8, dtype=np.uint8).reshape(-1)
+    s2 = np.asarray(s2, dtype=F32).reshape(-1)
+    g = np.arange(code8.size) // DQ_GROUP
+    scaled = (e4m3_decode(code8) * 2.0 ** -8).astype(F32)
+    prod = (scaled * s2[g]).astype(F32)
+    return (prod + F32(mu)).astype(F32)
+
+
+# --------------------------------------------------------------------------
+# bf16 round to nearest even
+# --------------------------------------------------------------------------
+def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) nearest to each finite float32, ties to even.
+
+    bf16 keeps the upper 16 bits of the float32 pattern; the discarded lower
+    half decides: above half goes up, below goes down, exactly half goes to
+    the pattern whose last kept bit is 0.
+    """
+    u = np.asarray(x, dtype=F32).view(np.uint32)
+    keep = u >> np.uint32(16)
+    rest = u & np.uint32(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & 1) == 1))
+    return (keep + up.astype(np.uint32)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
+
+
+# --------------------------------------------------------------------------
+# (a1-a5) quantise and dequantise a weight
+# --------------------------------------------------------------------------
+def quantize(w: np.ndarray) -> dict:
+    """Full NF4 + double quantisation of a float32 [rows, cols] weight.
+
+    The NF4 codes are taken against the original float32 block constants; the
+    8-bit constant codes are what is stored ([PL] order of presentation:
+    blockwise NF4 first, then the constants are quantised).
+    """
+    w = np.asarray(w, dtype=F32)
+    rows, cols = w.shape
+    assert cols % BLOCK == 0, "cols must be a multiple of 64"
+    c = block_absmax(w)
+    codes = nf4_encode(w, c)
+    code8, s2, mu = double_quantize(c)
+    return {
+        "rows": rows, "cols": cols,
+        "codes": pack_nibbles(codes),
+        "absmax_code": code8,
+        "absmax_scale": s2,
+        "absmax_offset": np.array([mu], dtype=F32),
+        "absmax_fp32": c,
+    }
+
+
+def dequantize_bits(state: dict) -> np.ndarray:
+    """bf16 bit patterns of the dequantised weight, uint16 [rows, cols].
+
+    [PL] 量子化を1段落で: restore by table lookup and multiply, x_hat = c * q[index];
+    [PL] 勾配は実際どこへ行くのか: the storage type is NF4, compute is bf16.
+    """
+    rows, cols = state["rows"], state["cols"]
+    q = nf4_levels()
+    codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
+    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
+                                     state["absmax_offset"][0])
+    prod = (q[codes] * cprime[:, None]).astype(F32)
+    return bf16_bits_rne(prod).reshape(rows, cols)
+
+
+def dequantize(state: dict) -> np.ndarray:
+    """Dequantised weight as float64 values of the bf16 results."""
+    return bf16_bits_to_f32(dequantize_bits(state)).astype(F64)
+
+
+def storage_bits_per_param(rows: int, cols: int) -> float:
+    """Bytes of the packed state * 8 / number of weights.
+
+    [PL] 二重量子化: 4 bits per code, 8 bits per 64 weights, 32 bits per
+    64*256 weights; plus one float32 mean per tensor (this build's reading).
+    """
+    n = rows * cols
+    n_b = n // BLOCK
+    n_g = (n_b + DQ_GROUP - 1) // DQ_GROUP
+    nbytes = n // 2 + n_b + 4 * n_g + 4
+    return nbytes * 8.0 / n
+
+
+# --------------------------------------------------------------------------
+# (a6-a11) LoRA linear layer, forward and backward, float64
+# --------------------------------------------------------------------------
+def linear_forward(x: np.ndarray, w_hat: np.ndarray, a: np.ndarray, b: np.ndarray,
+                   alpha: float, r: int):
+    """Y = X W^T + (alpha/r) (X A^T) B^T, float64.
+
+    [PL] 勾配は実際どこへ行くのか: h = dequant(W_NF4) x + B A x in bf16;
+    [WZ] 26.2.4: the adapter term is scaled by alpha / r.  Rows of X are
+    tokens, W is [out, in] like nn.Linear, A is [r, in], B is [out, r]
+    ([WZ] 26.2.1 shapes).  Returns (Y, U) with U = X A^T.
+    """
+    x = np.asarray(x, dtype=F64)
+    s = F64(alpha) / F64(r)
+    u = x @ np.asarray(a, dtype=F64).T
+    y = x @ np.asarray(w_hat, dtype=F64).T + s * (u @ np.asarray(b, dtype=F64).T)
+    return y, u
+
+
+def linear_backward(x: np.ndarray, dy: np.ndarray, w_hat: np.ndarray, a: np.ndarray,
+                    b: np.ndarray, alpha: float, r: int):
+    """Gradients of L = <dY, Y> for the layer above: dX, dA, dB; no dW.
+
+    [PL] 勾配は実際どこへ行くのか: the input gradient passes through the
+    dequantised W^T; only A and B receive gradients; W is never written.
+      G  = dY B
+      dX = dY W_hat + s G A
+      dA = s G^T X
+      dB = s dY^T (X A^T)
+    """
+    x = np.asarray(x, dtype=F64)
+    dy = np.asarray(dy, dtype=F64)
+    a = np.asarray(a, dtype=F64)
+    b = np.asarray(b, dtype=F64)
+    s = F64(alpha) / F64(r)
+    g = dy @ b
+    dx = dy @ np.asarray(w_hat, dtype=F64) + s * (g @ a)
+    da = s * (g.T @ x)
+    db = s * (dy.T @ (x @ a.T))
+    return dx, da, db
+
+
+def lora_param_count(d: int, k: int, r: int) -> int:
+    """Trainable numbers of one adapter, r (d + k).  [PL] 前提: LoRAの低ランク更新."""
+    return r * (d + k)
+
+
+def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_F / ||ref||_F in float64."""
+    got = np.asarray(got, dtype=F64)
+    ref = np.asarray(ref, dtype=F64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    return float(num / den) if den > 0 else float(num)
