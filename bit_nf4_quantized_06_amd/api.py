@@ -1,0 +1,186 @@
+"""Python binding of the C ABI, one function per entry point, same names.
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's
+kernels.  bf16 tensors are passed as their bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+@dataclass
+class NF4Weight:
+    """Packed NF4 weight: the four device buffers of qlora_nf4_weight."""
+    rows: int
+    cols: int
+    codes: torch.Tensor          # uint8 [rows * cols / 2]
+    absmax_code: torch.Tensor    # uint8 [n_b]     (E4M3 bit patterns)
+    absmax_scale: torch.Tensor   # float32 [n_g]
+    absmax_offset: torch.Tensor  # float32 [1]
+
+    @staticmethod
+    def empty(rows: int, cols: int, device=None) -> "NF4Weight":
+        lib = _lib.load()
+        sizes = [ctypes.c_size_t() for _ in range(4)]
+        _lib.check("qlora_nf4_buffer_sizes",
+                   lib.qlora_nf4_buffer_sizes(rows, cols, *[ctypes.byref(s) for s in sizes]))
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        return NF4Weight(
+            rows, cols,
+            torch.empty(sizes[0].value, dtype=torch.uint8, device=device),
+            torch.empty(sizes[1].value, dtype=torch.uint8, device=device),
+            torch.empty(sizes[2].value // 4, dtype=torch.float32, device=device),
+            torch.empty(1, dtype=torch.float32, device=device),
+        )
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def descriptor(self) -> _lib.Nf4WeightDesc:
+        lib = _lib.load()
+        d = _lib.Nf4WeightDesc()
+        _lib.check("qlora_nf4_weight_init", lib.qlora_nf4_weight_init(ctypes.byref(d), self.rows,
+                                                                       self.cols))
+        d.codes = self.codes.data_ptr()
+        d.absmax_code = self.absmax_code.data_ptr()
+        d.absmax_scale = self.absmax_scale.data_ptr()
+        d.absmax_offset = self.absmax_offset.data_ptr()
+        return d
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensor -> same storage viewed as int16 bit patterns."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def qlora_nf4_quantize(W: torch.Tensor, out: NF4Weight | None = None,
+                       workspace: torch.Tensor | None = None, stream=None) -> NF4Weight:
+    """NF4 + double quantisation of a float32 [rows, cols] weight (qlora_nf4_quantize)."""
+    lib = _lib.load()
+    rows, cols = W.shape
+    if out is None:
+        out = NF4Weight.empty(rows, cols, W.device)
+    _need(W, "W", torch.float32, (rows, cols), out.device)
+    ws_bytes = lib.qlora_nf4_quantize_workspace(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=W.device)
+    desc = out.descriptor()
+    _lib.check("qlora_nf4_quantize",
+               lib.qlora_nf4_quantize(W.data_ptr(), ctypes.byref(desc), workspace.data_ptr(),
+                                      workspace.numel(), _stream(stream)))
+    return out
+
+
+def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [rows, cols] dequantised weight (qlora_nf4_dequantize)."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device)
+    _need(out, "out", torch.bfloat16, (w.rows, w.cols), w.device)
+    desc = w.descriptor()
+    _lib.check("qlora_nf4_dequantize",
+               lib.qlora_nf4_dequantize(ctypes.byref(desc), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
+    return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
+
+
+def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                     alpha: float, Y: torch.Tensor | None = None,
+                     U_save: torch.Tensor | None = None, save_u: bool = True,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """Y = X dequant(W)^T + (alpha/r) (X A^T) B^T (qlora_linear_fwd).
+
+    Returns (Y, U) with U = X A^T in bf16 (None when save_u is False and no
+    U_save buffer is given).
+    """
+    lib = _lib.load()
+    T, K = X.shape
+    r = A.shape[0]
+    dev = w.device
+    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
+    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
+    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    if Y is None:
+        Y = torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
+    _need(Y, "Y", torch.bfloat16, (T, w.rows), dev)
+    if U_save is None and save_u:
+        U_save = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+    if U_save is not None:
+        _need(U_save, "U_save", torch.bfloat16, (T, r), dev)
+    ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 0)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    desc = w.descriptor()
+    _lib.check("qlora_linear_fwd",
+               lib.qlora_linear_fwd(ctypes.byref(desc), X.data_ptr(), T, A.data_ptr(),
+                                    B.data_ptr(), r, float(alpha), Y.data_ptr(), _ptr(U_save),
+                                    workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return Y, U_save
+
+
+def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, alpha: float, U_saved: torch.Tensor | None = None,
+                     dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                     dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     stream=None):
+    """dX (bf16), dA and dB (float32) of the layer; no dW (qlora_linear_bwd)."""
+    lib = _lib.load()
+    T = X.shape[0]
+    r = A.shape[0]
+    dev = w.device
+    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
+    _need(dY, "dY", torch.bfloat16, (T, w.rows), dev)
+    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
+    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    if U_saved is not None:
+        _need(U_saved, "U_saved", torch.bfloat16, (T, r), dev)
+    if dX is None:
+        dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty(r, w.cols, dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty(w.rows, r, dtype=torch.float32, device=dev)
+    _need(dX, "dX", torch.bfloat16, (T, w.cols), dev)
+    _need(dA, "dA", torch.float32, (r, w.cols), dev)
+    _need(dB, "dB", torch.float32, (w.rows, r), dev)
+    ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    desc = w.descriptor()
+    _lib.check("qlora_linear_bwd",
+               lib.qlora_linear_bwd(ctypes.byref(desc), X.data_ptr(), dY.data_ptr(), T,
+                                    A.data_ptr(), B.data_ptr(), r, float(alpha), _ptr(U_saved),
+                                    dX.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dX, dA, dB

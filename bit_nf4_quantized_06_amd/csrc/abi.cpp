@@ -1,0 +1,195 @@
+// C ABI entry points: validate on the host, then enqueue the gfx950 kernels on
+// the caller's stream.  No allocation, no synchronisation, no retained state
+// other than a per-device "is gfx950" cache.
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "abi_internal.h"
+#include "kernels.h"
+#include "qlora_nf4.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+qlora_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return QLORA_ERR_HIP;
+}
+
+qlora_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? QLORA_OK : QLORA_ERR_DEVICE;
+}
+
+template <typename T>
+T* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+qlora_status qlora_nf4_quantize(const float* W, const qlora_nf4_weight* out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_descriptor(out, &d);
+  if (s != QLORA_OK) return s;
+  if (!W || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  const QuantWs L = quant_ws_layout(d);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const hipError_t e = launch_quantize(W, d.n_b, out->codes, out->absmax_code, out->absmax_scale,
+                                       out->absmax_offset, ws_ptr<float>(ws, L.cblk_off),
+                                       ws_ptr<double>(ws, L.gpart_off),
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_descriptor(w, &d);
+  if (s != QLORA_OK) return s;
+  if (!W_bf16) return QLORA_ERR_NULL;
+  if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const hipError_t e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale,
+                                         w->absmax_offset, d.n, W_bf16,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                              uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
+                              void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_linear_args(w, T, r, alpha, &d);
+  if (s != QLORA_OK) return s;
+  if (!X || !A || !B || !Y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
+      (U_save && !aligned16(U_save)))
+    return QLORA_ERR_ALIGN;
+  const LinearWs L = linear_ws_layout(T, d, r, false);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  uint16_t* U = U_save ? U_save : ws_ptr<uint16_t>(ws, L.u_off);
+  float* P = ws_ptr<float>(ws, L.proj_off);
+  hipError_t e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
+  if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, U, nullptr, 0, st);
+  if (e == hipSuccess) {
+    GemmArgs g;
+    g.act = X;
+    g.codes = w->codes;
+    g.code8 = w->absmax_code;
+    g.s2 = w->absmax_scale;
+    g.mu = w->absmax_offset;
+    g.rows = d.rows;
+    g.cols = d.cols;
+    g.lora_l = U;
+    g.lora_r = B;
+    g.r = r;
+    g.scale = alpha / (float)r;
+    g.out = Y;
+    g.T = T;
+    e = launch_qlora_fwd_gemm(g, st);
+  }
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
+                              int64_t T, const uint16_t* A, const uint16_t* B, int32_t r,
+                              float alpha, const uint16_t* U_saved, uint16_t* dX, float* dA,
+                              float* dB, void* ws, size_t ws_bytes, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_linear_args(w, T, r, alpha, &d);
+  if (s != QLORA_OK) return s;
+  if (!X || !dY || !A || !B || !dX || !dA || !dB || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
+      !aligned16(dA) || !aligned16(dB) || !aligned16(ws) || (U_saved && !aligned16(U_saved)))
+    return QLORA_ERR_ALIGN;
+  const LinearWs L = linear_ws_layout(T, d, r, true);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
+
+  uint16_t* Bt = ws_ptr<uint16_t>(ws, L.bt_off);    // [r, rows]
+  uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
+  uint16_t* G = ws_ptr<uint16_t>(ws, L.g_off);      // [T, r]
+  uint16_t* Gt = ws_ptr<uint16_t>(ws, L.gt_off);    // [r, t_pad]
+  uint16_t* Ut = ws_ptr<uint16_t>(ws, L.ut_off);    // [r, t_pad]
+  float* P = ws_ptr<float>(ws, L.proj_off);
+  float* PG = ws_ptr<float>(ws, L.grad_off);
+
+  hipError_t e = launch_transpose_bf16(B, d.rows, r, Bt, d.rows, st);
+  if (e == hipSuccess) e = launch_transpose_bf16(A, r, d.cols, At, r, st);
+  // G = dY B  (and G^T for dA)
+  if (e == hipSuccess) e = launch_lora_proj_partial(dY, Bt, T, d.rows, r, L.s_proj_dy, P, st);
+  if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_dy, G, Gt, L.t_pad, st);
+  // U^T for dB: from the forward's U, or recomputed as X A^T
+  if (e == hipSuccess) {
+    if (U_saved) {
+      e = launch_transpose_bf16(U_saved, T, r, Ut, L.t_pad, st);
+    } else {
+      e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
+      if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, Ut, L.t_pad, st);
+    }
+  }
+  // dX = dY dequant(W) + s G A
+  if (e == hipSuccess) {
+    GemmArgs g;
+    g.act = dY;
+    g.codes = w->codes;
+    g.code8 = w->absmax_code;
+    g.s2 = w->absmax_scale;
+    g.mu = w->absmax_offset;
+    g.rows = d.rows;
+    g.cols = d.cols;
+    g.lora_l = G;
+    g.lora_r = At;
+    g.r = r;
+    g.scale = scale;
+    g.out = dX;
+    g.T = T;
+    e = launch_qlora_dx_gemm(g, st);
+  }
+  // dA = s G^T X ; dB = s (U^T dY)^T
+  if (e == hipSuccess) e = launch_lora_grad_partial(Gt, L.t_pad, X, T, d.cols, r, L.s_grad_a, PG, st);
+  if (e == hipSuccess) e = launch_lora_grad_reduce(PG, r, d.cols, L.s_grad_a, scale, 0, dA, st);
+  if (e == hipSuccess) e = launch_lora_grad_partial(Ut, L.t_pad, dY, T, d.rows, r, L.s_grad_b, PG, st);
+  if (e == hipSuccess) e = launch_lora_grad_reduce(PG, r, d.rows, L.s_grad_b, scale, 1, dB, st);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the gfx950
+// kernels.  Every launcher only enqueues work on `stream` and returns the
+// launch status; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace qlora {
+
+// --- bulk path (quantize.hip) ---------------------------------------------
+hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t* code8,
+                           float* s2, float* mu, float* cblk, double* gpart,
+                           hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* code8, const float* s2,
+                             const float* mu, int64_t n, uint16_t* out, hipStream_t stream);
+
+// --- fused dequant GEMMs (gemm.hip) ---------------------------------------
+// out[T, out_len] = act[T, red_len] * Wop + s * lora_l[T, r] * lora_r[out_len, r]^T
+// where Wop = dequant(W)^T (forward: red = cols, out = rows) or dequant(W)
+// (backward dX: red = rows, out = cols).
+struct GemmArgs {
+  const uint16_t* act;     // [T, red_len] bf16
+  const uint8_t* codes;    // packed weight [rows, cols]
+  const uint8_t* code8;
+  const float* s2;
+  const float* mu;
+  int64_t rows, cols;
+  const uint16_t* lora_l;  // [T, r] bf16
+  const uint16_t* lora_r;  // [out_len, r] bf16
+  int32_t r;
+  float scale;
+  uint16_t* out;           // [T, out_len] bf16
+  int64_t T;
+};
+hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
+
+// --- LoRA side products (lora.hip) ----------------------------------------
+// Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k],
+// L [T, red] bf16, R [r, red] bf16, P float32 [S][T][r].
+int lora_proj_splits(int64_t T, int64_t red);
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_t T,
+                                    int64_t red, int32_t r, int splits, float* P,
+                                    hipStream_t stream);
+// out_rm[t][p] = bf16(sum_s P) (if not NULL), out_tr[p][t] likewise with
+// row stride ld_tr and zeros for T <= t < ld_tr (if not NULL).
+hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
+                                   uint16_t* out_rm, uint16_t* out_tr, int64_t ld_tr,
+                                   hipStream_t stream);
+// out[c][r'] = in[r'][c] for a [R, C] bf16 matrix; out has row stride ld_out
+// and is zero for R <= r' < ld_out.
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t R, int64_t C, uint16_t* out,
+                                 int64_t ld_out, hipStream_t stream);
+// Partials C[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q]; St [r, ld_st]
+// bf16 (zero beyond T), L [T, Q] bf16.
+int lora_grad_splits(int64_t T, int64_t Q);
+hipError_t launch_lora_grad_partial(const uint16_t* St, int64_t ld_st, const uint16_t* L,
+                                    int64_t T, int64_t Q, int32_t r, int splits, float* P,
+                                    hipStream_t stream);
+// out = scale * sum_s P[s]: transposed == 0 -> out[p][q] ([r, Q]);
+// transposed != 0 -> out[q][p] ([Q, r]).
+hipError_t launch_lora_grad_reduce(const float* P, int32_t r, int64_t Q, int splits, float scale,
+                                   int transposed, float* out, hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,236 @@
+// Bulk kernels: blockwise NF4 quantisation, double quantisation of the block
+// constants, and dequantisation to bf16 (gfx950).
+//
+// Method: ta-paperlens "QLoRA — 650億パラメータ…", sections 量子化を1段落で
+// (absmax per block of 64, nearest level, restore by lookup and multiply),
+// NF4 (16 normal-quantile levels with an exact 0 and ends at +-1) and
+// 二重量子化 (constants grouped by 256, stored as 8-bit floats with one float32
+// per group, after subtracting their mean); Ultralytics glossary "QLoRA"
+// (levels construction, blocks of 64, blocks of 256).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlora {
+
+// ---------------------------------------------------------------------------
+// Quantise: one workgroup per group of 256 blocks (16384 weights, 64 KB of
+// float32).  A wave owns 64 consecutive blocks; per iteration 8 lanes share
+// a block, each lane reading 8 consecutive weights (2 x 16 B) and writing the
+// 8 packed codes as one 32-bit word.  The block absmax is an 8-lane xor
+// butterfly.  The quotient RN32(w / c) is computed as Markstein's corrected
+// product with the correctly rounded reciprocal of c's significand (one IEEE
+// division per block); with y = RN(1/c) and q0 = RN(w y) within an ulp, the
+// residual w - q0 c is exact and q0 + residual * y rounds to RN(w / c).
+// Scaling both w and c by 2^-e (e = exponent of c) keeps y normal for any
+// finite c, denormals included.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nf4_code(float r, const float* thr) {
+  uint32_t i = (r > thr[7]) ? 8u : 0u;
+  i += (r > thr[i + 3]) ? 4u : 0u;
+  i += (r > thr[i + 1]) ? 2u : 0u;
+  i += (r > thr[i]) ? 1u : 0u;
+  return i;
+}
+
+__global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
+    const float* __restrict__ W, int64_t n_b, uint32_t* __restrict__ codes,
+    float* __restrict__ cblk, double* __restrict__ gpart) {
+  __shared__ float thr[16];
+  __shared__ double wsum[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid < 15) thr[tid] = kNF4Thr[tid];
+  __syncthreads();
+
+  const int64_t blk0 = (int64_t)blockIdx.x * kGroup + wave * 64;
+  const int sub = lane & 7;
+  float c_keep = 0.0f;
+#pragma unroll 2
+  for (int it = 0; it < 8; ++it) {
+    const int64_t b = blk0 + it * 8 + (lane >> 3);
+    const bool valid = b < n_b;
+    float v[8];
+    if (valid) {
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(W + b * kBlock + sub * 8);
+      const f32x4_t x0 = __builtin_nontemporal_load(p);
+      const f32x4_t x1 = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x0[e];
+        v[4 + e] = x1[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+    float m = fabsf(v[0]);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+
+    uint32_t word;
+    if (m == 0.0f) {
+      word = 0x77777777u;                    // all-zero block: the zero level
+    } else {
+      int ex;
+      const float cm = frexpf(m, &ex);       // m = cm * 2^ex, cm in [0.5, 1)
+      const float y = __fdiv_rn(1.0f, cm);
+      word = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wm = ldexpf(v[e], -ex);
+        const float q0 = wm * y;
+        const float rem = fmaf(-q0, cm, wm);
+        const float r = fmaf(rem, y, q0);
+        word |= nf4_code(r, thr) << (4 * e);
+      }
+    }
+    if (valid) codes[b * 8 + sub] = word;
+    if (sub == it) c_keep = m;   // lane l keeps block (l & 7) * 8 + (l >> 3)
+  }
+  // lane j <- block j of this wave
+  const float c = __shfl(c_keep, (lane & 7) * 8 + (lane >> 3));
+  const int64_t bj = blk0 + lane;
+  if (bj < n_b) cblk[bj] = c;
+  // pairwise float64 tree over the wave's 64 consecutive blocks (padding = 0)
+  double s = (bj < n_b) ? (double)c : 0.0;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) s += __shfl_down(s, d);
+  if (lane == 0) wsum[wave] = s;
+  __syncthreads();
+  if (tid == 0) gpart[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Mean of the block constants: perfect binary float64 tree over the group
+// partials (which are its level-8 nodes), zero-padded to a power of two.
+// One workgroup of 1024 threads; thread t first folds an aligned run of
+// `per` leaves with a binary-counter cascade (same tree), then the 1024 run
+// sums are folded pairwise in shared memory.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void dq_mean_kernel(const double* __restrict__ gpart,
+                                                       int64_t n_g, int64_t n_b, int64_t per,
+                                                       float* __restrict__ mu_out) {
+  __shared__ double sh[1024];
+  const int t = threadIdx.x;
+  double stack[40];
+  int sp = 0;
+  for (int64_t i = 0; i < per; ++i) {
+    const int64_t idx = (int64_t)t * per + i;
+    double v = idx < n_g ? gpart[idx] : 0.0;
+    for (int64_t k = i; k & 1; k >>= 1) v = stack[--sp] + v;
+    stack[sp++] = v;
+  }
+  sh[t] = stack[0];
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    if ((t & (2 * d - 1)) == 0) sh[t] = sh[t] + sh[t + d];
+    __syncthreads();
+  }
+  if (t == 0) mu_out[0] = (float)(sh[0] / (double)n_b);
+}
+
+// ---------------------------------------------------------------------------
+// Double-quantisation codes: one workgroup (256 threads) per group.
+// d = RN32(c - mu); s2 = max |d|; code8 = E4M3_RNE(RN32(d / s2) * 256).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ cblk,
+                                                        const float* __restrict__ mu_p,
+                                                        int64_t n_b, uint8_t* __restrict__ code8,
+                                                        float* __restrict__ s2_out) {
+  __shared__ float wmax[4];
+  const int t = threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * kGroup + t;
+  const bool valid = b < n_b;
+  const float mu = mu_p[0];
+  const float d = valid ? __fsub_rn(cblk[b], mu) : 0.0f;
+  float a = fabsf(d);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((t & 63) == 0) wmax[t >> 6] = a;
+  __syncthreads();
+  const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  if (t == 0) s2_out[blockIdx.x] = s2;
+  if (valid) {
+    uint32_t code = 0u;
+    if (s2 > 0.0f) code = e4m3_encode_rne(__fdiv_rn(d, s2) * 256.0f);
+    code8[b] = (uint8_t)code;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantise to bf16: each thread handles 4 words of 8 codes, one wave-stride
+// apart so that every load (4 B per lane) and store (16 B per lane) of a wave
+// is contiguous.  The level is looked up in shared memory, multiplied by the
+// decoded block constant in float32 and rounded once to bf16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
+    const float* __restrict__ s2, const float* __restrict__ mu_p, int64_t n_words,
+    u32x4_t* __restrict__ out) {
+  __shared__ float q[16];
+  if (threadIdx.x < 16) q[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const float mu = mu_p[0];
+  const int64_t base = (int64_t)blockIdx.x * (256 * 4) + threadIdx.x;
+  uint32_t w[4];
+  float cp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + j * 256;
+    w[j] = 0u;
+    cp[j] = 0.0f;
+    if (i < n_words) {
+      w[j] = __builtin_nontemporal_load(codes + i);
+      const int64_t blk = i >> 3;
+      cp[j] = block_constant(code8[blk], s2[blk >> 8], mu);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + j * 256;
+    if (i < n_words) {
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __fmul_rn(q[(w[j] >> (8 * e)) & 15u], cp[j]);
+        const float b = __fmul_rn(q[(w[j] >> (8 * e + 4)) & 15u], cp[j]);
+        o[e] = pack_bf16x2(a, b);
+      }
+      __builtin_nontemporal_store(o, out + i);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t* code8,
+                           float* s2, float* mu, float* cblk, double* gpart,
+                           hipStream_t stream) {
+  const int64_t n_g = (n_b + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(nf4_quantize_blocks_kernel, dim3((unsigned)n_g), dim3(256), 0, stream, W,
+                     n_b, reinterpret_cast<uint32_t*>(codes), cblk, gpart);
+  int64_t pow2 = 1;
+  while (pow2 < n_g) pow2 <<= 1;
+  const int64_t per = pow2 > 1024 ? pow2 / 1024 : 1;
+  hipLaunchKernelGGL(dq_mean_kernel, dim3(1), dim3(1024), 0, stream, gpart, n_g, n_b, per, mu);
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)n_g), dim3(256), 0, stream, cblk, mu, n_b,
+                     code8, s2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* code8, const float* s2,
+                             const float* mu, int64_t n, uint16_t* out, hipStream_t stream) {
+  const int64_t n_words = n / 8;
+  const int64_t grid = (n_words + 1023) / 1024;
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(codes), code8, s2, mu, n_words,
+                     reinterpret_cast<u32x4_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,173 @@
+// Host-only argument validation and workspace layouts of the C ABI.  Pure
+// C++ with no HIP calls, so every error path can be exercised without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "abi_internal.h"
+
+namespace qlora {
+
+// Split counts of the LoRA side reductions: enough workgroups to cover the
+// chip (~512 for the projections, ~256 of 4 waves for the gradients) while
+// keeping the float32 partial buffers small.
+int lora_proj_splits(int64_t T, int64_t red) {
+  const int64_t rb = (T + 63) / 64;
+  int64_t s = (512 + rb - 1) / rb;
+  const int64_t max_s = (red + 63) / 64;
+  if (s > max_s) s = max_s;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int lora_grad_splits(int64_t T, int64_t Q) {
+  const int64_t qb = (Q + 127) / 128;
+  int64_t s = (256 + qb - 1) / qb;
+  const int64_t max_s = (T + 127) / 128;
+  if (s > max_s) s = max_s;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+qlora_status check_weight_shape(int64_t rows, int64_t cols, WeightDims* d) {
+  if (rows < 1 || cols < 64 || (cols % 64) != 0 || (rows % 16) != 0) return QLORA_ERR_SHAPE;
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n >= (int64_t(1) << 44)) return QLORA_ERR_SHAPE;
+  if (d) {
+    d->rows = rows;
+    d->cols = cols;
+    d->n = n;
+    d->n_b = n / 64;
+    d->n_g = (d->n_b + 255) / 256;
+  }
+  return QLORA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qlora_status check_descriptor(const qlora_nf4_weight* w, WeightDims* d) {
+  if (!w) return QLORA_ERR_NULL;
+  if (w->format_version != QLORA_NF4_FORMAT_VERSION || w->blocksize != QLORA_NF4_BLOCKSIZE ||
+      w->dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE)
+    return QLORA_ERR_FORMAT;
+  const qlora_status s = check_weight_shape(w->rows, w->cols, d);
+  if (s != QLORA_OK) return s;
+  if (!w->codes || !w->absmax_code || !w->absmax_scale || !w->absmax_offset) return QLORA_ERR_NULL;
+  if (!aligned16(w->codes) || !aligned16(w->absmax_code) || !aligned16(w->absmax_scale) ||
+      !aligned16(w->absmax_offset))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+QuantWs quant_ws_layout(const WeightDims& d) {
+  QuantWs q;
+  q.cblk_off = 0;
+  q.gpart_off = align_up(sizeof(float) * (size_t)d.n_b, kWsAlign);
+  q.total = q.gpart_off + align_up(sizeof(double) * (size_t)d.n_g, kWsAlign);
+  return q;
+}
+
+LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
+  LinearWs L;
+  memset(&L, 0, sizeof(L));
+  L.s_proj_x = lora_proj_splits(T, d.cols);
+  L.s_proj_dy = lora_proj_splits(T, d.rows);
+  L.s_grad_a = lora_grad_splits(T, d.cols);
+  L.s_grad_b = lora_grad_splits(T, d.rows);
+  L.t_pad = (T + 31) / 32 * 32;
+  size_t off = 0;
+  const int s_proj = bwd ? (L.s_proj_x > L.s_proj_dy ? L.s_proj_x : L.s_proj_dy) : L.s_proj_x;
+  L.proj_off = off;
+  off += align_up(sizeof(float) * (size_t)s_proj * (size_t)T * (size_t)r, kWsAlign);
+  L.u_off = off;
+  off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
+  if (bwd) {
+    L.bt_off = off;
+    off += align_up(2 * (size_t)r * (size_t)d.rows, kWsAlign);
+    L.at_off = off;
+    off += align_up(2 * (size_t)d.cols * (size_t)r, kWsAlign);
+    L.g_off = off;
+    off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
+    L.gt_off = off;
+    off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
+    L.ut_off = off;
+    off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
+    const size_t ga = (size_t)L.s_grad_a * (size_t)r * (size_t)d.cols;
+    const size_t gb = (size_t)L.s_grad_b * (size_t)r * (size_t)d.rows;
+    L.grad_off = off;
+    off += align_up(sizeof(float) * (ga > gb ? ga : gb), kWsAlign);
+  }
+  L.total = off;
+  return L;
+}
+
+qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
+                               WeightDims* d) {
+  const qlora_status s = check_descriptor(w, d);
+  if (s != QLORA_OK) return s;
+  if (T < 1 || T > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return QLORA_ERR_SHAPE;
+  if (!isfinite(alpha)) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+}  // namespace qlora
+
+extern "C" {
+
+qlora_status qlora_nf4_weight_init(qlora_nf4_weight* w, int64_t rows, int64_t cols) {
+  if (!w) return QLORA_ERR_NULL;
+  const qlora_status s = qlora::check_weight_shape(rows, cols, nullptr);
+  if (s != QLORA_OK) return s;
+  w->format_version = QLORA_NF4_FORMAT_VERSION;
+  w->blocksize = QLORA_NF4_BLOCKSIZE;
+  w->dq_blocksize = QLORA_NF4_DQ_BLOCKSIZE;
+  w->reserved = 0;
+  w->rows = rows;
+  w->cols = cols;
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_buffer_sizes(int64_t rows, int64_t cols, size_t* codes_bytes,
+                                    size_t* absmax_code_bytes, size_t* absmax_scale_bytes,
+                                    size_t* absmax_offset_bytes) {
+  qlora::WeightDims d;
+  const qlora_status s = qlora::check_weight_shape(rows, cols, &d);
+  if (s != QLORA_OK) return s;
+  if (codes_bytes) *codes_bytes = (size_t)(d.n / 2);
+  if (absmax_code_bytes) *absmax_code_bytes = (size_t)d.n_b;
+  if (absmax_scale_bytes) *absmax_scale_bytes = sizeof(float) * (size_t)d.n_g;
+  if (absmax_offset_bytes) *absmax_offset_bytes = sizeof(float);
+  return QLORA_OK;
+}
+
+size_t qlora_nf4_quantize_workspace(int64_t rows, int64_t cols) {
+  qlora::WeightDims d;
+  if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
+  return qlora::quant_ws_layout(d).total;
+}
+
+size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd) {
+  qlora::WeightDims d;
+  if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
+  if (T < 1 || T > (int64_t(1) << 31) || r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
+  return qlora::linear_ws_layout(T, d, r, is_bwd != 0).total;
+}
+
+const char* qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "a size is out of range";
+    case QLORA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    case QLORA_ERR_HIP: return "a HIP runtime call failed";
+    case QLORA_ERR_FORMAT: return "weight descriptor has a wrong format version or block size";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) library for the frozen-NF4
+ * linear layer with a LoRA adapter.
+ *
+ * The method (sources named by page title and section):
+ *   - "QLoRA — 650億パラメータのモデルをGPU 1枚で微調整する" (ta-paperlens),
+ *     sections 量子化を1段落で, NF4, 二重量子化, 勾配は実際どこへ行くのか;
+ *   - LLM book chapter 26 "LoRA/QLoRA" (waylandz), 26.2.1-26.2.4, 26.6.3;
+ *   - Ultralytics glossary "QLoRA", "So funktioniert QLoRA" and its code example.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer (memory of the current HIP device)
+ *     unless a comment says "host".  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream); every call only enqueues work on it and
+ *     returns without synchronising.
+ *   - The caller allocates and owns all memory, including workspaces.  The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     non-OK status nothing has been enqueued.  Errors of already enqueued
+ *     kernels surface at the caller's next synchronisation.
+ *   - Inputs must be finite (NaN/Inf are outside the contract).
+ *   - Calls are stateless and may be made from several host threads.
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_NF4_FORMAT_VERSION 1
+#define QLORA_NF4_BLOCKSIZE 64       /* weights per absmax block               */
+#define QLORA_NF4_DQ_BLOCKSIZE 256   /* block constants per second-level scale */
+#define QLORA_MAX_RANK 128
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,       /* a required pointer is NULL                       */
+  QLORA_ERR_SHAPE = 2,      /* a size is out of range (see each entry point)    */
+  QLORA_ERR_ALIGN = 3,      /* a device pointer is not 16-byte aligned          */
+  QLORA_ERR_WORKSPACE = 4,  /* workspace smaller than the matching *_workspace() */
+  QLORA_ERR_DEVICE = 5,     /* the current device is not a gfx950 GPU           */
+  QLORA_ERR_HIP = 6,        /* a HIP runtime call failed; see qlora_last_hip_error */
+  QLORA_ERR_FORMAT = 7      /* weight descriptor has a wrong version/blocksize  */
+} qlora_status;
+
+/*
+ * Packed NF4 weight with double-quantised block constants (host struct that
+ * holds device pointers; caller-owned).
+ *
+ * W is [rows = out_features, cols = in_features] row-major, cols % 64 == 0.
+ * Block b covers elements [64 b, 64 b + 64) of the row-major flattening, so a
+ * block never crosses a row.  n = rows * cols, n_b = n / 64,
+ * n_g = ceil(n_b / 256).
+ *   codes         [n / 2]  NF4 codes, element 2i in the low nibble of byte i
+ *                          (ta-paperlens NF4 section; waylandz 26.6.3: half a
+ *                          byte per weight).
+ *   absmax_code   [n_b]    OCP FP8 E4M3 bit pattern of the centred, group-scaled
+ *                          block constant (ta-paperlens 二重量子化).
+ *   absmax_scale  [n_g]    float32 s2_g: largest |c_b - mu| in group g.
+ *   absmax_offset [1]      float32 mu: mean of all block constants.
+ * Decoded block constant: c'_b = RN32(RN32(e4m3(code_b) * 2^-8 * s2_g) + mu);
+ * dequantised weight: bf16_RNE(RN32(q[code] * c'_b)).
+ * Storage: n/2 + n_b + 4 n_g + 4 bytes = 4 + 8/64 + 32/16384 bits per weight
+ * plus 32 bits per tensor (ta-paperlens 二重量子化: about 4.127 bits).
+ */
+typedef struct {
+  int32_t format_version;   /* QLORA_NF4_FORMAT_VERSION */
+  int32_t blocksize;        /* QLORA_NF4_BLOCKSIZE      */
+  int32_t dq_blocksize;     /* QLORA_NF4_DQ_BLOCKSIZE   */
+  int32_t reserved;         /* 0 */
+  int64_t rows;
+  int64_t cols;
+  uint8_t *codes;
+  uint8_t *absmax_code;
+  float *absmax_scale;
+  float *absmax_offset;
+} qlora_nf4_weight;
+
+/* Fill a descriptor's header fields for a [rows, cols] weight (host call;
+ * pointers are left untouched).  Returns QLORA_ERR_SHAPE unless rows >= 1,
+ * cols >= 64 and cols % 64 == 0; QLORA_ERR_NULL if w is NULL. */
+qlora_status qlora_nf4_weight_init(qlora_nf4_weight *w, int64_t rows, int64_t cols);
+
+/* Byte sizes of the four device buffers of a [rows, cols] weight (host call).
+ * Any output pointer may be NULL.  Returns QLORA_ERR_SHAPE on a bad shape. */
+qlora_status qlora_nf4_buffer_sizes(int64_t rows, int64_t cols, size_t *codes_bytes,
+                                    size_t *absmax_code_bytes, size_t *absmax_scale_bytes,
+                                    size_t *absmax_offset_bytes);
+
+/* Workspace bytes qlora_nf4_quantize needs: the float32 block constants and
+ * one float64 partial sum per group (0 on a bad shape). */
+size_t qlora_nf4_quantize_workspace(int64_t rows, int64_t cols);
+
+/*
+ * Blockwise NF4 quantisation plus double quantisation of a float32 weight.
+ * (ta-paperlens 量子化を1段落で, NF4, 二重量子化; Ultralytics code example.)
+ *   W    [rows, cols] float32, read only.
+ *   out  host descriptor initialised by qlora_nf4_weight_init for the same
+ *        shape; its four device buffers are written.
+ *   ws   device workspace of at least qlora_nf4_quantize_workspace() bytes.
+ * Per block: c = max |w|; code = nearest NF4 level to RN32(w / c), ties to the
+ * lower index; an all-zero block gets the zero level.  Then mu = mean of all
+ * c (fixed pairwise float64 tree), d = RN32(c - mu), s2 = max |d| per group of
+ * 256 blocks, code8 = E4M3 round-to-nearest-even of RN32(d / s2) * 256
+ * (0x00 when s2 == 0).
+ */
+qlora_status qlora_nf4_quantize(const float *W, const qlora_nf4_weight *out, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/*
+ * Dequantise a packed weight to bf16 [rows, cols] (W_bf16 written).
+ * (ta-paperlens 量子化を1段落で: restore by lookup and multiply; the bf16
+ * values are bit-identical to those the fused linear kernels use.)
+ */
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream);
+
+/* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
+ * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args). */
+size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd);
+
+/*
+ * Forward of the frozen-NF4 linear layer with a LoRA adapter:
+ *   Y = X dequant(W)^T + (alpha / r) (X A^T) B^T
+ * (ta-paperlens 勾配は実際どこへ行くのか: h = dequant(W_NF4) x + B A x with bf16
+ * compute; waylandz 26.2.4: the adapter term is scaled by alpha / r).
+ *   X      [T, cols] bf16        A [r, cols] bf16        B [rows, r] bf16
+ *   Y      [T, rows] bf16 (written)
+ *   U_save [T, r] bf16 (written; X A^T for the backward) or NULL
+ * T >= 1, r % 16 == 0, 16 <= r <= 128.  Accumulation is float32 on bf16 MFMA;
+ * the packed weight is only read.
+ */
+qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
+                              const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                              uint16_t *Y, uint16_t *U_save, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Backward of the same layer for an upstream gradient dY; there is no
+ * gradient for W (ta-paperlens 勾配は実際どこへ行くのか: the input gradient
+ * passes through dequant(W)^T, only A and B are trained, W is never written).
+ *   G  = dY B
+ *   dX = dY dequant(W) + s G A              [T, cols] bf16 (written)
+ *   dA = s G^T X                            [r, cols] float32 (written)
+ *   dB = s dY^T U                           [rows, r] float32 (written)
+ * with s = alpha / r and U = X A^T: U_saved (the forward's U_save) when not
+ * NULL, else recomputed.  Same shape rules as the forward.
+ */
+qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
+                              int64_t T, const uint16_t *A, const uint16_t *B, int32_t r,
+                              float alpha, const uint16_t *U_saved, uint16_t *dX, float *dA,
+                              float *dB, void *ws, size_t ws_bytes, void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *qlora_status_string(qlora_status s);
+
+/* hipError_t value of the last QLORA_ERR_HIP on the calling host thread. */
+int qlora_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */
