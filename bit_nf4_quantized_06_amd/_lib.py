@@ -49,6 +49,7 @@ SIGNATURES = {
                                         _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_DESC_P, _P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _P, _SZ, _P]),
+    "qlora_set_timing_events": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_last_hip_error": (ctypes.c_int, []),
 }

@@ -38,6 +38,25 @@ qlora_status check_device() {
   return st == 1 ? QLORA_OK : QLORA_ERR_DEVICE;
 }
 
+struct TimingPair {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local TimingPair g_timing[4];
+
+// Run `launch` between the caller's timing events of group `which` (if set).
+template <typename F>
+hipError_t timed(int which, hipStream_t st, F&& launch) {
+  const TimingPair& tp = g_timing[which];
+  if (tp.start) {
+    const hipError_t e = hipEventRecord(tp.start, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e == hipSuccess && tp.stop) e = hipEventRecord(tp.stop, st);
+  return e;
+}
+
 template <typename T>
 T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -48,6 +67,13 @@ T* ws_ptr(void* ws, size_t off) {
 extern "C" {
 
 int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+qlora_status qlora_set_timing_events(int which, void* start_event, void* stop_event) {
+  if (which < 0 || which > 3) return QLORA_ERR_SHAPE;
+  g_timing[which].start = static_cast<hipEvent_t>(start_event);
+  g_timing[which].stop = static_cast<hipEvent_t>(stop_event);
+  return QLORA_OK;
+}
 
 qlora_status qlora_nf4_quantize(const float* W, const qlora_nf4_weight* out, void* ws,
                                 size_t ws_bytes, void* stream) {
@@ -61,10 +87,12 @@ qlora_status qlora_nf4_quantize(const float* W, const qlora_nf4_weight* out, voi
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;
-  const hipError_t e = launch_quantize(W, d.n_b, out->codes, out->absmax_code, out->absmax_scale,
-                                       out->absmax_offset, ws_ptr<float>(ws, L.cblk_off),
-                                       ws_ptr<double>(ws, L.gpart_off),
-                                       static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(QLORA_TIMING_QUANTIZE, st, [&] {
+    return launch_quantize(W, d.n_b, out->codes, out->absmax_code, out->absmax_scale,
+                           out->absmax_offset, ws_ptr<float>(ws, L.cblk_off),
+                           ws_ptr<double>(ws, L.gpart_off), st);
+  });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -77,9 +105,11 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, v
   if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
   s = check_device();
   if (s != QLORA_OK) return s;
-  const hipError_t e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale,
-                                         w->absmax_offset, d.n, W_bf16,
-                                         static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(QLORA_TIMING_DEQUANT, st, [&] {
+    return launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n,
+                             W_bf16, st);
+  });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -120,7 +150,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
     g.scale = alpha / (float)r;
     g.out = Y;
     g.T = T;
-    e = launch_qlora_fwd_gemm(g, st);
+    e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
   }
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -182,7 +212,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
     g.scale = scale;
     g.out = dX;
     g.T = T;
-    e = launch_qlora_dx_gemm(g, st);
+    e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
   // dA = s G^T X ; dB = s (U^T dY)^T
   if (e == hipSuccess) e = launch_lora_grad_partial(Gt, L.t_pad, X, T, d.cols, r, L.s_grad_a, PG, st);

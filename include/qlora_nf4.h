@@ -20,7 +20,9 @@
  *     non-OK status nothing has been enqueued.  Errors of already enqueued
  *     kernels surface at the caller's next synchronisation.
  *   - Inputs must be finite (NaN/Inf are outside the contract).
- *   - Calls are stateless and may be made from several host threads.
+ *   - Calls keep no state between them (apart from the per-thread timing
+ *     events of qlora_set_timing_events) and may be made from several host
+ *     threads.
  *   - Device pointers must be 16-byte aligned.
  */
 #ifndef QLORA_NF4_H
@@ -53,7 +55,8 @@ typedef enum {
  * Packed NF4 weight with double-quantised block constants (host struct that
  * holds device pointers; caller-owned).
  *
- * W is [rows = out_features, cols = in_features] row-major, cols % 64 == 0.
+ * W is [rows = out_features, cols = in_features] row-major, rows % 16 == 0,
+ * cols % 64 == 0.
  * Block b covers elements [64 b, 64 b + 64) of the row-major flattening, so a
  * block never crosses a row.  n = rows * cols, n_b = n / 64,
  * n_g = ceil(n_b / 256).
@@ -83,8 +86,9 @@ typedef struct {
 } qlora_nf4_weight;
 
 /* Fill a descriptor's header fields for a [rows, cols] weight (host call;
- * pointers are left untouched).  Returns QLORA_ERR_SHAPE unless rows >= 1,
- * cols >= 64 and cols % 64 == 0; QLORA_ERR_NULL if w is NULL. */
+ * pointers are left untouched).  Returns QLORA_ERR_SHAPE unless rows >= 16,
+ * rows % 16 == 0, cols >= 64, cols % 64 == 0 and rows * cols < 2^44;
+ * QLORA_ERR_NULL if w is NULL. */
 qlora_status qlora_nf4_weight_init(qlora_nf4_weight *w, int64_t rows, int64_t cols);
 
 /* Byte sizes of the four device buffers of a [rows, cols] weight (host call).
@@ -155,6 +159,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
                               int64_t T, const uint16_t *A, const uint16_t *B, int32_t r,
                               float alpha, const uint16_t *U_saved, uint16_t *dX, float *dA,
                               float *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Measurement aid.  On the calling host thread, until changed, every later
+ * call that launches kernel group `which` records `start_event` on the
+ * caller's stream right before that group and `stop_event` right after it
+ * (hipEvent_t handles passed as void*, created by the caller; NULL, NULL
+ * turns it off).  Groups: QLORA_TIMING_FWD_GEMM (the fused forward GEMM),
+ * QLORA_TIMING_DX_GEMM (the fused backward-dX GEMM), QLORA_TIMING_QUANTIZE
+ * (the three quantisation kernels), QLORA_TIMING_DEQUANT.  Returns
+ * QLORA_ERR_SHAPE for an unknown group.
+ */
+#define QLORA_TIMING_FWD_GEMM 0
+#define QLORA_TIMING_DX_GEMM 1
+#define QLORA_TIMING_QUANTIZE 2
+#define QLORA_TIMING_DEQUANT 3
+qlora_status qlora_set_timing_events(int which, void *start_event, void *stop_event);
 
 /* Static English text for a status code (never NULL). */
 const char *qlora_status_string(qlora_status s);

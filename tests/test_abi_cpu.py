@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -113,6 +113,14 @@ def test_linear_validation():
              None) == 3
     for bad_r in (0, 8, 136):
         assert lib.qlora_linear_workspace(T, 1024, 1024, bad_r, 1) == 0
+
+
+def test_timing_hook_validation():
+    lib = _lib.load()
+    assert lib.qlora_set_timing_events(4, None, None) == 2
+    assert lib.qlora_set_timing_events(-1, None, None) == 2
+    for k in range(4):
+        assert lib.qlora_set_timing_events(k, None, None) == 0
 
 
 def test_status_strings():
