@@ -131,10 +131,12 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  uint16_t* U = U_save ? U_save : ws_ptr<uint16_t>(ws, L.u_off);
+  const float scale = alpha / (float)r;
+  uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * X A^T)
   float* P = ws_ptr<float>(ws, L.proj_off);
   hipError_t e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
-  if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, U, nullptr, 0, st);
+  if (e == hipSuccess)
+    e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, U_save, Us, scale, nullptr, 0, st);
   if (e == hipSuccess) {
     GemmArgs g;
     g.act = X;
@@ -144,10 +146,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
     g.mu = w->absmax_offset;
     g.rows = d.rows;
     g.cols = d.cols;
-    g.lora_l = U;
+    g.lora_l = Us;
     g.lora_r = B;
     g.r = r;
-    g.scale = alpha / (float)r;
     g.out = Y;
     g.T = T;
     e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
@@ -176,7 +177,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
 
   uint16_t* Bt = ws_ptr<uint16_t>(ws, L.bt_off);    // [r, rows]
   uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
-  uint16_t* G = ws_ptr<uint16_t>(ws, L.g_off);      // [T, r]
+  uint16_t* Gs = ws_ptr<uint16_t>(ws, L.g_off);     // [T, r] bf16(s * dY B)
   uint16_t* Gt = ws_ptr<uint16_t>(ws, L.gt_off);    // [r, t_pad]
   uint16_t* Ut = ws_ptr<uint16_t>(ws, L.ut_off);    // [r, t_pad]
   float* P = ws_ptr<float>(ws, L.proj_off);
@@ -186,17 +187,19 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   if (e == hipSuccess) e = launch_transpose_bf16(A, r, d.cols, At, r, st);
   // G = dY B  (and G^T for dA)
   if (e == hipSuccess) e = launch_lora_proj_partial(dY, Bt, T, d.rows, r, L.s_proj_dy, P, st);
-  if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_dy, G, Gt, L.t_pad, st);
+  if (e == hipSuccess)
+    e = launch_lora_proj_reduce(P, T, r, L.s_proj_dy, nullptr, Gs, scale, Gt, L.t_pad, st);
   // U^T for dB: from the forward's U, or recomputed as X A^T
   if (e == hipSuccess) {
     if (U_saved) {
       e = launch_transpose_bf16(U_saved, T, r, Ut, L.t_pad, st);
     } else {
       e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
-      if (e == hipSuccess) e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, Ut, L.t_pad, st);
+      if (e == hipSuccess)
+        e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, nullptr, 0.0f, Ut, L.t_pad, st);
     }
   }
-  // dX = dY dequant(W) + s G A
+  // dX = dY dequant(W) + (s G) A
   if (e == hipSuccess) {
     GemmArgs g;
     g.act = dY;
@@ -206,10 +209,9 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
     g.mu = w->absmax_offset;
     g.rows = d.rows;
     g.cols = d.cols;
-    g.lora_l = G;
+    g.lora_l = Gs;
     g.lora_r = At;
     g.r = r;
-    g.scale = scale;
     g.out = dX;
     g.T = T;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });

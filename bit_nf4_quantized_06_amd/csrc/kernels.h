@@ -16,7 +16,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* code8, const f
                              const float* mu, int64_t n, uint16_t* out, hipStream_t stream);
 
 // --- fused dequant GEMMs (gemm.hip) ---------------------------------------
-// out[T, out_len] = act[T, red_len] * Wop + s * lora_l[T, r] * lora_r[out_len, r]^T
+// out[T, out_len] = act[T, red_len] * Wop + lora_l[T, r] * lora_r[out_len, r]^T
 // where Wop = dequant(W)^T (forward: red = cols, out = rows) or dequant(W)
 // (backward dX: red = rows, out = cols).
 struct GemmArgs {
@@ -26,10 +26,9 @@ struct GemmArgs {
   const float* s2;
   const float* mu;
   int64_t rows, cols;
-  const uint16_t* lora_l;  // [T, r] bf16
+  const uint16_t* lora_l;  // [T, r] bf16, already multiplied by alpha / r
   const uint16_t* lora_r;  // [out_len, r] bf16
   int32_t r;
-  float scale;
   uint16_t* out;           // [T, out_len] bf16
   int64_t T;
 };
@@ -43,11 +42,12 @@ int lora_proj_splits(int64_t T, int64_t red);
 hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_t T,
                                     int64_t red, int32_t r, int splits, float* P,
                                     hipStream_t stream);
-// out_rm[t][p] = bf16(sum_s P) (if not NULL), out_tr[p][t] likewise with
-// row stride ld_tr and zeros for T <= t < ld_tr (if not NULL).
+// v = sum_s P (fixed order).  Each output may be NULL: out_rm[t][p] = bf16(v),
+// out_sc[t][p] = bf16(scale * v), out_tr[p][t] = bf16(v) with row stride ld_tr
+// and zeros for T <= t < ld_tr.
 hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
-                                   uint16_t* out_rm, uint16_t* out_tr, int64_t ld_tr,
-                                   hipStream_t stream);
+                                   uint16_t* out_rm, uint16_t* out_sc, float scale,
+                                   uint16_t* out_tr, int64_t ld_tr, hipStream_t stream);
 // out[c][r'] = in[r'][c] for a [R, C] bf16 matrix; out has row stride ld_out
 // and is zero for R <= r' < ld_out.
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t R, int64_t C, uint16_t* out,

@@ -77,9 +77,14 @@ hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_
   return hipGetLastError();
 }
 
+// Fixed-order sum of the split partials.  Writes any of: out_rm[t][p] =
+// bf16(v), out_sc[t][p] = bf16(scale * v) (the pre-scaled operand the fused
+// GEMM seeds its accumulators with), out_tr[p][t] = bf16(v) with row stride
+// ld_tr and zeros for T <= t < ld_tr.
 __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(
     const float* __restrict__ P, int64_t T, int r, int splits, uint16_t* __restrict__ out_rm,
-    uint16_t* __restrict__ out_tr, int64_t ld_tr, int64_t rows_total) {
+    uint16_t* __restrict__ out_sc, float scale, uint16_t* __restrict__ out_tr, int64_t ld_tr,
+    int64_t rows_total) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows_total * r) return;
   const int64_t t = i / r;
@@ -88,18 +93,21 @@ __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(
   if (t < T) {
     for (int s = 0; s < splits; ++s) v += P[((int64_t)s * T + t) * r + p];
   }
-  const uint32_t b = pack_bf16x2(v, 0.0f) & 0xFFFFu;
-  if (out_rm && t < T) out_rm[t * r + p] = (uint16_t)b;
-  if (out_tr) out_tr[(int64_t)p * ld_tr + t] = (uint16_t)b;
+  const uint16_t b = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+  if (t < T) {
+    if (out_rm) out_rm[t * r + p] = b;
+    if (out_sc) out_sc[t * r + p] = (uint16_t)(pack_bf16x2(v * scale, 0.0f) & 0xFFFFu);
+  }
+  if (out_tr) out_tr[(int64_t)p * ld_tr + t] = b;
 }
 
 hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
-                                   uint16_t* out_rm, uint16_t* out_tr, int64_t ld_tr,
-                                   hipStream_t stream) {
+                                   uint16_t* out_rm, uint16_t* out_sc, float scale,
+                                   uint16_t* out_tr, int64_t ld_tr, hipStream_t stream) {
   const int64_t rows_total = out_tr ? ld_tr : T;
   const int64_t n = rows_total * r;
   hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     stream, P, T, r, splits, out_rm, out_tr, ld_tr, rows_total);
+                     stream, P, T, r, splits, out_rm, out_sc, scale, out_tr, ld_tr, rows_total);
   return hipGetLastError();
 }
 
