@@ -12,20 +12,26 @@
 // 128 x 128 sub-tile held as 4 x 4 MFMA 32x32x16 blocks (256 AGPRs).  The
 // reduction advances 64 per step, i.e. one NF4 block per weight row.
 //
-// Per step, both operands come from LDS (two stages of 64 KB each):
-//   * activations (X or dY) 256 x 64 bf16: global -> registers -> LDS;
-//   * the weight tile is dequantised once per workgroup straight into LDS.
-//     Each thread owns one block of 64 weights: it builds the 16-entry bf16
-//     table q[k] * c' (16 float32 products rounded once, as the bulk
-//     dequantiser does) and translates its 32 bytes of nibbles with v_perm
+// Operands, both read from LDS:
+//   * activations (X or dY), 256 x 64 bf16 per step, are fetched straight
+//     into LDS by buffer loads (no registers), two steps ahead, into a ring
+//     of three 32 KB stages;
+//   * the weight tile is dequantised once per workgroup into one of two
+//     32 KB stages.  Each thread owns one block of 64 weights per step: its
+//     32 bytes of packed codes arrive in registers two steps ahead; it builds
+//     the 16-entry bf16 table q[k] * c' (16 float32 products rounded once,
+//     as the bulk dequantiser does) and translates its nibbles with v_perm
 //     byte lookups.  The tile keeps W's own row layout in both directions;
 //     the backward reads its operand (reduction = W rows) with
 //     ds_read_b64_tr_b16, which hands each lane 4 consecutive rows of one
 //     column.
-// The work of step k+1 (global loads issued one step ahead for activations
-// and two steps ahead for the packed codes, dequantisation, LDS stores) is
-// interleaved with the 64 MFMAs of step k; MFMA fragments are read one
-// 16-wide slice ahead.  One barrier per step.
+// All out-of-range rows and columns are handled by buffer-descriptor range
+// checks (reads past the end return 0), so every 16-MFMA slice is a single
+// basic block.  Within a slice the MFMAs are interleaved with the
+// dequantisation VALU work, the LDS stores of the next stage and the
+// fragment reads of the next slice (sched_group_barrier).  The one barrier
+// per step sits before the last four MFMAs of the step, so the first
+// fragments of the next step are read while they run.
 //
 // LDS layouts (16-byte chunks XOR-swizzled so that every ds_read_b128,
 // ds_read_b64_tr_b16 and ds_write_b128 pattern used here touches 16 distinct
@@ -48,10 +54,15 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kStageElems = BM * BK;           // 16384 bf16 = 32 KB
+constexpr int kAStages = 3;
+constexpr int kBStages = 2;
+constexpr uint32_t kOOB = 0x80000000u;         // buffer offset that reads as 0
+constexpr int kVmemPerStep = 12;               // 8 activation DMAs + 4 code loads
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ int swz_a(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
@@ -74,12 +85,24 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, c
 
 // two ds_read_b64_tr_b16 -> one 8 x bf16 MFMA operand
 __device__ __forceinline__ u32x4_t ld_lds_tr(const uint16_t* p0, const uint16_t* p1) {
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
   const uint2 l = __builtin_bit_cast(uint2, lo);
   const uint2 h = __builtin_bit_cast(uint2, hi);
   return u32x4_t{l.x, l.y, h.x, h.y};
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0), then a workgroup barrier that is also a
+// compiler memory barrier.  Outstanding LDS-DMA loads beyond the n newest
+// are complete afterwards.
+template <int N>
+__device__ __forceinline__ void barrier_keep_vmem() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // tile index -> (token tile, column tile): XCD-major, then groups of 4 token tiles
@@ -100,9 +123,9 @@ __device__ __forceinline__ void tile_coords(int pid, int mt, int nt, int& tm, in
 
 template <bool kBwd>
 __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStageElems];   // 128 KB
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(kAStages + kBStages) * kStageElems];
   uint16_t* const As0 = smem;
-  uint16_t* const Bs0 = smem + 2 * kStageElems;
+  uint16_t* const Bs0 = smem + kAStages * kStageElems;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,9 +146,8 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  f32x16_t acc[4][4];
-
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -151,16 +173,41 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
   }
 
-  // ---- per-thread staging state -------------------------------------------
-  // activation chunk i of this thread: tile row (tid >> 3) + 32 i, chunk tid & 7
-  u32x4_t a_reg[8];
-  // packed codes of this thread's weight block, for step k+1 (cur) and k+2 (nxt)
-  u32x4_t c_cur[2], c_nxt[2];
-  float cp_cur = 0.0f, cp_nxt = 0.0f;
-  bool ok_cur = false, ok_nxt = false;
+  // ---- buffer descriptors ---------------------------------------------------
+  const int64_t rows_here = (g.T - m0) < BM ? (g.T - m0) : BM;
+  const __amdgpu_buffer_rsrc_t act_rs =
+      make_rsrc(g.act + m0 * red_len, (uint32_t)(rows_here * red_len * 2));
+  const __amdgpu_buffer_rsrc_t codes_rs = make_rsrc(g.codes, (uint32_t)((g.rows * g.cols) >> 1));
+  const __amdgpu_buffer_rsrc_t code8_rs = make_rsrc(g.code8, (uint32_t)(g.rows * kblocks));
+  const __amdgpu_buffer_rsrc_t s2_rs =
+      make_rsrc(g.s2, (uint32_t)(((g.rows * kblocks + 255) >> 8) * 4));
 
-  // weight block owned by this thread at step `step`
-  auto w_coords = [&](int step, int64_t& n, int64_t& kc) {
+  // activation DMA of step `step` into stage (step % 3): wave w, load i covers
+  // LDS bytes [(8 w + i) KB, +1 KB) of the stage, i.e. rows 8 (8 w + i) .. +8
+  auto issue_act = [&](int step) {
+    uint16_t* stage = As0 + (step % kAStages) * kStageElems;
+    const int64_t k0 = (int64_t)step * BK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (wave * 8 + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int64_t k = k0 + 8 * c;
+      const uint32_t off = (step < nsteps && k < red_len)
+                               ? (uint32_t)((row * red_len + k) * 2) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_void_t*)(stage + (wave * 8 + i) * 512),
+                                               16, off, 0, 0, 0);
+    }
+  };
+
+  // packed codes + block constant inputs of this thread's block at `step`
+  struct CodeRegs {
+    u32x4_t c0, c1;
+    uint32_t code8;
+    float s2;
+    bool ok;
+  };
+  auto issue_codes = [&](int step, CodeRegs& r) {
+    int64_t n, kc;
     if (!kBwd) {
       n = n0 + tid;
       kc = (int64_t)step * BK;
@@ -168,38 +215,24 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
       n = (int64_t)step * BK + (tid & 63);
       kc = n0 + 64 * (tid >> 6);
     }
+    r.ok = step < nsteps && n < g.rows && kc < g.cols;
+    const int64_t blk = n * kblocks + (kc >> 6);
+    const uint32_t off = r.ok ? (uint32_t)((n * g.cols + kc) >> 1) : kOOB;
+    const uint32_t off8 = r.ok ? (uint32_t)blk : kOOB;
+    const uint32_t offs = r.ok ? (uint32_t)((blk >> 8) * 4) : kOOB;
+    r.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(codes_rs, off, 0, 0));
+    r.c1 = __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(codes_rs, off + 16, 0, 0));
+    r.code8 = __builtin_amdgcn_raw_buffer_load_b8(code8_rs, off8, 0, 0);
+    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s2_rs, offs, 0, 0));
   };
-  auto load_codes = [&](int step, u32x4_t* c, float& cp, bool& ok) {
-    int64_t n, kc;
-    w_coords(step, n, kc);
-    ok = step < nsteps && n < g.rows && kc < g.cols;
-    if (ok) {
-      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(g.codes + ((n * g.cols + kc) >> 1));
-      c[0] = p[0];
-      c[1] = p[1];
-      const int64_t blk = n * kblocks + (kc >> 6);
-      cp = block_constant(g.code8[blk], g.s2[blk >> 8], mu);
-    }
-  };
-  auto load_act = [&](int step) {
-    const int64_t kbase = (int64_t)step * BK + (tid & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t t = m0 + (tid >> 3) + 32 * i;
-      a_reg[i] = (t < g.T && kbase < red_len) ? ld_global16(g.act + t * red_len + kbase)
-                                              : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_act = [&](uint16_t* as, int i) {
-    *reinterpret_cast<u32x4_t*>(as + swz_a((tid >> 3) + 32 * i, tid & 7)) = a_reg[i];
-  };
-  // dequantise word pair (2w, 2w+1) of the current block and store 16 weights
-  auto store_w = [&](uint16_t* bs, const Nf4Lut& lut, int w) {
-    uint32_t d0[4] = {0u, 0u, 0u, 0u}, d1[4] = {0u, 0u, 0u, 0u};
-    if (ok_cur) {
-      dequant8(lut, c_cur[w >> 1][(2 * w) & 3], d0);
-      dequant8(lut, c_cur[w >> 1][(2 * w + 1) & 3], d1);
-    }
+
+  // dequantise words (2w, 2w+1) of `r` with `lut` into stage `bs`
+  auto store_w = [&](uint16_t* bs, const Nf4Lut& lut, const CodeRegs& r, int w) {
+    const u32x4_t& src = (w < 2) ? r.c0 : r.c1;
+    uint32_t d0[4], d1[4];
+    dequant8(lut, src[(2 * w) & 3], d0);
+    dequant8(lut, src[(2 * w + 1) & 3], d1);
     if (!kBwd) {
       *reinterpret_cast<u32x4_t*>(bs + swz_a(tid, 2 * w)) = u32x4_t{d0[0], d0[1], d0[2], d0[3]};
       *reinterpret_cast<u32x4_t*>(bs + swz_a(tid, 2 * w + 1)) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
@@ -210,7 +243,12 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
       *reinterpret_cast<u32x4_t*>(bs + swz_bt(row, chunk + 1)) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
     }
   };
-  // MFMA fragments of slice s from stage buffers (as, bs)
+  auto lut_of = [&](const CodeRegs& r) {
+    const float cp = r.ok ? block_constant(r.code8, r.s2, mu) : 0.0f;   // 0: invalid rows
+    return make_lut(cp);
+  };
+
+  // MFMA fragments of slice s from stages (as, bs)
   auto load_frags = [&](const uint16_t* as, const uint16_t* bs, int s, u32x4_t* fa, u32x4_t* fb) {
     const int chunk = 2 * s + lhi;
 #pragma unroll
@@ -220,69 +258,92 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) fb[j] = ld_lds16(bs + swz_a(128 * wn + 32 * j + l32, chunk));
     } else {
       // rows 16 s + 8 lhi + 4 rr + (lane % 16) / 4, columns col0 .. col0 + 3
-      const int rbase = 16 * s + 8 * lhi + ((lane & 15) >> 2);
+      const int r0 = 16 * s + 8 * lhi + ((lane & 15) >> 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col0 = 128 * wn + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const int r0 = rbase, r1 = rbase + 4;
         fb[j] = ld_lds_tr(bs + swz_bt(r0, col0 >> 3) + (col0 & 7),
-                          bs + swz_bt(r1, col0 >> 3) + (col0 & 7));
+                          bs + swz_bt(r0 + 4, col0 >> 3) + (col0 & 7));
       }
     }
   };
 
-  // ---- prologue: stage 0 in LDS, codes of step 1 in registers ---------------
-  load_act(0);
-  load_codes(0, c_cur, cp_cur, ok_cur);
-  load_codes(1, c_nxt, cp_nxt, ok_nxt);
+  // ---- prologue ------------------------------------------------------------
+  CodeRegs cr_cur, cr_nxt;
+  issue_act(0);
+  issue_codes(0, cr_cur);
+  issue_act(1);
+  issue_codes(1, cr_nxt);
   {
+    const Nf4Lut lut = lut_of(cr_cur);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) store_act(As0, i);
-    const Nf4Lut lut = make_lut(cp_cur);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) store_w(Bs0, lut, w);
+    for (int w = 0; w < 4; ++w) store_w(Bs0, lut, cr_cur, w);
   }
-  c_cur[0] = c_nxt[0];
-  c_cur[1] = c_nxt[1];
-  cp_cur = cp_nxt;
-  ok_cur = ok_nxt;
-  __syncthreads();
+  cr_cur = cr_nxt;
+  barrier_keep_vmem<kVmemPerStep>();   // activation stage 0 complete
 
   u32x4_t fa[2][4], fb[2][4];
   load_frags(As0, Bs0, 0, fa[0], fb[0]);
 
   for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const uint16_t* as = As0 + cur * kStageElems;
-    const uint16_t* bs = Bs0 + cur * kStageElems;
-    uint16_t* as_n = As0 + (cur ^ 1) * kStageElems;
-    uint16_t* bs_n = Bs0 + (cur ^ 1) * kStageElems;
-    const bool more = step + 1 < nsteps;
-    if (more) load_act(step + 1);
-    load_codes(step + 2, c_nxt, cp_nxt, ok_nxt);
-    Nf4Lut lut;
-    if (more) lut = make_lut(cp_cur);
+    const uint16_t* as = As0 + (step % kAStages) * kStageElems;
+    const uint16_t* bs = Bs0 + (step & 1) * kStageElems;
+    const uint16_t* as_n = As0 + ((step + 1) % kAStages) * kStageElems;
+    uint16_t* bs_n = Bs0 + ((step + 1) & 1) * kStageElems;
 
+    issue_act(step + 2);
+    issue_codes(step + 2, cr_nxt);
+    const Nf4Lut lut = lut_of(cr_cur);
+
+    // slices 0..2: 16 MFMAs each, interleaved with the next slice's fragment
+    // reads and half of a word pair's dequantisation + stores
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 3; ++s) {
       const int f = s & 1;
-      if (s < 3) load_frags(as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
+      load_frags(as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
-      if (more) {
-        store_w(bs_n, lut, s);
-        store_act(as_n, 2 * s);
-        store_act(as_n, 2 * s + 1);
+      store_w(bs_n, lut, cr_cur, s);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
       }
     }
-    c_cur[0] = c_nxt[0];
-    c_cur[1] = c_nxt[1];
-    cp_cur = cp_nxt;
-    ok_cur = ok_nxt;
-    __syncthreads();
-    if (more) load_frags(as_n, bs_n, 0, fa[0], fb[0]);
+    // slice 3: last word pair, then the barrier ahead of the final 4 MFMAs
+    {
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
+      store_w(bs_n, lut, cr_cur, 3);
+#pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      barrier_keep_vmem<kVmemPerStep>();   // stage step+1 ready everywhere
+      u32x4_t ga[4], gb[4];
+      load_frags(as_n, bs_n, 0, ga, gb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[0][i] = ga[i];
+        fb[0][i] = gb[i];
+      }
+    }
+    cr_cur = cr_nxt;
   }
 
   // ---- epilogue: round to bf16 and store ------------------------------------
