@@ -121,30 +121,273 @@ __device__ __forceinline__ void tile_coords(int pid, int mt, int nt, int& tm, in
   tn = local / gm;
 }
 
+// Everything one workgroup needs across steps.  The five LDS stages are
+// separate objects and every stage index is a compile-time constant (the
+// step loop is unrolled by 6 = lcm(3, 2)), so the compiler can tell an
+// activation DMA into one stage from LDS traffic on another and does not
+// insert waits for outstanding DMA loads before unrelated LDS accesses.
+template <bool kBwd>
+struct GemmCtx {
+  const GemmArgs& g;
+  uint16_t* A[kAStages];
+  uint16_t* B[kBStages];
+  int tid, lane, wave, wm, wn, l32, lhi, nsteps;
+  int64_t m0, n0, red_len, kblocks;
+  float mu;
+  // buffer ranges (base, bytes) of the operands read with range checking
+  const uint16_t* act_base;
+  uint32_t act_bytes, codes_bytes, code8_bytes, s2_bytes;
+  // per-lane byte offsets that do not change with the step
+  uint32_t act_voff[2];     // activation DMA, even / odd 8-row block
+  uint32_t code_voff;       // this thread's packed codes at step 0
+  int64_t blk0;             // this thread's block index at step 0
+  bool w_row_ok;            // this thread's weight block lies inside W
+  // per-lane LDS element offsets inside a stage (loop invariant); the row
+  // blocks i (+32 rows) and, in the backward weight tile, the slices (+16
+  // rows) are constant additions folded into instruction offsets
+  int a_frag[4];            // activation fragment, slice s, row block 0
+  int b_frag[8];            // forward: [s]; backward: [2 j + rr] for slice 0
+  int w_store[8];           // dequantised chunk w of this thread's block
+};
+
+struct CodeRegs {
+  u32x4_t c0, c1;
+  uint32_t code8;
+  float s2;
+  bool ok;
+};
+
+// Activation DMA of step `step` into `stage`: wave w, load i fills LDS bytes
+// [(8 w + i) KB, +1 KB) of the stage, i.e. tile rows 8 (8 w + i) .. +8.  The
+// swizzle of a row only depends on the lane and on the parity of i, so each
+// lane has two fixed byte offsets; the row block and the step enter through
+// the scalar offset.  Columns past the end of the reduction (the last step
+// of a backward whose weight has rows % 64 != 0) read real neighbouring
+// data; the matching rows of the dequantised weight tile are exactly 0.
+// Steps past the end read nothing (scalar offset beyond the range: zeros).
+template <bool kBwd>
+__device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
+  const uint32_t sbase = step < c.nsteps ? (uint32_t)(step * BK * 2) : kOOB;
+  const uint32_t row_bytes = (uint32_t)(c.red_len * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t soff = step < c.nsteps ? sbase + (uint32_t)((c.wave * 8 + i) * 8) * row_bytes
+                                          : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.act_base, c.act_bytes),
+                                             (lds_void_t*)(stage + (c.wave * 8 + i) * 512), 16,
+                                             c.act_voff[i & 1], soff, 0, 0);
+  }
+}
+
+// packed codes and block-constant inputs of this thread's block at `step`
+template <bool kBwd>
+__device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, CodeRegs& r) {
+  // forward: the block moves along the row (+32 B, +1 block per step);
+  // backward: it moves down 64 rows (+64 rows of codes and constants)
+  const bool in = step < c.nsteps;
+  const int64_t dblk = kBwd ? (int64_t)step * 64 * c.kblocks : (int64_t)step;
+  const uint32_t dcode = kBwd ? (uint32_t)((int64_t)step * 64 * (c.g.cols >> 1)) : (uint32_t)(step * 32);
+  int64_t n_ok_rows = c.g.rows - (kBwd ? (int64_t)step * 64 : 0);
+  r.ok = in && c.w_row_ok && (!kBwd || (c.tid & 63) < n_ok_rows);
+  const uint32_t scode = in ? dcode : kOOB;
+  const int64_t blk = c.blk0 + dblk;
+  const __amdgpu_buffer_rsrc_t codes_rs = make_rsrc(c.g.codes, c.codes_bytes);
+  r.c0 = __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(codes_rs, c.code_voff, scode, 0));
+  r.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                         codes_rs, c.code_voff + 16, scode, 0));
+  r.code8 = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(c.g.code8, c.code8_bytes),
+                                                r.ok ? (uint32_t)blk : kOOB, 0, 0);
+  r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       make_rsrc(c.g.s2, c.s2_bytes),
+                                       r.ok ? (uint32_t)((blk >> 8) * 4) : kOOB, 0, 0));
+}
+
+template <bool kBwd>
+__device__ __forceinline__ Nf4Lut lut_of(const GemmCtx<kBwd>& c, const CodeRegs& r) {
+  const float cp = r.ok ? block_constant(r.code8, r.s2, c.mu) : 0.0f;   // 0: rows past the end
+  return make_lut(cp);
+}
+
+// dequantise words (2w, 2w+1) of `r` into weight stage `bs`
+template <bool kBwd>
+__device__ __forceinline__ void store_w(const GemmCtx<kBwd>& c, uint16_t* bs, const Nf4Lut& lut,
+                                        const CodeRegs& r, int w) {
+  const u32x4_t& src = (w < 2) ? r.c0 : r.c1;
+  uint32_t d0[4], d1[4];
+  dequant8(lut, src[(2 * w) & 3], d0);
+  dequant8(lut, src[(2 * w + 1) & 3], d1);
+  *reinterpret_cast<u32x4_t*>(bs + c.w_store[2 * w]) = u32x4_t{d0[0], d0[1], d0[2], d0[3]};
+  *reinterpret_cast<u32x4_t*>(bs + c.w_store[2 * w + 1]) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
+}
+
+// MFMA fragments of slice s from stages (as, bs)
+template <bool kBwd>
+__device__ __forceinline__ void load_frags(const GemmCtx<kBwd>& c, const uint16_t* as,
+                                           const uint16_t* bs, int s, u32x4_t* fa, u32x4_t* fb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = ld_lds16(as + c.a_frag[s] + 32 * i * BK);
+  if (!kBwd) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = ld_lds16(bs + c.b_frag[s] + 32 * j * BK);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[j] = ld_lds_tr(bs + c.b_frag[2 * j] + 16 * s * BN, bs + c.b_frag[2 * j + 1] + 16 * s * BN);
+  }
+}
+
+// Interleave pattern of one 16-MFMA slice: each MFMA is followed by `v`
+// VALU ops; the first 8 also carry one LDS read (next slice's fragments),
+// two of the later ones an LDS store, and the first four one VMEM load.
+template <int V, bool kVmem>
+__device__ __forceinline__ void slice_schedule() {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (kVmem && q < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if (q == 9 || q == 13) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+  }
+}
+
+// One reduction step on activation stage SA and weight stage SB.  On entry
+// fa[0], fb[0] hold slice 0 of this step and `cur` the codes of step+1; on
+// exit fa[0], fb[0] hold slice 0 of step+1 and `cur` the codes of step+2.
+template <bool kBwd, int SA, int SB>
+__device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][4],
+                                          u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][4],
+                                          CodeRegs& cur, CodeRegs& nxt) {
+#if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins; the host pass needs no body
+  const uint16_t* as = c.A[SA];
+  const uint16_t* bs = c.B[SB];
+  uint16_t* as_next = c.A[(SA + 1) % kAStages];
+  uint16_t* bs_next = c.B[(SB + 1) % kBStages];
+
+  // slice 0: loads for step+2, the block table for step+1
+  issue_act(c, c.A[(SA + 2) % kAStages], step + 2);
+  issue_codes(c, step + 2, nxt);
+  const Nf4Lut lut = lut_of(c, cur);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int f = s & 1;
+    load_frags(c, as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
+    store_w(c, bs_next, lut, cur, s);
+    if (s == 0)
+      slice_schedule<6, true>();
+    else
+      slice_schedule<4, false>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // slice 3: 12 MFMAs with the last word pair, barrier, next step's first
+  // fragments under the remaining 4 MFMAs
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
+  store_w(c, bs_next, lut, cur, 3);
+#pragma unroll
+  for (int q = 0; q < 12; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    if (q == 5 || q == 9) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_keep_vmem<kVmemPerStep>();   // stage step+1 complete and visible
+  u32x4_t ga[4], gb[4];
+  load_frags(c, as_next, bs_next, 0, ga, gb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[0][i] = ga[i];
+    fb[0][i] = gb[i];
+  }
+  cur = nxt;
+#endif
+}
+
 template <bool kBwd>
 __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[(kAStages + kBStages) * kStageElems];
-  uint16_t* const As0 = smem;
-  uint16_t* const Bs0 = smem + kAStages * kStageElems;
+  __shared__ __attribute__((aligned(1024))) uint16_t sa0[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa1[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t sa2[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb0[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb1[kStageElems];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int64_t red_len = kBwd ? g.rows : g.cols;
+  GemmCtx<kBwd> c{g, {sa0, sa1, sa2}, {sb0, sb1}};
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.wm = c.wave >> 1;
+  c.wn = c.wave & 1;
+  c.l32 = c.lane & 31;
+  c.lhi = c.lane >> 5;
+  c.red_len = kBwd ? g.rows : g.cols;
   const int64_t out_len = kBwd ? g.cols : g.rows;
   const int mt = (int)((g.T + BM - 1) / BM);
   const int nt = (int)((out_len + BN - 1) / BN);
   int tm, tn;
   tile_coords(blockIdx.x, mt, nt, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
-  const int nsteps = (int)((red_len + BK - 1) / BK);
-  const int64_t kblocks = g.cols >> 6;
-  const float mu = g.mu[0];
-  const int l32 = lane & 31;
-  const int lhi = lane >> 5;
+  c.m0 = (int64_t)tm * BM;
+  c.n0 = (int64_t)tn * BN;
+  c.nsteps = (int)((c.red_len + BK - 1) / BK);
+  c.kblocks = g.cols >> 6;
+  c.mu = g.mu[0];
+  const int64_t rows_here = (g.T - c.m0) < BM ? (g.T - c.m0) : BM;
+  {
+    // activation DMA lane offsets (see issue_act): row-in-block = lane / 8,
+    // swizzle ((row >> 1) & 7) with row bit 3 = parity of the load index
+    const int rl = c.lane >> 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = 8 * par + rl;
+      const int ch = (c.lane & 7) ^ ((row >> 1) & 7);
+      c.act_voff[par] = (uint32_t)((rl * c.red_len + 8 * ch) * 2);
+    }
+    int64_t n, kc;
+    if (!kBwd) {
+      n = c.n0 + c.tid;
+      kc = 0;
+    } else {
+      n = c.tid & 63;
+      kc = c.n0 + 64 * (c.tid >> 6);
+    }
+    c.w_row_ok = kBwd ? kc < g.cols : n < g.rows;   // backward rows are checked per step
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) c.a_frag[sl] = swz_a(128 * c.wm + c.l32, 2 * sl + c.lhi);
+    if (!kBwd) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) c.b_frag[sl] = swz_a(128 * c.wn + c.l32, 2 * sl + c.lhi);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) c.w_store[w] = swz_a(c.tid, w);
+    } else {
+      // tr16 source lane: row 8 lhi + 4 rr + (lane % 16) / 4, columns col0 .. col0 + 3
+      const int r0 = 8 * c.lhi + ((c.lane & 15) >> 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col0 = 128 * c.wn + 32 * j + 16 * ((c.lane >> 4) & 1) + 4 * (c.lane & 3);
+        c.b_frag[2 * j] = swz_bt(r0, col0 >> 3) + (col0 & 7);
+        c.b_frag[2 * j + 1] = swz_bt(r0 + 4, col0 >> 3) + (col0 & 7);
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) c.w_store[w] = swz_bt(c.tid & 63, 8 * (c.tid >> 6) + w);
+    }
+    c.code_voff = c.w_row_ok ? (uint32_t)((n * g.cols + kc) >> 1) : kOOB;
+    c.blk0 = n * (g.cols >> 6) + (kc >> 6);
+  }
+  c.act_base = g.act + c.m0 * c.red_len;
+  c.act_bytes = (uint32_t)(rows_here * c.red_len * 2);
+  c.codes_bytes = (uint32_t)((g.rows * g.cols) >> 1);
+  c.code8_bytes = (uint32_t)(g.rows * c.kblocks);
+  c.s2_bytes = (uint32_t)(((g.rows * c.kblocks + 255) >> 8) * 4);
+  const int lane = c.lane, l32 = c.l32, lhi = c.lhi, wm = c.wm, wn = c.wn;
+  const int64_t m0 = c.m0, n0 = c.n0;
 
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
   f32x16_t acc[4][4];
@@ -172,178 +415,37 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
   }
-
-  // ---- buffer descriptors ---------------------------------------------------
-  const int64_t rows_here = (g.T - m0) < BM ? (g.T - m0) : BM;
-  const __amdgpu_buffer_rsrc_t act_rs =
-      make_rsrc(g.act + m0 * red_len, (uint32_t)(rows_here * red_len * 2));
-  const __amdgpu_buffer_rsrc_t codes_rs = make_rsrc(g.codes, (uint32_t)((g.rows * g.cols) >> 1));
-  const __amdgpu_buffer_rsrc_t code8_rs = make_rsrc(g.code8, (uint32_t)(g.rows * kblocks));
-  const __amdgpu_buffer_rsrc_t s2_rs =
-      make_rsrc(g.s2, (uint32_t)(((g.rows * kblocks + 255) >> 8) * 4));
-
-  // activation DMA of step `step` into stage (step % 3): wave w, load i covers
-  // LDS bytes [(8 w + i) KB, +1 KB) of the stage, i.e. rows 8 (8 w + i) .. +8
-  auto issue_act = [&](int step) {
-    uint16_t* stage = As0 + (step % kAStages) * kStageElems;
-    const int64_t k0 = (int64_t)step * BK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (wave * 8 + i) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      const int64_t k = k0 + 8 * c;
-      const uint32_t off = (step < nsteps && k < red_len)
-                               ? (uint32_t)((row * red_len + k) * 2) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_void_t*)(stage + (wave * 8 + i) * 512),
-                                               16, off, 0, 0, 0);
-    }
-  };
-
-  // packed codes + block constant inputs of this thread's block at `step`
-  struct CodeRegs {
-    u32x4_t c0, c1;
-    uint32_t code8;
-    float s2;
-    bool ok;
-  };
-  auto issue_codes = [&](int step, CodeRegs& r) {
-    int64_t n, kc;
-    if (!kBwd) {
-      n = n0 + tid;
-      kc = (int64_t)step * BK;
-    } else {
-      n = (int64_t)step * BK + (tid & 63);
-      kc = n0 + 64 * (tid >> 6);
-    }
-    r.ok = step < nsteps && n < g.rows && kc < g.cols;
-    const int64_t blk = n * kblocks + (kc >> 6);
-    const uint32_t off = r.ok ? (uint32_t)((n * g.cols + kc) >> 1) : kOOB;
-    const uint32_t off8 = r.ok ? (uint32_t)blk : kOOB;
-    const uint32_t offs = r.ok ? (uint32_t)((blk >> 8) * 4) : kOOB;
-    r.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(codes_rs, off, 0, 0));
-    r.c1 = __builtin_bit_cast(u32x4_t,
-                              __builtin_amdgcn_raw_buffer_load_b128(codes_rs, off + 16, 0, 0));
-    r.code8 = __builtin_amdgcn_raw_buffer_load_b8(code8_rs, off8, 0, 0);
-    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s2_rs, offs, 0, 0));
-  };
-
-  // dequantise words (2w, 2w+1) of `r` with `lut` into stage `bs`
-  auto store_w = [&](uint16_t* bs, const Nf4Lut& lut, const CodeRegs& r, int w) {
-    const u32x4_t& src = (w < 2) ? r.c0 : r.c1;
-    uint32_t d0[4], d1[4];
-    dequant8(lut, src[(2 * w) & 3], d0);
-    dequant8(lut, src[(2 * w + 1) & 3], d1);
-    if (!kBwd) {
-      *reinterpret_cast<u32x4_t*>(bs + swz_a(tid, 2 * w)) = u32x4_t{d0[0], d0[1], d0[2], d0[3]};
-      *reinterpret_cast<u32x4_t*>(bs + swz_a(tid, 2 * w + 1)) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
-    } else {
-      const int row = tid & 63;
-      const int chunk = 8 * (tid >> 6) + 2 * w;
-      *reinterpret_cast<u32x4_t*>(bs + swz_bt(row, chunk)) = u32x4_t{d0[0], d0[1], d0[2], d0[3]};
-      *reinterpret_cast<u32x4_t*>(bs + swz_bt(row, chunk + 1)) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
-    }
-  };
-  auto lut_of = [&](const CodeRegs& r) {
-    const float cp = r.ok ? block_constant(r.code8, r.s2, mu) : 0.0f;   // 0: invalid rows
-    return make_lut(cp);
-  };
-
-  // MFMA fragments of slice s from stages (as, bs)
-  auto load_frags = [&](const uint16_t* as, const uint16_t* bs, int s, u32x4_t* fa, u32x4_t* fb) {
-    const int chunk = 2 * s + lhi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = ld_lds16(as + swz_a(128 * wm + 32 * i + l32, chunk));
-    if (!kBwd) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = ld_lds16(bs + swz_a(128 * wn + 32 * j + l32, chunk));
-    } else {
-      // rows 16 s + 8 lhi + 4 rr + (lane % 16) / 4, columns col0 .. col0 + 3
-      const int r0 = 16 * s + 8 * lhi + ((lane & 15) >> 2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col0 = 128 * wn + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        fb[j] = ld_lds_tr(bs + swz_bt(r0, col0 >> 3) + (col0 & 7),
-                          bs + swz_bt(r0 + 4, col0 >> 3) + (col0 & 7));
-      }
-    }
-  };
+  (void)lane;
 
   // ---- prologue ------------------------------------------------------------
-  CodeRegs cr_cur, cr_nxt;
-  issue_act(0);
-  issue_codes(0, cr_cur);
-  issue_act(1);
-  issue_codes(1, cr_nxt);
+  CodeRegs cur, nxt;
+  issue_act(c, sa0, 0);
+  issue_codes(c, 0, cur);
+  issue_act(c, sa1, 1);
+  issue_codes(c, 1, nxt);
   {
-    const Nf4Lut lut = lut_of(cr_cur);
+    const Nf4Lut lut = lut_of(c, cur);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) store_w(Bs0, lut, cr_cur, w);
+    for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, cur, w);
   }
-  cr_cur = cr_nxt;
+  cur = nxt;
   barrier_keep_vmem<kVmemPerStep>();   // activation stage 0 complete
 
   u32x4_t fa[2][4], fb[2][4];
-  load_frags(As0, Bs0, 0, fa[0], fb[0]);
+  load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
 
-  for (int step = 0; step < nsteps; ++step) {
-    const uint16_t* as = As0 + (step % kAStages) * kStageElems;
-    const uint16_t* bs = Bs0 + (step & 1) * kStageElems;
-    const uint16_t* as_n = As0 + ((step + 1) % kAStages) * kStageElems;
-    uint16_t* bs_n = Bs0 + ((step + 1) & 1) * kStageElems;
-
-    issue_act(step + 2);
-    issue_codes(step + 2, cr_nxt);
-    const Nf4Lut lut = lut_of(cr_cur);
-
-    // slices 0..2: 16 MFMAs each, interleaved with the next slice's fragment
-    // reads and half of a word pair's dequantisation + stores
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int f = s & 1;
-      load_frags(as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
-      store_w(bs_n, lut, cr_cur, s);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-      }
-    }
-    // slice 3: last word pair, then the barrier ahead of the final 4 MFMAs
-    {
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
-      store_w(bs_n, lut, cr_cur, 3);
-#pragma unroll
-      for (int q = 0; q < 12; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-      barrier_keep_vmem<kVmemPerStep>();   // stage step+1 ready everywhere
-      u32x4_t ga[4], gb[4];
-      load_frags(as_n, bs_n, 0, ga, gb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[0][i] = ga[i];
-        fb[0][i] = gb[i];
-      }
-    }
-    cr_cur = cr_nxt;
+  for (int step = 0; step < c.nsteps; step += 6) {
+    gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cur, nxt);
+    if (step + 1 >= c.nsteps) break;
+    gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, cur, nxt);
+    if (step + 2 >= c.nsteps) break;
+    gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cur, nxt);
+    if (step + 3 >= c.nsteps) break;
+    gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, cur, nxt);
+    if (step + 4 >= c.nsteps) break;
+    gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cur, nxt);
+    if (step + 5 >= c.nsteps) break;
+    gemm_step<kBwd, 2, 1>(c, step + 5, acc, fa, fb, cur, nxt);
   }
 
   // ---- epilogue: round to bf16 and store ------------------------------------
