@@ -183,21 +183,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   float* P = ws_ptr<float>(ws, L.proj_off);
   float* PG = ws_ptr<float>(ws, L.grad_off);
 
-  hipError_t e = launch_transpose_bf16(B, d.rows, r, Bt, d.rows, st);
-  if (e == hipSuccess) e = launch_transpose_bf16(A, r, d.cols, At, r, st);
-  // G = dY B  (and G^T for dA)
+  // B^T, A^T and (if the forward's U is given) U^T in one launch
+  TransposeJobs tj;
+  tj.n = 0;
+  tj.job[tj.n++] = TransposeJob{B, d.rows, r, Bt, d.rows};
+  tj.job[tj.n++] = TransposeJob{A, r, d.cols, At, r};
+  if (U_saved) tj.job[tj.n++] = TransposeJob{U_saved, T, r, Ut, L.t_pad};
+  hipError_t e = launch_transposes(tj, st);
+  // G = dY B: (s G) for the dX seed, G^T for dA
   if (e == hipSuccess) e = launch_lora_proj_partial(dY, Bt, T, d.rows, r, L.s_proj_dy, P, st);
   if (e == hipSuccess)
     e = launch_lora_proj_reduce(P, T, r, L.s_proj_dy, nullptr, Gs, scale, Gt, L.t_pad, st);
-  // U^T for dB: from the forward's U, or recomputed as X A^T
-  if (e == hipSuccess) {
-    if (U_saved) {
-      e = launch_transpose_bf16(U_saved, T, r, Ut, L.t_pad, st);
-    } else {
-      e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
-      if (e == hipSuccess)
-        e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, nullptr, 0.0f, Ut, L.t_pad, st);
-    }
+  // U^T for dB when the forward's U was not kept: recompute X A^T
+  if (e == hipSuccess && !U_saved) {
+    e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
+    if (e == hipSuccess)
+      e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, nullptr, 0.0f, Ut, L.t_pad, st);
   }
   // dX = dY dequant(W) + (s G) A
   if (e == hipSuccess) {
@@ -216,11 +217,16 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
     g.T = T;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
-  // dA = s G^T X ; dB = s (U^T dY)^T
-  if (e == hipSuccess) e = launch_lora_grad_partial(Gt, L.t_pad, X, T, d.cols, r, L.s_grad_a, PG, st);
-  if (e == hipSuccess) e = launch_lora_grad_reduce(PG, r, d.cols, L.s_grad_a, scale, 0, dA, st);
-  if (e == hipSuccess) e = launch_lora_grad_partial(Ut, L.t_pad, dY, T, d.rows, r, L.s_grad_b, PG, st);
-  if (e == hipSuccess) e = launch_lora_grad_reduce(PG, r, d.rows, L.s_grad_b, scale, 1, dB, st);
+  // dA = s G^T X and dB = s (U^T dY)^T: partials of both in one launch, then
+  // one fixed-order reduction
+  if (e == hipSuccess) {
+    GradJobs gj;
+    gj.n = 2;
+    gj.job[0] = GradJob{Gt, L.t_pad, X, d.cols, PG, dA, 0};
+    gj.job[1] = GradJob{Ut, L.t_pad, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
+    e = launch_lora_grad_partial(gj, T, r, L.s_grad, st);
+    if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
+  }
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

@@ -48,19 +48,42 @@ hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_
 hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
                                    uint16_t* out_rm, uint16_t* out_sc, float scale,
                                    uint16_t* out_tr, int64_t ld_tr, hipStream_t stream);
-// out[c][r'] = in[r'][c] for a [R, C] bf16 matrix; out has row stride ld_out
-// and is zero for R <= r' < ld_out.
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t R, int64_t C, uint16_t* out,
-                                 int64_t ld_out, hipStream_t stream);
-// Partials C[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q]; St [r, ld_st]
-// bf16 (zero beyond T), L [T, Q] bf16.
+// Up to three bf16 transposes in one launch: out[c][r'] = in[r'][c] for an
+// [R, C] input; out has row stride ld_out and is zero for R <= r' < ld_out.
+struct TransposeJob {
+  const uint16_t* in;
+  int64_t R, C;
+  uint16_t* out;
+  int64_t ld_out;
+};
+struct TransposeJobs {
+  TransposeJob job[3];
+  int tiles[3];   // filled by the launcher
+  int n;
+};
+hipError_t launch_transposes(TransposeJobs jobs, hipStream_t stream);
+
+// Adapter-gradient partials and their reduction, up to two problems per
+// launch: P[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q] with St [r, ld_st]
+// bf16 (zero for t >= T), L [T, Q] bf16; then out = scale * sum_s P[s],
+// as [r, Q] (transposed == 0) or [Q, r] (transposed != 0).
+struct GradJob {
+  const uint16_t* St;
+  int64_t ld_st;
+  const uint16_t* L;
+  int64_t Q;
+  float* P;
+  float* out;
+  int transposed;
+};
+struct GradJobs {
+  GradJob job[2];
+  int n;
+};
 int lora_grad_splits(int64_t T, int64_t Q);
-hipError_t launch_lora_grad_partial(const uint16_t* St, int64_t ld_st, const uint16_t* L,
-                                    int64_t T, int64_t Q, int32_t r, int splits, float* P,
+hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
                                     hipStream_t stream);
-// out = scale * sum_s P[s]: transposed == 0 -> out[p][q] ([r, Q]);
-// transposed != 0 -> out[q][p] ([Q, r]).
-hipError_t launch_lora_grad_reduce(const float* P, int32_t r, int64_t Q, int splits, float scale,
-                                   int transposed, float* out, hipStream_t stream);
+hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
+                                   hipStream_t stream);
 
 }  // namespace qlora

@@ -4,76 +4,108 @@
 // (ta-paperlens 勾配は実際どこへ行くのか: only A and B receive gradients;
 //  waylandz 26.2.1/26.2.4: B is [out, r], A is [r, in], scale alpha / r.)
 //
-// All reductions are split into fixed chunks whose float32 partial sums are
-// added in a fixed order by a second kernel: results are run-to-run
-// deterministic (no floating-point atomics).
+// These kernels stream one large activation-shaped operand (X or dY) against
+// a small rank-r one, so they are bound by HBM bandwidth.  Each wave keeps
+// 8-16 loads of 1 KB in flight (unrolled loops, buffer loads whose
+// out-of-range reads return 0 instead of branches).  Reductions are split
+// into fixed chunks whose float32 partial sums are added in a fixed order by
+// a second kernel: every result is run-to-run deterministic (no
+// floating-point atomics).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace qlora {
 
-__device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that reads as 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0ull : bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // ---------------------------------------------------------------------------
-// P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k].  Workgroup = 4 waves, a
-// wave owns 16 rows of L and all r columns; MFMA 16x16x32 with L rows as the
-// A operand and rows of R as the B operand (both reduction-contiguous).
+// P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k]   (L [T, red], R [r, red])
+// Workgroup = 4 waves over 128 rows of L; a wave owns 32 rows (two MFMA
+// 16x16x32 row groups) and all r = 16 NJ columns, and walks its reduction
+// chunk 128 at a time with all 8 L loads and 4 NJ R loads issued first.
 // ---------------------------------------------------------------------------
+template <int NJ>
 __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ R, int64_t T, int64_t red,
-    int r, int64_t chunk, float* __restrict__ P) {
+    int64_t chunk, float* __restrict__ P) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t m0 = (int64_t)blockIdx.x * 128 + wave * 32;
   const int64_t kb = (int64_t)blockIdx.y * chunk;
   const int64_t ke = kb + chunk < red ? kb + chunk : red;
-  const int nj = r >> 4;
-  const int64_t row = m0 + (lane & 15);
-  const bool row_ok = row < T;
-  f32x4_t acc[8];
+  const __amdgpu_buffer_rsrc_t lr = rsrc(L, (uint64_t)T * red * 2);
+  const __amdgpu_buffer_rsrc_t rr = rsrc(R, (uint64_t)(16 * NJ) * red * 2);
+  const int kl = 8 * (lane >> 4);
+  f32x4_t acc[2][NJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = kb; k < ke; k += 32) {
-    const int64_t kk = k + 8 * (lane >> 4);
-    const bool k_ok = kk < ke;
-    u32x4_t a = u32x4_t{0u, 0u, 0u, 0u};
-    if (row_ok && k_ok) a = load16(L + row * red + kk);
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < nj) {
-        u32x4_t b = u32x4_t{0u, 0u, 0u, 0u};
-        if (k_ok) b = load16(R + (int64_t)(16 * j + (lane & 15)) * red + kk);
-        acc[j] = mfma16(a, b, acc[j]);
+    for (int j = 0; j < NJ; ++j) acc[g][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k = kb; k < ke; k += 128) {
+    u32x4_t a[4][2], b[4][NJ];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t kk = k + 32 * u + kl;
+      const bool ok = kk < ke;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int64_t row = m0 + 16 * g + (lane & 15);
+        a[u][g] = bload16(lr, ok && row < T ? (uint32_t)((row * red + kk) * 2) : kOOB);
       }
-    }
-  }
-  float* out = P + (int64_t)blockIdx.y * T * r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < nj) {
+      for (int j = 0; j < NJ; ++j)
+        b[u][j] = bload16(rr, ok ? (uint32_t)(((int64_t)(16 * j + (lane & 15)) * red + kk) * 2)
+                                 : kOOB);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[g][j] = mfma16(a[u][g], b[u][j], acc[g][j]);
+  }
+  float* out = P + (int64_t)blockIdx.y * T * (16 * NJ);
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t t = m0 + 4 * (lane >> 4) + e;
-        if (t < T) out[t * r + 16 * j + (lane & 15)] = acc[j][e];
+        const int64_t t = m0 + 16 * g + 4 * (lane >> 4) + e;
+        if (t < T) out[t * (16 * NJ) + 16 * j + (lane & 15)] = acc[g][j][e];
       }
-    }
-  }
 }
 
 static int64_t proj_chunk(int64_t red, int splits) {
   int64_t c = (red + splits - 1) / splits;
-  return (c + 63) / 64 * 64;
+  return (c + 127) / 128 * 128;
 }
 
 hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_t T,
                                     int64_t red, int32_t r, int splits, float* P,
                                     hipStream_t stream) {
   const int64_t chunk = proj_chunk(red, splits);
-  dim3 grid((unsigned)((T + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(lora_proj_partial_kernel, grid, dim3(256), 0, stream, L, R, T, red, r,
-                     chunk, P);
+  const dim3 grid((unsigned)((T + 127) / 128), (unsigned)splits);
+  switch (r >> 4) {
+#define QLORA_PROJ_CASE(NJ)                                                                   \
+  case NJ:                                                                                    \
+    hipLaunchKernelGGL(lora_proj_partial_kernel<NJ>, grid, dim3(256), 0, stream, L, R, T, red, \
+                       chunk, P);                                                             \
+    break;
+    QLORA_PROJ_CASE(1) QLORA_PROJ_CASE(2) QLORA_PROJ_CASE(3) QLORA_PROJ_CASE(4)
+    QLORA_PROJ_CASE(5) QLORA_PROJ_CASE(6) QLORA_PROJ_CASE(7) QLORA_PROJ_CASE(8)
+#undef QLORA_PROJ_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -112,166 +144,200 @@ hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int spl
 }
 
 // ---------------------------------------------------------------------------
-// out[c][r'] = in[r'][c], 32x32 tiles through shared memory; rows R..ld_out-1
-// of the input side are written as zeros.
+// Up to three bf16 transposes in one launch: out[c][r'] = in[r'][c] for an
+// [R, C] input; out has row stride ld_out and is zero for R <= r' < ld_out.
+// 32 x 32 tiles through shared memory; workgroups are assigned to jobs by
+// the tile counts of the jobs before them.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
-                                                             int64_t R, int64_t C,
-                                                             uint16_t* __restrict__ out,
-                                                             int64_t ld_out) {
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs jobs) {
   __shared__ uint16_t tile[32][33];
+  int b = blockIdx.x;
+  int jdx = 0;
+  while (jdx < jobs.n - 1 && b >= jobs.tiles[jdx]) {
+    b -= jobs.tiles[jdx];
+    ++jdx;
+  }
+  const TransposeJob& jb = jobs.job[jdx];
+  const int64_t tiles_c = (jb.C + 31) / 32;
+  const int64_t c0 = (int64_t)(b % tiles_c) * 32;
+  const int64_t r0 = (int64_t)(b / tiles_c) * 32;
   const int tx = threadIdx.x & 31;
   const int ty = threadIdx.x >> 5;   // 0..7
-  const int64_t c0 = (int64_t)blockIdx.x * 32;
-  const int64_t r0 = (int64_t)blockIdx.y * 32;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t rr = r0 + ty + 8 * k;
     const int64_t cc = c0 + tx;
-    tile[ty + 8 * k][tx] = (rr < R && cc < C) ? in[rr * C + cc] : (uint16_t)0;
+    tile[ty + 8 * k][tx] = (rr < jb.R && cc < jb.C) ? jb.in[rr * jb.C + cc] : (uint16_t)0;
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int64_t cc = c0 + ty + 8 * k;
     const int64_t rr = r0 + tx;
-    if (cc < C && rr < ld_out) out[cc * ld_out + rr] = tile[tx][ty + 8 * k];
+    if (cc < jb.C && rr < jb.ld_out) jb.out[cc * jb.ld_out + rr] = tile[tx][ty + 8 * k];
   }
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t R, int64_t C, uint16_t* out,
-                                 int64_t ld_out, hipStream_t stream) {
-  dim3 grid((unsigned)((C + 31) / 32), (unsigned)((ld_out + 31) / 32));
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, in, R, C, out, ld_out);
+hipError_t launch_transposes(TransposeJobs jobs, hipStream_t stream) {
+  int total = 0;
+  for (int i = 0; i < jobs.n; ++i) {
+    const TransposeJob& j = jobs.job[i];
+    jobs.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
+    total += jobs.tiles[i];
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)total), dim3(256), 0, stream, jobs);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// C[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q].
-// Workgroup = 4 waves over the same 128 columns q; the waves take interleaved
-// 32-token slices of the chunk and their partials are added in a fixed order
-// through shared memory.  The B operand needs 8 consecutive tokens of one
-// column per lane while L is token-major: each lane loads an 8 x 8 tile
-// (8 rows, 16 B each; 16 lanes cover 256 contiguous bytes of a row) and
-// transposes it in registers, which yields operands for 8 columns
-// q = q0 + 8 * (lane % 16) + v, v = 0..7 (one MFMA per v).
+// C[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q], for up to two problems at
+// once (blockIdx.z): the dA partials (St = G^T, L = X) and the dB^T partials
+// (St = U^T, L = dY).  Workgroup = 4 waves over the same 128 columns q; the
+// waves take interleaved 64-token slices of the chunk and their partials are
+// added in a fixed order through shared memory.  The B operand needs 8
+// consecutive tokens of one column per lane while L is token-major: each lane
+// loads an 8 x 8 tile (8 rows, 16 B each; 16 lanes cover 256 contiguous bytes
+// of a row) and transposes it in registers, which yields operands for 8
+// columns q = q0 + 8 (lane % 16) + v, v = 0..7 (one MFMA per v).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void lora_grad_partial_kernel(
-    const uint16_t* __restrict__ St, int64_t ld_st, const uint16_t* __restrict__ L, int64_t T,
-    int64_t Q, int r, int64_t chunk, float* __restrict__ P) {
-  __shared__ f32x4_t red_buf[8 * 8 * 64];
+template <int NP>
+__global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, int64_t T,
+                                                               int64_t chunk) {
+  __shared__ f32x4_t red_buf[NP * 8 * 64];
+  const GradJob& jb = jobs.job[blockIdx.z];
+  const int64_t Q = jb.Q;
+  const int64_t q0 = (int64_t)blockIdx.x * 128;
+  if (q0 >= Q) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t q0 = (int64_t)blockIdx.x * 128;
   const int64_t tb = (int64_t)blockIdx.y * chunk;
   const int64_t te = tb + chunk < T ? tb + chunk : T;
-  const int np = r >> 4;
   const int64_t qc = q0 + 8 * (lane & 15);
-  const bool q_ok = qc < Q;
-  f32x4_t acc[8][8];
+  const __amdgpu_buffer_rsrc_t lr = rsrc(jb.L, (uint64_t)T * Q * 2);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(jb.St, (uint64_t)(16 * NP) * jb.ld_st * 2);
+  f32x4_t acc[NP][8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[p][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = tb + 32 * wave; t0 < te; t0 += 128) {
-    const int64_t tl = t0 + 8 * (lane >> 4);
-    u32x4_t in[8];
+  for (int64_t t0 = tb + 64 * wave; t0 < te; t0 += 256) {
+    u32x4_t in[2][8];
+    u32x4_t sa[2][NP];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      in[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (q_ok && tl + i < te) in[i] = load16(L + (tl + i) * Q + qc);
-    }
-    u32x4_t bop[8];
+    for (int h = 0; h < 2; ++h) {
+      const int64_t tl = t0 + 32 * h + 8 * (lane >> 4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+      for (int i = 0; i < 8; ++i)
+        in[h][i] = bload16(lr, (tl + i < te && qc < Q) ? (uint32_t)(((tl + i) * Q + qc) * 2) : kOOB);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        bop[2 * c][d] = perm(in[2 * d + 1][c], in[2 * d][c], 0x05040100u);
-        bop[2 * c + 1][d] = perm(in[2 * d + 1][c], in[2 * d][c], 0x07060302u);
-      }
+      for (int p = 0; p < NP; ++p)
+        sa[h][p] = bload16(sr, (uint32_t)(((int64_t)(16 * p + (lane & 15)) * jb.ld_st + tl) * 2));
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (p < np) {
-        const u32x4_t a = load16(St + (int64_t)(16 * p + (lane & 15)) * ld_st + tl);
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t bop[8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[p][v] = mfma16(a, bop[v], acc[p][v]);
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          bop[2 * c][d] = perm(in[h][2 * d + 1][c], in[h][2 * d][c], 0x05040100u);
+          bop[2 * c + 1][d] = perm(in[h][2 * d + 1][c], in[h][2 * d][c], 0x07060302u);
+        }
       }
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[p][v] = mfma16(sa[h][p], bop[v], acc[p][v]);
     }
   }
   // fixed-order sum of the 4 waves: ((w0 + w1) + w2) + w3
   for (int w = 1; w < 4; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        if (p < np)
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int v = 0; v < 8; ++v) red_buf[(p * 8 + v) * 64 + lane] = acc[p][v];
+        for (int v = 0; v < 8; ++v) red_buf[(p * 8 + v) * 64 + lane] = acc[p][v];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        if (p < np)
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int v = 0; v < 8; ++v) acc[p][v] += red_buf[(p * 8 + v) * 64 + lane];
+        for (int v = 0; v < 8; ++v) acc[p][v] += red_buf[(p * 8 + v) * 64 + lane];
     }
     __syncthreads();
   }
-  if (wave == 0 && q_ok) {
-    float* out = P + (int64_t)blockIdx.y * r * Q;
+  if (wave == 0 && qc < Q) {
+    float* out = jb.P + (int64_t)blockIdx.y * (16 * NP) * Q;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (p < np) {
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pr = 16 * p + 4 * (lane >> 4) + e;
-          f32x4_t lo = f32x4_t{acc[p][0][e], acc[p][1][e], acc[p][2][e], acc[p][3][e]};
-          f32x4_t hi = f32x4_t{acc[p][4][e], acc[p][5][e], acc[p][6][e], acc[p][7][e]};
-          f32x4_t* dst = reinterpret_cast<f32x4_t*>(out + (int64_t)pr * Q + qc);
-          dst[0] = lo;
-          dst[1] = hi;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int pr = 16 * p + 4 * (lane >> 4) + e;
+        f32x4_t lo = f32x4_t{acc[p][0][e], acc[p][1][e], acc[p][2][e], acc[p][3][e]};
+        f32x4_t hi = f32x4_t{acc[p][4][e], acc[p][5][e], acc[p][6][e], acc[p][7][e]};
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(out + (int64_t)pr * Q + qc);
+        dst[0] = lo;
+        dst[1] = hi;
       }
     }
   }
 }
 
-hipError_t launch_lora_grad_partial(const uint16_t* St, int64_t ld_st, const uint16_t* L,
-                                    int64_t T, int64_t Q, int32_t r, int splits, float* P,
+hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
                                     hipStream_t stream) {
   int64_t chunk = (T + splits - 1) / splits;
-  chunk = (chunk + 127) / 128 * 128;
-  dim3 grid((unsigned)((Q + 127) / 128), (unsigned)splits);
-  hipLaunchKernelGGL(lora_grad_partial_kernel, grid, dim3(256), 0, stream, St, ld_st, L, T, Q, r,
-                     chunk, P);
+  chunk = (chunk + 255) / 256 * 256;
+  int64_t qmax = 0;
+  for (int i = 0; i < jobs.n; ++i) qmax = jobs.job[i].Q > qmax ? jobs.job[i].Q : qmax;
+  const dim3 grid((unsigned)((qmax + 127) / 128), (unsigned)splits, (unsigned)jobs.n);
+  switch (r >> 4) {
+#define QLORA_GRAD_CASE(NP)                                                                  \
+  case NP:                                                                                   \
+    hipLaunchKernelGGL(lora_grad_partial_kernel<NP>, grid, dim3(256), 0, stream, jobs, T,    \
+                       chunk);                                                               \
+    break;
+    QLORA_GRAD_CASE(1) QLORA_GRAD_CASE(2) QLORA_GRAD_CASE(3) QLORA_GRAD_CASE(4)
+    QLORA_GRAD_CASE(5) QLORA_GRAD_CASE(6) QLORA_GRAD_CASE(7) QLORA_GRAD_CASE(8)
+#undef QLORA_GRAD_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(const float* __restrict__ P,
-                                                               int r, int64_t Q, int splits,
-                                                               float scale, int transposed,
-                                                               float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)r * Q) return;
+// out = scale * sum_s P[s] for each job: transposed == 0 -> out[p][q] ([r, Q]),
+// transposed != 0 -> out[q][p] ([Q, r]).  All jobs in one launch.
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradJobs jobs, int r, int splits,
+                                                               float scale) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int jdx = 0;
+  while (jdx < jobs.n && i >= (int64_t)r * jobs.job[jdx].Q) {
+    i -= (int64_t)r * jobs.job[jdx].Q;
+    ++jdx;
+  }
+  if (jdx >= jobs.n) return;
+  const GradJob& jb = jobs.job[jdx];
+  const int64_t Q = jb.Q;
   float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += P[(int64_t)s * r * Q + i];
+  for (int s = 0; s < splits; ++s) v += jb.P[(int64_t)s * r * Q + i];
   v *= scale;
-  if (!transposed) {
-    out[i] = v;
+  if (!jb.transposed) {
+    jb.out[i] = v;
   } else {
     const int64_t p = i / Q;
     const int64_t q = i - p * Q;
-    out[q * r + p] = v;
+    jb.out[q * r + p] = v;
   }
 }
 
-hipError_t launch_lora_grad_reduce(const float* P, int32_t r, int64_t Q, int splits, float scale,
-                                   int transposed, float* out, hipStream_t stream) {
-  const int64_t n = (int64_t)r * Q;
+hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
+                                   hipStream_t stream) {
+  int64_t n = 0;
+  for (int i = 0; i < jobs.n; ++i) n += (int64_t)r * jobs.job[i].Q;
   hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     stream, P, r, Q, splits, scale, transposed, out);
+                     stream, jobs, r, splits, scale);
   return hipGetLastError();
 }
 

@@ -7,15 +7,14 @@
 
 namespace qlora {
 
-// Split counts of the LoRA side reductions: enough workgroups to cover the
-// chip (~512 for the projections, ~256 of 4 waves for the gradients) while
-// keeping the float32 partial buffers small.
+// Split counts of the LoRA side reductions: about 256 workgroups of 4 waves
+// (one per CU) while keeping the float32 partial buffers small.
 int lora_proj_splits(int64_t T, int64_t red) {
-  const int64_t rb = (T + 63) / 64;
-  int64_t s = (512 + rb - 1) / rb;
-  const int64_t max_s = (red + 63) / 64;
+  const int64_t rb = (T + 127) / 128;
+  int64_t s = (256 + rb - 1) / rb;
+  const int64_t max_s = (red + 127) / 128;
   if (s > max_s) s = max_s;
-  if (s > 16) s = 16;
+  if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -23,7 +22,7 @@ int lora_proj_splits(int64_t T, int64_t red) {
 int lora_grad_splits(int64_t T, int64_t Q) {
   const int64_t qb = (Q + 127) / 128;
   int64_t s = (256 + qb - 1) / qb;
-  const int64_t max_s = (T + 127) / 128;
+  const int64_t max_s = (T + 255) / 256;
   if (s > max_s) s = max_s;
   if (s > 16) s = 16;
   if (s < 1) s = 1;
@@ -74,8 +73,7 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
   memset(&L, 0, sizeof(L));
   L.s_proj_x = lora_proj_splits(T, d.cols);
   L.s_proj_dy = lora_proj_splits(T, d.rows);
-  L.s_grad_a = lora_grad_splits(T, d.cols);
-  L.s_grad_b = lora_grad_splits(T, d.rows);
+  L.s_grad = lora_grad_splits(T, d.cols > d.rows ? d.cols : d.rows);
   L.t_pad = (T + 31) / 32 * 32;
   size_t off = 0;
   const int s_proj = bwd ? (L.s_proj_x > L.s_proj_dy ? L.s_proj_x : L.s_proj_dy) : L.s_proj_x;
@@ -94,10 +92,10 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
     off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
     L.ut_off = off;
     off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
-    const size_t ga = (size_t)L.s_grad_a * (size_t)r * (size_t)d.cols;
-    const size_t gb = (size_t)L.s_grad_b * (size_t)r * (size_t)d.rows;
     L.grad_off = off;
-    off += align_up(sizeof(float) * (ga > gb ? ga : gb), kWsAlign);
+    off += align_up(sizeof(float) * (size_t)L.s_grad * (size_t)r * (size_t)d.cols, kWsAlign);
+    L.grad_b_off = off;
+    off += align_up(sizeof(float) * (size_t)L.s_grad * (size_t)r * (size_t)d.rows, kWsAlign);
   }
   L.total = off;
   return L;
