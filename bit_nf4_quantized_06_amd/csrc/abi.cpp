@@ -151,7 +151,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
     g.r = r;
     g.out = Y;
     g.T = T;
-    e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
+    if (L.s_gemv > 0) {
+      float* Pg = ws_ptr<float>(ws, L.gemv_off);
+      e = timed(QLORA_TIMING_FWD_GEMM, st,
+                [&] { return launch_qlora_gemv(g, Pg, L.s_gemv, st); });
+    } else {
+      e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
+    }
   }
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }

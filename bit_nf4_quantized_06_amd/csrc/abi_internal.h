@@ -10,6 +10,10 @@
 namespace qlora {
 
 constexpr size_t kWsAlign = 256;
+
+// Token counts up to this use the skinny forward (gemv.hip).
+constexpr int64_t kGemvMaxTokens = 64;
+int gemv_splits(int64_t rows, int64_t cols);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WeightDims {
@@ -34,9 +38,12 @@ struct LinearWs {
   int s_proj_dy;    // split count of dY B over rows
   int s_grad;       // split count of G^T X and U^T dY over tokens
   int64_t t_pad;    // token stride of the transposed G / U (multiple of 32)
-  size_t proj_off, u_off, bt_off, at_off, g_off, gt_off, ut_off, grad_off, grad_b_off, total;
+  int s_gemv;       // split count of the skinny forward (0: fused GEMM path)
+  size_t proj_off, u_off, gemv_off, bt_off, at_off, g_off, gt_off, ut_off, grad_off, grad_b_off, total;
 };
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd);
+
+bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
 
 qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
                                WeightDims* d);

@@ -35,6 +35,10 @@ struct GemmArgs {
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
 
+// Skinny forward for T <= kGemvMaxTokens (gemv.hip): split partials
+// P [splits][T][rows] float32, then Y = bf16(sum_s P + lora_l lora_r^T).
+hipError_t launch_qlora_gemv(const GemmArgs& a, float* P, int splits, hipStream_t stream);
+
 // --- LoRA side products (lora.hip) ----------------------------------------
 // Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k],
 // L [T, red] bf16, R [r, red] bf16, P float32 [S][T][r].

@@ -113,18 +113,38 @@ hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_
 // bf16(v), out_sc[t][p] = bf16(scale * v) (the pre-scaled operand the fused
 // GEMM seeds its accumulators with), out_tr[p][t] = bf16(v) with row stride
 // ld_tr and zeros for T <= t < ld_tr.
+// 64 outputs (t, p) per workgroup; wave q adds splits q, q + 4, q + 8, ...
+// (loads issued 8 at a time), then the four wave sums are added in order q =
+// 0..3: a fixed order for any launch.
 __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(
     const float* __restrict__ P, int64_t T, int r, int splits, uint16_t* __restrict__ out_rm,
     uint16_t* __restrict__ out_sc, float scale, uint16_t* __restrict__ out_tr, int64_t ld_tr,
     int64_t rows_total) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows_total * r) return;
-  const int64_t t = i / r;
-  const int p = (int)(i - t * r);
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = i < rows_total * r;
+  const int64_t t = live ? i / r : 0;
+  const int p = live ? (int)(i - t * r) : 0;
   float v = 0.0f;
-  if (t < T) {
-    for (int s = 0; s < splits; ++s) v += P[((int64_t)s * T + t) * r + p];
+  if (live && t < T) {
+    const float* src = P + t * r + p;
+    const int64_t stride = T * r;
+    int s = q;
+    for (; s + 28 < splits; s += 32) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + 4 * j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += x[j];
+    }
+    for (; s < splits; s += 4) v += src[(int64_t)s * stride];
   }
+  part[q][lane] = v;
+  __syncthreads();
+  if (q != 0 || !live) return;
+  v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
   const uint16_t b = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
   if (t < T) {
     if (out_rm) out_rm[t * r + p] = b;
@@ -138,7 +158,7 @@ hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int spl
                                    uint16_t* out_tr, int64_t ld_tr, hipStream_t stream) {
   const int64_t rows_total = out_tr ? ld_tr : T;
   const int64_t n = rows_total * r;
-  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0,
                      stream, P, T, r, splits, out_rm, out_sc, scale, out_tr, ld_tr, rows_total);
   return hipGetLastError();
 }

@@ -29,6 +29,19 @@ int lora_grad_splits(int64_t T, int64_t Q) {
   return (int)s;
 }
 
+// Split count of the skinny forward: about 1024 workgroups (4 per CU), each
+// wave keeping at least 4 blocks of the reduction.
+int gemv_splits(int64_t rows, int64_t cols) {
+  const int64_t tiles = (rows + 63) / 64;
+  const int64_t kblocks = cols / 64;
+  int64_t s = (1024 + tiles - 1) / tiles;
+  int64_t max_s = kblocks / 16;
+  if (max_s < 1) max_s = 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 qlora_status check_weight_shape(int64_t rows, int64_t cols, WeightDims* d) {
   if (rows < 1 || cols < 64 || (cols % 64) != 0 || (rows % 16) != 0) return QLORA_ERR_SHAPE;
   if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
@@ -42,6 +55,18 @@ qlora_status check_weight_shape(int64_t rows, int64_t cols, WeightDims* d) {
     d->n_g = (d->n_b + 255) / 256;
   }
   return QLORA_OK;
+}
+
+// The linear-layer kernels address the packed codes and each bf16 activation
+// or gradient tensor with 32-bit buffer offsets: every one of them must stay
+// below 2 GiB.
+bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols) {
+  const int64_t kMaxDim = int64_t(1) << 22;
+  const int64_t kMaxElems16 = (int64_t(1) << 30) - 64;   // bf16 elements below 2 GiB
+  if (T < 1 || rows > kMaxDim || cols > kMaxDim) return false;
+  if (rows * cols > 2 * kMaxElems16) return false;      // packed codes below 2 GiB
+  if (T > kMaxElems16 / cols || T > kMaxElems16 / rows) return false;
+  return true;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,12 +100,15 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
   L.s_proj_dy = lora_proj_splits(T, d.rows);
   L.s_grad = lora_grad_splits(T, d.cols > d.rows ? d.cols : d.rows);
   L.t_pad = (T + 31) / 32 * 32;
+  L.s_gemv = (!bwd && T <= kGemvMaxTokens) ? gemv_splits(d.rows, d.cols) : 0;
   size_t off = 0;
   const int s_proj = bwd ? (L.s_proj_x > L.s_proj_dy ? L.s_proj_x : L.s_proj_dy) : L.s_proj_x;
   L.proj_off = off;
   off += align_up(sizeof(float) * (size_t)s_proj * (size_t)T * (size_t)r, kWsAlign);
   L.u_off = off;
   off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
+  L.gemv_off = off;
+  off += align_up(sizeof(float) * (size_t)L.s_gemv * (size_t)T * (size_t)d.rows, kWsAlign);
   if (bwd) {
     L.bt_off = off;
     off += align_up(2 * (size_t)r * (size_t)d.rows, kWsAlign);
@@ -105,7 +133,7 @@ qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, 
                                WeightDims* d) {
   const qlora_status s = check_descriptor(w, d);
   if (s != QLORA_OK) return s;
-  if (T < 1 || T > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  if (T < 1 || !linear_dims_ok(T, d->rows, d->cols)) return QLORA_ERR_SHAPE;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_SHAPE;
   return QLORA_OK;
@@ -150,7 +178,8 @@ size_t qlora_nf4_quantize_workspace(int64_t rows, int64_t cols) {
 size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd) {
   qlora::WeightDims d;
   if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
-  if (T < 1 || T > (int64_t(1) << 31) || r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
+  if (!qlora::linear_dims_ok(T, rows, cols)) return 0;
+  if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
   return qlora::linear_ws_layout(T, d, r, is_bwd != 0).total;
 }
 

@@ -319,12 +319,53 @@ def dequantize_bits(state: dict) -> np.ndarray:
     [PL] 勾配は実際どこへ行くのか: the storage type is NF4, compute is bf16.
     """
     rows, cols = state["rows"], state["cols"]
-    q = nf4_levels()
     codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
     cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
                                      state["absmax_offset"][0])
-    prod = (q[codes] * cprime[:, None]).astype(F32)
-    return bf16_bits_rne(prod).reshape(rows, cols)
+    return _decode_bits(codes, cprime).reshape(rows, cols)
+
+
+def _decode_bits(codes: np.ndarray, cprime: np.ndarray) -> np.ndarray:
+    """bf16_RNE(RN32(q[code] * c')) for codes [n_blocks, 64] and c' [n_blocks]."""
+    q = nf4_levels()
+    prod = (q[codes] * np.asarray(cprime, dtype=F32)[:, None]).astype(F32)
+    return bf16_bits_rne(prod)
+
+
+def quantize_sampled_rows(w: np.ndarray, sel) -> dict:
+    """quantize() of the whole weight, keeping the NF4 codes of rows `sel` only.
+
+    The block constants and their double quantisation cover every block (they
+    are exactly quantize()'s); only the per-element encode is restricted.
+    Meant for sampled checks of weights too large for a full CPU encode.
+    The packed codes are [len(sel), cols // 2]; 'sel' is kept in the state.
+    """
+    w = np.asarray(w, dtype=F32)
+    rows, cols = w.shape
+    assert cols % BLOCK == 0, "cols must be a multiple of 64"
+    sel = np.asarray(sel, dtype=np.int64).reshape(-1)
+    kb = cols // BLOCK
+    c = block_absmax(w)
+    code8, s2, mu = double_quantize(c)
+    codes = nf4_encode(w[sel], c.reshape(rows, kb)[sel])
+    return {
+        "rows": rows, "cols": cols, "sel": sel,
+        "codes": pack_nibbles(codes).reshape(sel.size, cols // 2),
+        "absmax_code": code8,
+        "absmax_scale": s2,
+        "absmax_offset": np.array([mu], dtype=F32),
+    }
+
+
+def dequantize_sampled_bits(state: dict) -> np.ndarray:
+    """dequantize_bits() restricted to the rows of a quantize_sampled_rows()
+    state: uint16 [len(sel), cols]."""
+    rows, cols, sel = state["rows"], state["cols"], state["sel"]
+    kb = cols // BLOCK
+    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
+                                     state["absmax_offset"][0]).reshape(rows, kb)[sel]
+    codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
+    return _decode_bits(codes, cprime.reshape(-1)).reshape(sel.size, cols)
 
 
 def dequantize(state: dict) -> np.ndarray:

@@ -115,6 +115,36 @@ def test_linear_validation():
         assert lib.qlora_linear_workspace(T, 1024, 1024, bad_r, 1) == 0
 
 
+def test_linear_size_limits():
+    """The linear kernels address each bf16 tensor and the packed codes with
+    32-bit offsets: T * rows and T * cols below 2^30 elements, rows * cols
+    below 2^32, rows and cols at most 2^22; everything else is rejected."""
+    lib = _lib.load()
+    ws = lib.qlora_linear_workspace
+    assert ws(8192, 22016, 8192, 64, 1) > 0          # 65B MLP shape, training tokens
+    assert ws(16, 8192, 22016, 64, 0) > 0            # decode
+    assert ws((1 << 30) // 4096, 4096, 4096, 16, 0) == 0
+    assert ws((1 << 30) // 4096 - 1, 4096, 4096, 16, 0) > 0
+    assert ws(16, 1 << 23, 64, 16, 0) == 0           # rows above 2^22
+    assert ws(16, 16, 1 << 23, 16, 0) == 0           # cols above 2^22
+    assert ws(1, 1 << 21, 1 << 21, 16, 0) == 0       # packed codes of 2 TiB
+    d = ctypes.byref(_desc(4096, 4096))
+    big_t = (1 << 30) // 4096
+    assert lib.qlora_linear_fwd(d, FAKE, big_t, FAKE, FAKE, 16, 32.0, FAKE, None, FAKE, 1 << 40,
+                                None) == 2
+
+
+def test_skinny_forward_workspace():
+    """Few tokens take the skinny forward, whose split partials need extra
+    workspace; the backward layout does not depend on it."""
+    lib = _lib.load()
+    ws = lib.qlora_linear_workspace
+    small = ws(64, 8192, 8192, 64, 0)
+    assert small > 4 * 64 * 8192                      # at least one float32 partial
+    assert ws(65, 8192, 8192, 64, 0) < small          # fused GEMM path: no partials
+    assert ws(64, 8192, 8192, 64, 1) > 0
+
+
 def test_timing_hook_validation():
     lib = _lib.load()
     assert lib.qlora_set_timing_events(4, None, None) == 2

@@ -1,0 +1,102 @@
+"""GPU parity of the skinny forward (T <= 64 tokens, the generation case):
+Y and U against the float64 oracle (relative Frobenius error <= 5e-3) at
+small ragged shapes, and at the 65B-style decode shapes (16 tokens) on
+sampled output rows in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from gpu_util import GEMM_TOL, bf16_dev, bits_host, f32_dev, linear_case, oracle_linear
+from oracle import qlora_nf4_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+# (name, T, N=rows=out, K=cols=in, r, alpha)
+CASES = [
+    ("T1_N16_K64_r16", 1, 16, 64, 16, 16.0),
+    ("T16_N1040_K4096_r64", 16, 1040, 4096, 64, 16.0),     # ragged row tile, 4 splits
+    ("T31_N272_K1088_r32", 31, 272, 1088, 32, 32.0),       # 17 blocks per row
+    ("T33_N528_K576_r16", 33, 528, 576, 16, 32.0),         # two token groups
+    ("T64_N256_K2048_r128", 64, 256, 2048, 128, 16.0),     # largest skinny T, largest r
+]
+
+
+def _fwd(inp, alpha):
+    import bit_nf4_quantized_06_amd as q
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B = bf16_dev(inp["x"]), bf16_dev(inp["a"]), bf16_dev(inp["b"])
+    Y, U = q.qlora_linear_fwd(wq, X, A, B, alpha)
+    torch.cuda.synchronize()
+    return wq, X, A, B, Y, U
+
+
+def _val(t):
+    return WL.bf16_bits_value(bits_host(t)).astype(np.float64)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_skinny_forward_parity(case):
+    name, T, N, K, r, alpha = case
+    print(f"[gemv] case={name}", flush=True)
+    inp = linear_case(T, N, K, r, alpha, seed=21, outliers=True)
+    inp.pop("dy")
+    _, _, _, _, Y, U = _fwd(inp, alpha)
+    ref = oracle_linear(inp, O.dequantize(O.quantize(inp["w"])), r, alpha)
+    ey = O.rel_frobenius(_val(Y), ref["y"])
+    eu = O.rel_frobenius(_val(U), ref["u"])
+    print(f"[gemv] {name} rel_frobenius y={ey:.2e} u={eu:.2e}", flush=True)
+    assert ey <= GEMM_TOL and eu <= GEMM_TOL
+
+
+def test_skinny_forward_deterministic_and_b_zero():
+    """Repeated calls give identical bits; with B = 0 the output equals the
+    A = 0 output (the frozen base alone), bit for bit."""
+    T, N, K, r, alpha = 16, 528, 1024, 32, 32.0
+    print("[gemv] determinism / b_zero", flush=True)
+    import bit_nf4_quantized_06_amd as q
+    inp_b0 = linear_case(T, N, K, r, alpha, seed=8, b_zero=True)
+    inp_a0 = linear_case(T, N, K, r, alpha, seed=8, a_zero=True)
+    wq, X, A, B, Y1, _ = _fwd(inp_b0, alpha)
+    Y2, _ = q.qlora_linear_fwd(wq, X, A, B, alpha)
+    _, _, _, _, Ya, _ = _fwd(inp_a0, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(Y1.view(torch.int16), Ya.view(torch.int16))
+
+
+def _decode_cases():
+    wl = WL.WORKLOADS["block_65b_decode"]
+    seen, out = set(), []
+    for li, lin in enumerate(wl.linears):
+        shape = (lin.out_features, lin.in_features)
+        if shape not in seen:
+            seen.add(shape)
+            out.append((lin.name, li))
+    return out
+
+
+@pytest.mark.parametrize("lin", _decode_cases(), ids=[c[0] for c in _decode_cases()])
+def test_decode_65b_full_size_sampled_rows(lin):
+    """The 65B decode block at 16 tokens, one linear of each shape at full
+    size through the same entry point the benchmark times; Y compared on 64
+    sampled output features (plus the first and last), U in full."""
+    name, li = lin
+    wl = WL.WORKLOADS["block_65b_decode"]
+    inp = WL.linear_inputs(wl, li)
+    inp.pop("dy", None)
+    N, K = inp["w"].shape
+    print(f"[gemv] decode {name} W={N}x{K} T={wl.tokens}", flush=True)
+    _, _, _, _, Y, U = _fwd(inp, wl.alpha)
+    sel = np.sort(np.random.default_rng(li).choice(N, 64, replace=False))
+    sel = np.unique(np.concatenate([sel, [0, N - 1]]))
+    st = O.quantize_sampled_rows(inp["w"], sel)
+    w_rows = O.bf16_bits_to_f32(O.dequantize_sampled_bits(st)).astype(np.float64)
+    x = WL.bf16_bits_value(inp["x"]).astype(np.float64)
+    a = WL.bf16_bits_value(inp["a"]).astype(np.float64)
+    b = WL.bf16_bits_value(inp["b"]).astype(np.float64)[sel]
+    y_ref, u_ref = O.linear_forward(x, w_rows, a, b, wl.alpha, wl.rank)
+    ey = O.rel_frobenius(_val(Y)[:, sel], y_ref)
+    eu = O.rel_frobenius(_val(U), u_ref)
+    print(f"[gemv] decode {name} rel_frobenius y={ey:.2e} u={eu:.2e}", flush=True)
+    assert ey <= GEMM_TOL and eu <= GEMM_TOL

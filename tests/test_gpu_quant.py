@@ -113,22 +113,14 @@ def test_bulk_8192x22016_full_constants_sampled_rows():
     out = dequantize(wq)
     torch.cuda.synchronize()
     got = state_host(wq)
-    c = O.block_absmax(w)
-    code8, s2, mu = O.double_quantize(c)
-    assert np.float32(got["absmax_offset"][0]) == mu
-    assert np.array_equal(got["absmax_scale"].view(np.uint32), s2.view(np.uint32))
-    assert np.array_equal(got["absmax_code"], code8)
     sel = np.sort(np.random.default_rng(0).choice(rows, 48, replace=False))
     sel = np.unique(np.concatenate([sel, [0, rows - 1]]))
-    kb = cols // 64
-    c_rows = c.reshape(rows, kb)[sel]
-    codes = O.nf4_encode(w[sel], c_rows).reshape(len(sel), cols)
-    packed = O.pack_nibbles(codes).reshape(len(sel), cols // 2)
+    ref = O.quantize_sampled_rows(w, sel)
+    assert np.float32(got["absmax_offset"][0]) == ref["absmax_offset"][0]
+    assert np.array_equal(got["absmax_scale"].view(np.uint32), ref["absmax_scale"].view(np.uint32))
+    assert np.array_equal(got["absmax_code"], ref["absmax_code"])
     got_codes = got["codes"].reshape(rows, cols // 2)[sel]
-    assert np.array_equal(got_codes, packed)
-    cprime = O.block_constants_from_dq(code8, s2, mu).reshape(rows, kb)[sel]
-    q = O.nf4_levels()
-    prod = (q[codes].reshape(len(sel), kb, 64) * cprime[:, :, None]).astype(np.float32)
-    ref_bits = O.bf16_bits_rne(prod).reshape(len(sel), cols)
+    assert np.array_equal(got_codes, ref["codes"])
+    ref_bits = O.dequantize_sampled_bits(ref)
     got_bits = bits_host(out[torch.from_numpy(sel).to(out.device)])
     assert np.array_equal(got_bits, ref_bits)

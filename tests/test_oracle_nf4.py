@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import workloads as WL
 from oracle import qlora_nf4_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -210,3 +211,17 @@ def test_storage_bits_closed_form(rows, cols):
     no_dq = 4 + 32 / 64
     assert no_dq == gold["storage_bits_without_double_quant"]["value"]
     assert round(no_dq - bits, 3) == gold["saving_bits"]["value"]
+
+
+def test_sampled_rows_equal_full_quantize_rows():
+    """The sampled-row helpers (used for checks at full size) agree with the
+    full quantize / dequantize on every selected row, including the first and
+    last row and rows whose blocks straddle DQ-group boundaries."""
+    w = WL.weight(96, 704, seed=13, outliers=True)     # 1056 blocks, 5 DQ groups
+    sel = np.array([0, 5, 23, 24, 71, 95])
+    full = O.quantize(w)
+    part = O.quantize_sampled_rows(w, sel)
+    for k in ("absmax_code", "absmax_scale", "absmax_offset"):
+        assert np.array_equal(np.asarray(part[k]).view(np.uint8), np.asarray(full[k]).view(np.uint8))
+    assert np.array_equal(part["codes"], full["codes"].reshape(96, 352)[sel])
+    assert np.array_equal(O.dequantize_sampled_bits(part), O.dequantize_bits(full)[sel])
