@@ -132,6 +132,30 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   const float scale = alpha / (float)r;
+  if (L.s_gemv > 0) {
+    // few tokens: U = X A^T and X dequant(W)^T in one streaming pass
+    GemvArgs ga;
+    ga.X = X;
+    ga.codes = w->codes;
+    ga.code8 = w->absmax_code;
+    ga.s2 = w->absmax_scale;
+    ga.mu = w->absmax_offset;
+    ga.rows = d.rows;
+    ga.cols = d.cols;
+    ga.T = T;
+    ga.A = A;
+    ga.B = B;
+    ga.r = r;
+    ga.scale = scale;
+    ga.Y = Y;
+    ga.U_save = U_save;
+    ga.P = ws_ptr<float>(ws, L.gemv_off);
+    ga.PU = ws_ptr<float>(ws, L.gemv_u_off);
+    ga.splits = L.s_gemv;
+    const hipError_t e =
+        timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_gemv(ga, st); });
+    return e == hipSuccess ? QLORA_OK : hip_fail(e);
+  }
   uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * X A^T)
   float* P = ws_ptr<float>(ws, L.proj_off);
   hipError_t e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
@@ -151,13 +175,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
     g.r = r;
     g.out = Y;
     g.T = T;
-    if (L.s_gemv > 0) {
-      float* Pg = ws_ptr<float>(ws, L.gemv_off);
-      e = timed(QLORA_TIMING_FWD_GEMM, st,
-                [&] { return launch_qlora_gemv(g, Pg, L.s_gemv, st); });
-    } else {
-      e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
-    }
+    e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
   }
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }

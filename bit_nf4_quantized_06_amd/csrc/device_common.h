@@ -49,13 +49,12 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// OCP FP8 E4M3 value of a bit pattern, times 2^-8, as float32 (exact).
-// Exponent field 0 is subnormal: m * 2^-9 (times 2^-8 = m * 2^-17).
+// OCP FP8 E4M3 value of a bit pattern (low byte of `code`), times 2^-8, as
+// float32.  v_cvt_f32_fp8 decodes the OCP format exactly on gfx950 (every
+// finite pattern; the quantiser never emits the NaN patterns 0x7F / 0xFF);
+// the scaling by 2^-8 is exact for every finite pattern.
 __device__ __forceinline__ float e4m3_decode_scaled(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u;
-  const uint32_t m = code & 7u;
-  float v = e ? __uint_as_float(((e + 112u) << 23) | (m << 20)) : (float)m * 0x1p-17f;
-  return (code & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * 0x1p-8f;
 }
 
 // OCP FP8 E4M3 bit pattern nearest to x, ties to even; |x| <= 256 assumed

@@ -1,35 +1,36 @@
 // Skinny forward of the QLoRA linear layer for few tokens (T <= 64):
-//   Y = X dequant(W)^T + (s X A^T) B^T.
+//   Y = X dequant(W)^T + s (X A^T) B^T,   U = X A^T.
 // ta-paperlens 落とし穴: the 4-bit format pays off in generation with small
 // batches, which is bound by how many weight bytes are read.  Here every
-// weight meets at most 64 tokens, so the kernel is built to read the packed
+// weight meets at most 64 tokens, so the kernels are built to read the packed
 // weight once (0.516 B per weight with its constants) and to dequantise each
-// weight exactly once, in registers.
+// weight exactly once, in registers.  Two launches:
 //
-// Mapping.  A workgroup of 4 waves owns 64 weight rows and one split of the
-// reduction; the waves take the 64-wide NF4 blocks of that split in turn
-// (wave w: blocks w, w+4, ...), so together they stream 128 contiguous bytes
-// of every row.  Each wave computes C[token][row] for 32 (or 64) tokens x 64
-// rows with MFMA 32x32x16: the weight is the B operand (lane l holds row
-// l % 32 of the row group and half l / 32 of the block, i.e. 32 codes = 16
-// bytes), the activations are the A operand (lane l holds token l % 32, the
-// same half of the block).  Inside one MFMA the pairing of reduction indices
-// with operand slots is free as long as both operands agree, so the weights
-// are produced in the order the byte lookups give them -- elements
-// (0,2,4,6,1,3,5,7) of each code word -- and the activations are permuted
-// to that order instead (4 byte permutes per 8 activations, shared by both
-// row groups).
-//
-// Dequantisation: for its row and block a lane decodes c' from the 8-bit code
-// and the group's scale and offset, forms the 16-entry bf16 table q[k] * c'
-// (float32 product, one rounding, as the bulk dequantiser) and translates
-// nibbles with byte permutes; no dequantised tile is stored anywhere.
-//
-// The LoRA term (s U) B^T seeds the accumulators of the first split (one
-// more MFMA chain).  The four waves' float32 partial tiles are summed in LDS
-// in a fixed order and written as one split partial; a finishing kernel adds
-// the splits in order and rounds once to bf16 (a single split is rounded and
-// stored directly).
+// 1. qlora_gemv_partial_kernel.  A workgroup of 4 waves owns 64 output rows
+//    and one split of the reduction; the waves take the 64-wide blocks of that
+//    split in turn (wave w: blocks w, w+4, ...), so together they stream 128
+//    contiguous bytes of every weight row.  The row tiles past the weight's
+//    rows are the r rows of the LoRA factor A, read as plain bf16: U = X A^T
+//    is formed by the same launch as X dequant(W)^T.
+//    Each wave computes C[token][row] for 32 (or 64) tokens x 64 rows with
+//    MFMA 32x32x16: the weight is the B operand (lane l holds row l % 32 of a
+//    32-row group and half l / 32 of the block: 32 codes = 16 bytes), the
+//    activations are the A operand (lane l: token l % 32, same half).  Inside
+//    one MFMA the pairing of reduction indices with operand slots is free as
+//    long as both operands agree, so the weights are produced in the order
+//    the byte lookups give them -- elements (0,2,4,6,1,3,5,7) of each code
+//    word -- and the activations are permuted to that order (4 byte permutes
+//    per 8 activations, shared by both row groups).
+//    Dequantisation: c' is decoded from the 8-bit code (hardware FP8
+//    conversion) and the group's scale and offset; the 16-entry bf16 table
+//    q[k] * c' (float32 product, one rounding, as the bulk dequantiser) is
+//    built half by half -- the two lanes that share a row each form 8
+//    entries and exchange them with v_permlane32_swap -- and nibbles are
+//    translated with byte permutes.  The four waves' float32 tiles are added
+//    in LDS in a fixed order and stored as one split partial.
+// 2. qlora_gemv_finish_kernel.  U = sum of the A-tile partials (fixed order),
+//    stored as bf16 and, scaled by s, kept in LDS as bf16; the LoRA term
+//    (s U) B^T comes from MFMA 32x32x16 and Y = bf16(sum_s P + LoRA).
 #include "abi_internal.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -72,7 +73,7 @@ __device__ __forceinline__ u32x4_t dequant8_eo(const Nf4Lut& t, uint32_t w) {
   return o;
 }
 
-// 8 consecutive bf16 activations to the same slot order.
+// 8 consecutive bf16 values to the same slot order.
 __device__ __forceinline__ u32x4_t act_eo(const u32x4_t& d) {
   u32x4_t o;
   o[0] = perm(d[1], d[0], 0x05040100u);
@@ -82,43 +83,68 @@ __device__ __forceinline__ u32x4_t act_eo(const u32x4_t& d) {
   return o;
 }
 
-template <int TG>
+// Table of one row's block, lanes l and l + 32 holding the same c': lane half
+// h forms entries 8h .. 8h+7 (kq = the levels 8h .. 8h+7) as byte planes and
+// the halves are exchanged.
+__device__ __forceinline__ Nf4Lut make_lut_pair(float cp, const float kq[8]) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pack_bf16x2(__fmul_rn(kq[2 * j], cp), __fmul_rn(kq[2 * j + 1], cp));
+  const uint32_t lo_a = perm(p[1], p[0], 0x06040200u);
+  const uint32_t lo_b = perm(p[3], p[2], 0x06040200u);
+  const uint32_t hi_a = perm(p[1], p[0], 0x07050301u);
+  const uint32_t hi_b = perm(p[3], p[2], 0x07050301u);
+  // permlane32_swap(x, x): first result = lower half's x in every lane,
+  // second = upper half's x in every lane.
+  const auto sa = __builtin_amdgcn_permlane32_swap(lo_a, lo_a, false, false);
+  const auto sb = __builtin_amdgcn_permlane32_swap(lo_b, lo_b, false, false);
+  const auto sc = __builtin_amdgcn_permlane32_swap(hi_a, hi_a, false, false);
+  const auto sd = __builtin_amdgcn_permlane32_swap(hi_b, hi_b, false, false);
+  Nf4Lut t;
+  t.lo[0] = sa[0];
+  t.lo[1] = sb[0];
+  t.lo[2] = sa[1];
+  t.lo[3] = sb[1];
+  t.hi[0] = sc[0];
+  t.hi[1] = sd[0];
+  t.hi[2] = sc[1];
+  t.hi[3] = sd[1];
+  return t;
+}
+
+template <int TG, bool kLora>
 struct GemvStage {
-  u32x4_t code[2];       // 16 bytes of codes per row group
-  u32x4_t x[TG][4];      // 32 activations per token group
+  u32x4_t w[2][kLora ? 4 : 1];   // NF4: 16 code bytes per row group; A: 32 bf16
   uint32_t c8[2];
   float s2[2];
+  u32x4_t x[TG][4];              // 32 activations per token group
 };
 
-}  // namespace
-
-// TG = token groups of 32 (T <= 32 TG).  Grid: (ceil(rows / 64), splits).
-template <int TG>
-__global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int steps_per,
-                                                                 float* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) float red[3 * TG * 2 * 16 * 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// acc[tg][ng] += X[tokens of tg][k] * Wrow[ng][k] over the blocks st0 + wave,
+// st0 + wave + 4, ... below st1.
+template <int TG, bool kLora>
+__device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t st0,
+                                          int64_t st1, int wave, int lane,
+                                          f32x16_t (&acc)[TG][2]) {
   const int half = lane >> 5;
-  const int64_t N = g.rows, K = g.cols;
+  const int64_t K = g.cols;
   const int64_t kblocks = K >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
-  const int64_t st0 = (int64_t)blockIdx.y * steps_per;
-  const int64_t st1 = st0 + steps_per < kblocks ? st0 + steps_per : kblocks;
-  const float mu = g.mu[0];
-
-  const __amdgpu_buffer_rsrc_t xr = rsrc_v(g.act, (uint64_t)g.T * K * 2);
-  const __amdgpu_buffer_rsrc_t cr = rsrc_v(g.codes, (uint64_t)(N * K) >> 1);
-  const __amdgpu_buffer_rsrc_t c8r = rsrc_v(g.code8, (uint64_t)(N * kblocks));
-  const __amdgpu_buffer_rsrc_t s2r = rsrc_v(g.s2, (uint64_t)((N * kblocks + 255) >> 8) * 4);
+  const int64_t nrows = kLora ? g.r : g.rows;
+  const __amdgpu_buffer_rsrc_t xr = rsrc_v(g.X, (uint64_t)g.T * K * 2);
+  const __amdgpu_buffer_rsrc_t wr =
+      kLora ? rsrc_v(g.A, (uint64_t)g.r * K * 2) : rsrc_v(g.codes, (uint64_t)(g.rows * K) >> 1);
+  const __amdgpu_buffer_rsrc_t c8r = rsrc_v(g.code8, (uint64_t)(g.rows * kblocks));
+  const __amdgpu_buffer_rsrc_t s2r =
+      rsrc_v(g.s2, (uint64_t)((g.rows * kblocks + 255) >> 8) * 4);
+  const float mu = kLora ? 0.0f : g.mu[0];
 
   bool row_ok[2];
   int64_t row[2];
 #pragma unroll
   for (int ng = 0; ng < 2; ++ng) {
     row[ng] = n0 + 32 * ng + (lane & 31);
-    row_ok[ng] = row[ng] < N;
+    row_ok[ng] = row[ng] < nrows;
   }
   bool tok_ok[TG];
   int64_t xbase[TG];
@@ -128,17 +154,26 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int
     tok_ok[tg] = t < g.T;
     xbase[tg] = (t * K + 32 * half) * 2;
   }
+  float kq[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kq[j] = half ? kNF4[8 + j] : kNF4[j];
 
-  auto load = [&](int64_t st, bool ok, GemvStage<TG>& s) {
+  auto load = [&](int64_t st, bool ok, GemvStage<TG, kLora>& s) {
 #pragma unroll
     for (int ng = 0; ng < 2; ++ng) {
       const bool v = ok && row_ok[ng];
-      const int64_t blk = row[ng] * kblocks + st;
-      s.code[ng] = load16(cr, v ? (uint32_t)(blk * 32 + 16 * half) : kOOBv);
-      s.c8[ng] = __builtin_amdgcn_raw_buffer_load_b8(c8r, v ? (uint32_t)blk : kOOBv, 0, 0);
-      s.s2[ng] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(s2r, v ? (uint32_t)((blk >> 8) * 4) : kOOBv,
-                                                      0, 0));
+      if (kLora) {
+        const uint32_t off = v ? (uint32_t)((row[ng] * K + st * 64 + 32 * half) * 2) : kOOBv;
+#pragma unroll
+        for (int q = 0; q < (kLora ? 4 : 1); ++q) s.w[ng][q] = load16(wr, off + 16 * q);
+      } else {
+        const int64_t blk = row[ng] * kblocks + st;
+        s.w[ng][0] = load16(wr, v ? (uint32_t)(blk * 32 + 16 * half) : kOOBv);
+        s.c8[ng] = __builtin_amdgcn_raw_buffer_load_b8(c8r, v ? (uint32_t)blk : kOOBv, 0, 0);
+        s.s2[ng] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       s2r, v ? (uint32_t)((blk >> 8) * 4) : kOOBv, 0, 0));
+      }
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -148,35 +183,7 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int
     }
   };
 
-  f32x16_t acc[TG][2];
-#pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-    for (int ng = 0; ng < 2; ++ng)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[tg][ng][e] = 0.0f;
-
-  // The first split's wave 0 starts from the LoRA term (s U) B^T of its
-  // tile (U pre-scaled), so every output gets it exactly once.
-  if (blockIdx.y == 0 && wave == 0) {
-    const __amdgpu_buffer_rsrc_t ur = rsrc_v(g.lora_l, (uint64_t)g.T * g.r * 2);
-    const __amdgpu_buffer_rsrc_t br = rsrc_v(g.lora_r, (uint64_t)N * g.r * 2);
-    for (int p0 = 0; p0 < g.r; p0 += 16) {
-      const int p = p0 + 8 * half;
-#pragma unroll
-      for (int ng = 0; ng < 2; ++ng) {
-        const u32x4_t bv = load16(br, row_ok[ng] ? (uint32_t)((row[ng] * g.r + p) * 2) : kOOBv);
-#pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          const u32x4_t av = load16(
-              ur, tok_ok[tg] ? (uint32_t)(((32 * tg + (lane & 31)) * g.r + p) * 2) : kOOBv);
-          acc[tg][ng] = mfma32(av, bv, acc[tg][ng]);
-        }
-      }
-    }
-  }
-
-  GemvStage<TG> cur, nxt;
+  GemvStage<TG, kLora> cur, nxt;
   int64_t st = st0 + wave;
   load(st, st < st1, cur);
   for (; st < st1; st += 4) {
@@ -188,17 +195,57 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int
       for (int q = 0; q < 4; ++q) a[tg][q] = act_eo(cur.x[tg][q]);
 #pragma unroll
     for (int ng = 0; ng < 2; ++ng) {
-      const float cp = row_ok[ng] ? block_constant(cur.c8[ng], cur.s2[ng], mu) : 0.0f;
-      const Nf4Lut lt = make_lut(cp);
+      if (kLora) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t b = dequant8_eo(lt, cur.code[ng][q]);
+        for (int q = 0; q < 4; ++q) {
+          const u32x4_t b = act_eo(cur.w[ng][kLora ? q : 0]);
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
+          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
+        }
+      } else {
+        const float cp = row_ok[ng] ? block_constant(cur.c8[ng], cur.s2[ng], mu) : 0.0f;
+        const Nf4Lut lt = make_lut_pair(cp, kq);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4_t b = dequant8_eo(lt, cur.w[ng][0][q]);
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
+        }
       }
     }
     cur = nxt;
   }
+}
+
+}  // namespace
+
+// Grid: (w_tiles + LoRA tiles, splits); TG = token groups of 32.
+template <int TG>
+__global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemvArgs g, int w_tiles,
+                                                                 int steps_per) {
+  __shared__ __attribute__((aligned(16))) float red[3 * TG * 2 * 16 * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int64_t kblocks = g.cols >> 6;
+  const bool lora = (int)blockIdx.x >= w_tiles;
+  const int64_t n0 = (int64_t)(lora ? (int)blockIdx.x - w_tiles : (int)blockIdx.x) * 64;
+  const int64_t nrows = lora ? g.r : g.rows;
+  const int64_t st0 = (int64_t)blockIdx.y * steps_per;
+  const int64_t st1 = st0 + steps_per < kblocks ? st0 + steps_per : kblocks;
+
+  f32x16_t acc[TG][2];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int ng = 0; ng < 2; ++ng)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tg][ng][e] = 0.0f;
+  if (lora)
+    gemv_tile<TG, true>(g, n0, st0, st1, wave, lane, acc);
+  else
+    gemv_tile<TG, false>(g, n0, st0, st1, wave, lane, acc);
 
   // ---- fixed-order sum of the four waves' tiles, one split partial -------
   if (wave > 0) {
@@ -212,12 +259,12 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int
   }
   __syncthreads();
   if (wave == 0) {
-    const bool direct = gridDim.y == 1;
-    float* out = P + (int64_t)blockIdx.y * g.T * N;
+    float* out = (lora ? g.PU : g.P) + (int64_t)blockIdx.y * g.T * nrows;
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-      for (int ng = 0; ng < 2; ++ng)
+      for (int ng = 0; ng < 2; ++ng) {
+        const int64_t n = n0 + 32 * ng + (lane & 31);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int idx = ((tg * 2 + ng) * 16 + e) * 64 + lane;
@@ -226,52 +273,138 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemmArgs g, int
           v += red[TG * 2 * 16 * 64 + idx];
           v += red[2 * TG * 2 * 16 * 64 + idx];
           const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (t < g.T && row_ok[ng]) {
-            if (direct)
-              g.out[t * N + row[ng]] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-            else
-              out[t * N + row[ng]] = v;
-          }
+          if (t < g.T && n < nrows) out[t * nrows + n] = v;
         }
+      }
   }
 }
 
-// Y = bf16(sum_s P[s]) over the flattened [T, rows] outputs, 4 per thread,
-// splits added in order.
-__global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(int64_t n4, int splits,
-                                                                const float* __restrict__ P,
-                                                                uint16_t* __restrict__ Y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const f32x4_t* p4 = reinterpret_cast<const f32x4_t*>(P);
-  f32x4_t v = p4[i];
-  for (int s = 1; s < splits; ++s) {
-    const f32x4_t w = p4[(int64_t)s * n4 + i];
-    v[0] += w[0];
-    v[1] += w[1];
-    v[2] += w[2];
-    v[3] += w[3];
+// Grid: ceil(rows / 128); wave w owns rows 128 blockIdx.x + 32 w .. + 31.
+template <int TG>
+__global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t us[64 * 128];   // bf16(s U) [t][p]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int64_t N = g.rows, T = g.T;
+  const int r = g.r;
+  const int splits = g.splits;
+
+  // ---- U = sum over splits of the A-tile partials (fixed order) -----------
+  // 4 entries per thread and round, 8 splits per batch of loads; splits past
+  // the end read the last split and add 0.
+  const int64_t TR = T * r;
+  for (int64_t e0 = 0; e0 < TR; e0 += 1024) {
+    int64_t ei[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ei[j] = e0 + tid + 256 * j;
+      if (ei[j] >= TR) ei[j] = TR - 1;
+    }
+    float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float x[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sc = s0 + i < splits ? s0 + i : splits - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[i][j] = g.PU[(int64_t)sc * TR + ei[j]];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] += s0 + i < splits ? x[i][j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = e0 + tid + 256 * j;
+      if (e < TR) {
+        us[e] = (uint16_t)(pack_bf16x2(u[j] * g.scale, 0.0f) & 0xFFFFu);
+        if (blockIdx.x == 0 && g.U_save)
+          g.U_save[e] = (uint16_t)(pack_bf16x2(u[j], 0.0f) & 0xFFFFu);
+      }
+    }
   }
-  uint2 o;
-  o.x = pack_bf16x2(v[0], v[1]);
-  o.y = pack_bf16x2(v[2], v[3]);
-  reinterpret_cast<uint2*>(Y)[i] = o;
+  __syncthreads();
+
+  // ---- LoRA term (s U) B^T by MFMA, plus the W partials ----------------------
+  const int64_t n = (int64_t)blockIdx.x * 128 + 32 * wave + (lane & 31);
+  const __amdgpu_buffer_rsrc_t br = rsrc_v(g.B, (uint64_t)N * r * 2);
+  f32x16_t acc[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[tg][e] = 0.0f;
+  for (int p0 = 0; p0 < r; p0 += 16) {
+    const int p = p0 + 8 * half;
+    const u32x4_t b = load16(br, n < N ? (uint32_t)((n * r + p) * 2) : kOOBv);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      // token rows past T read stale table entries; they only reach output
+      // rows that are never stored
+      const int t = 32 * tg + (lane & 31);
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(us + t * r + p);
+      acc[tg] = mfma32(a, b, acc[tg]);
+    }
+  }
+  if (n >= N) return;
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    // rows past T are read from row T - 1 (loads stay unconditional) and
+    // never stored
+    int64_t off[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
+      off[e] = (t < T ? t : T - 1) * N + n;
+    }
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float x[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sc = s0 + i < splits ? s0 + i : splits - 1;
+        const float* ps = g.P + (int64_t)sc * T * N;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[i][e] = ps[off[e]];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] += s0 + i < splits ? x[i][e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
+      if (t < T) g.Y[t * N + n] = (uint16_t)(pack_bf16x2(v[e] + acc[tg][e], 0.0f) & 0xFFFFu);
+    }
+  }
 }
 
-hipError_t launch_qlora_gemv(const GemmArgs& a, float* P, int splits, hipStream_t stream) {
+hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream) {
   const int64_t kblocks = a.cols / 64;
-  if (a.T < 1 || a.T > kGemvMaxTokens || splits < 1 || splits > kblocks) return hipErrorInvalidValue;
-  const int per = (int)((kblocks + splits - 1) / splits);
-  const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)splits);
-  if (a.T <= 32)
-    hipLaunchKernelGGL(qlora_gemv_partial_kernel<1>, grid, dim3(256), 0, stream, a, per, P);
-  else
-    hipLaunchKernelGGL(qlora_gemv_partial_kernel<2>, grid, dim3(256), 0, stream, a, per, P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  const int64_t n4 = a.T * a.rows / 4;
-  hipLaunchKernelGGL(qlora_gemv_finish_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                     stream, n4, splits, P, a.out);
+  if (a.T < 1 || a.T > kGemvMaxTokens || a.splits < 1 || a.splits > kblocks || a.r < 16 ||
+      a.r > 128)
+    return hipErrorInvalidValue;
+  const int per = (int)((kblocks + a.splits - 1) / a.splits);
+  const int w_tiles = (int)((a.rows + 63) / 64);
+  const int l_tiles = (a.r + 63) / 64;
+  const dim3 grid((unsigned)(w_tiles + l_tiles), (unsigned)a.splits);
+  const dim3 fgrid((unsigned)((a.rows + 127) / 128));
+  if (a.T <= 32) {
+    hipLaunchKernelGGL(qlora_gemv_partial_kernel<1>, grid, dim3(256), 0, stream, a, w_tiles, per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(qlora_gemv_finish_kernel<1>, fgrid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(qlora_gemv_partial_kernel<2>, grid, dim3(256), 0, stream, a, w_tiles, per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(qlora_gemv_finish_kernel<2>, fgrid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

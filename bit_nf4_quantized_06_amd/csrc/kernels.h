@@ -35,9 +35,27 @@ struct GemmArgs {
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
 
-// Skinny forward for T <= kGemvMaxTokens (gemv.hip): split partials
-// P [splits][T][rows] float32, then Y = bf16(sum_s P + lora_l lora_r^T).
-hipError_t launch_qlora_gemv(const GemmArgs& a, float* P, int splits, hipStream_t stream);
+// Skinny forward for T <= kGemvMaxTokens (gemv.hip): split partials of
+// X dequant(W)^T (P) and of U = X A^T (PU), then
+// Y = bf16(sum_s P + bf16(scale U) B^T) and U_save = bf16(U).
+struct GemvArgs {
+  const uint16_t* X;       // [T, cols] bf16
+  const uint8_t* codes;    // packed weight [rows, cols]
+  const uint8_t* code8;
+  const float* s2;
+  const float* mu;
+  int64_t rows, cols, T;
+  const uint16_t* A;       // [r, cols] bf16
+  const uint16_t* B;       // [rows, r] bf16
+  int32_t r;
+  float scale;             // alpha / r
+  uint16_t* Y;             // [T, rows] bf16
+  uint16_t* U_save;        // [T, r] bf16 or NULL
+  float* P;                // [splits][T][rows]
+  float* PU;               // [splits][T][r]
+  int32_t splits;
+};
+hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream);
 
 // --- LoRA side products (lora.hip) ----------------------------------------
 // Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k],
