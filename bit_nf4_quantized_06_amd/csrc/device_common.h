@@ -79,6 +79,14 @@ __device__ __forceinline__ float block_constant(uint32_t code8, float s2, float 
   return __fadd_rn(__fmul_rn(e4m3_decode_scaled(code8), s2), mu);
 }
 
+// c' of a block, or +0 for a block outside the weight (a mask, not a branch,
+// so the surrounding straight-line schedule is kept).
+__device__ __forceinline__ float block_constant_or_zero(bool ok, uint32_t code8, float s2,
+                                                        float mu) {
+  const float v = block_constant(code8, s2, mu);
+  return __uint_as_float(__float_as_uint(v) & (ok ? 0xFFFFFFFFu : 0u));
+}
+
 // 16-entry bf16 lookup table of one block, q[k] * c' rounded once to bf16,
 // split into byte planes for v_perm lookups:
 //   lo[i] byte j = low byte of entry 4i+j, hi[i] byte j = high byte.

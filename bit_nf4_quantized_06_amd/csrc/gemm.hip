@@ -205,7 +205,7 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
 
 template <bool kBwd>
 __device__ __forceinline__ Nf4Lut lut_of(const GemmCtx<kBwd>& c, const CodeRegs& r) {
-  const float cp = r.ok ? block_constant(r.code8, r.s2, c.mu) : 0.0f;   // 0: rows past the end
+  const float cp = block_constant_or_zero(r.ok, r.code8, r.s2, c.mu);   // 0: rows past the end
   return make_lut(cp);
 }
 
@@ -323,7 +323,9 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   GemmCtx<kBwd> c{g, {sa0, sa1, sa2}, {sb0, sb1}};
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
-  c.wave = c.tid >> 6;
+  // wave index through readfirstlane: provably uniform, so the DMA scalar
+  // offsets and LDS bases derived from it stay in SGPRs
+  c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
   c.wm = c.wave >> 1;
   c.wn = c.wave & 1;
   c.l32 = c.lane & 31;

@@ -203,7 +203,7 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
           for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
         }
       } else {
-        const float cp = row_ok[ng] ? block_constant(cur.c8[ng], cur.s2[ng], mu) : 0.0f;
+        const float cp = block_constant_or_zero(row_ok[ng], cur.c8[ng], cur.s2[ng], mu);
         const Nf4Lut lt = make_lut_pair(cp, kq);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
