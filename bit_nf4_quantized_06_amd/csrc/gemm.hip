@@ -7,35 +7,38 @@
 // dequant(W)^T; W is never written.  Ultralytics "So funktioniert QLoRA":
 // dequantise right before the matmul and add the LoRA path.
 //
-// Kernel shape.  A workgroup of 4 waves (one per SIMD) computes a 256-token x
-// 256-column output tile with float32 accumulators; each wave owns a
-// 128 x 128 sub-tile held as 4 x 4 MFMA 32x32x16 blocks (256 AGPRs).  The
-// reduction advances 64 per step, i.e. one NF4 block per weight row.
+// Kernel shape.  A workgroup of 8 waves computes a 256-token x 256-column
+// output tile with float32 accumulators; the reduction advances 64 per step,
+// i.e. one NF4 block per weight row.  Waves w and w + 4 share a SIMD and
+// split one 128 x 128 quadrant into two 128 x 64 halves (4 x 2 MFMA
+// 32x32x16 blocks, 128 AGPRs each).  With two waves per SIMD one wave's
+// MFMAs keep the matrix core busy while the other waits on its loads, its
+// LDS traffic or the dequantisation work; a single wave per SIMD cannot hide
+// the VMEM issue stalls of the activation stream.
 //
 // Operands, both read from LDS:
 //   * activations (X or dY), 256 x 64 bf16 per step, are fetched straight
 //     into LDS by buffer loads (no registers), two steps ahead, into a ring
-//     of three 32 KB stages;
+//     of three 32 KB stages (4 loads of 1 KB per wave and step);
 //   * the weight tile is dequantised once per workgroup into one of two
-//     32 KB stages.  Each thread owns one block of 64 weights per step: its
-//     32 bytes of packed codes arrive in registers two steps ahead; it builds
-//     the 16-entry bf16 table q[k] * c' (16 float32 products rounded once,
-//     as the bulk dequantiser does) and translates its nibbles with v_perm
-//     byte lookups.  The tile keeps W's own row layout in both directions;
-//     the backward reads its operand (reduction = W rows) with
-//     ds_read_b64_tr_b16, which hands each lane 4 consecutive rows of one
-//     column.
+//     32 KB stages.  Each pair of adjacent lanes owns one block of 64
+//     weights per step, each lane 32 of them: its 16 bytes of packed codes
+//     arrive in registers two steps ahead; it builds the 16-entry bf16 table
+//     q[k] * c' (16 float32 products rounded once, as the bulk dequantiser
+//     does) and translates its nibbles with v_perm byte lookups.  The tile
+//     keeps W's own row layout in both directions; the backward reads its
+//     operand (reduction = W rows) with ds_read_b64_tr_b16, which hands each
+//     lane 4 consecutive rows of one column.
 // All out-of-range rows and columns are handled by buffer-descriptor range
-// checks (reads past the end return 0), so every 16-MFMA slice is a single
+// checks (reads past the end return 0), so every 8-MFMA slice is a single
 // basic block.  Within a slice the MFMAs are interleaved with the
-// dequantisation VALU work, the LDS stores of the next stage and the
-// fragment reads of the next slice (sched_group_barrier).  The one barrier
-// per step sits before the last four MFMAs of the step, so the first
-// fragments of the next step are read while they run.
+// dequantisation VALU work, the LDS store of the next stage and the fragment
+// reads of the next slice (sched_group_barrier).  The one barrier per step
+// sits before the last two MFMAs of the step, so the first fragments of the
+// next step are read while they run.
 //
-// LDS layouts (16-byte chunks XOR-swizzled so that every ds_read_b128,
-// ds_read_b64_tr_b16 and ds_write_b128 pattern used here touches 16 distinct
-// 16-byte bank groups per 256 bytes):
+// LDS layouts (16-byte chunks XOR-swizzled; measured with the LDS bank
+// conflict counter against unswizzled and other XOR layouts):
 //   activation / forward weight tile: 256 rows x 8 chunks,
 //       chunk' = chunk ^ ((row >> 1) & 7)
 //   backward weight tile: 64 rows (W rows) x 32 chunks (256 W columns),
@@ -57,7 +60,9 @@ constexpr int kStageElems = BM * BK;           // 16384 bf16 = 32 KB
 constexpr int kAStages = 3;
 constexpr int kBStages = 2;
 constexpr uint32_t kOOB = 0x80000000u;         // buffer offset that reads as 0
-constexpr int kVmemPerStep = 12;               // 8 activation DMAs + 4 code loads
+constexpr int kThreads = 512;                  // 8 waves
+constexpr int kActLoads = 4;                   // activation DMAs per wave and step
+constexpr int kVmemPerStep = kActLoads + 3;    // + codes, 8-bit code, group scale
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -131,7 +136,7 @@ struct GemmCtx {
   const GemmArgs& g;
   uint16_t* A[kAStages];
   uint16_t* B[kBStages];
-  int tid, lane, wave, wm, wn, l32, lhi, nsteps;
+  int tid, lane, wave, wm, wn, wg, l32, lhi, nsteps;
   int64_t m0, n0, red_len, kblocks;
   float mu;
   // buffer ranges (base, bytes) of the operands read with range checking
@@ -139,26 +144,32 @@ struct GemmCtx {
   uint32_t act_bytes, codes_bytes, code8_bytes, s2_bytes;
   // per-lane byte offsets that do not change with the step
   uint32_t act_voff[2];     // activation DMA, even / odd 8-row block
-  uint32_t code_voff;       // this thread's packed codes at step 0
-  int64_t blk0;             // this thread's block index at step 0
-  bool w_row_ok;            // this thread's weight block lies inside W
+  uint32_t code_voff;       // this lane's 16 code bytes at step 0
+  int64_t blk0;             // this lane's block index at step 0
+  bool w_row_ok;            // this lane's weight block lies inside W
+  int wrow;                 // backward: W row of the block within the step
+  // forward only (the backward keeps a whole table per lane: its transposed
+  // fragments leave no registers for the split):
+  float kq[kBwd ? 1 : 8];   // NF4 levels 8h .. 8h+7 of this lane's table half
+  uint32_t code_flip;       // 0x88888888 on lanes holding the upper table half first
   // per-lane LDS element offsets inside a stage (loop invariant); the row
-  // blocks i (+32 rows) and, in the backward weight tile, the slices (+16
-  // rows) are constant additions folded into instruction offsets
+  // blocks i (+32 rows), column blocks j and, in the backward weight tile,
+  // the slices (+16 rows) are constant additions folded into instruction
+  // offsets
   int a_frag[4];            // activation fragment, slice s, row block 0
-  int b_frag[8];            // forward: [s]; backward: [2 j + rr] for slice 0
-  int w_store[8];           // dequantised chunk w of this thread's block
+  int b_frag[4];            // forward: [s]; backward: [2 j + rr] for slice 0
+  int w_store[4];           // dequantised chunk w of this lane's half block
 };
 
 struct CodeRegs {
-  u32x4_t c0, c1;
+  u32x4_t c;                // 32 codes: 4 words of 8
   uint32_t code8;
   float s2;
   bool ok;
 };
 
 // Activation DMA of step `step` into `stage`: wave w, load i fills LDS bytes
-// [(8 w + i) KB, +1 KB) of the stage, i.e. tile rows 8 (8 w + i) .. +8.  The
+// [(4 w + i) KB, +1 KB) of the stage, i.e. tile rows 8 (4 w + i) .. +8.  The
 // swizzle of a row only depends on the lane and on the parity of i, so each
 // lane has two fixed byte offsets; the row block and the step enter through
 // the scalar offset.  Columns past the end of the reduction (the last step
@@ -170,16 +181,16 @@ __device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stag
   const uint32_t sbase = step < c.nsteps ? (uint32_t)(step * BK * 2) : kOOB;
   const uint32_t row_bytes = (uint32_t)(c.red_len * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t soff = step < c.nsteps ? sbase + (uint32_t)((c.wave * 8 + i) * 8) * row_bytes
-                                          : kOOB;
+  for (int i = 0; i < kActLoads; ++i) {
+    const int blk8 = c.wave * kActLoads + i;
+    const uint32_t soff = step < c.nsteps ? sbase + (uint32_t)(blk8 * 8) * row_bytes : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.act_base, c.act_bytes),
-                                             (lds_void_t*)(stage + (c.wave * 8 + i) * 512), 16,
+                                             (lds_void_t*)(stage + blk8 * 512), 16,
                                              c.act_voff[i & 1], soff, 0, 0);
   }
 }
 
-// packed codes and block-constant inputs of this thread's block at `step`
+// packed codes and block-constant inputs of this lane's half block at `step`
 template <bool kBwd>
 __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, CodeRegs& r) {
   // forward: the block moves along the row (+32 B, +1 block per step);
@@ -187,15 +198,12 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
   const bool in = step < c.nsteps;
   const int64_t dblk = kBwd ? (int64_t)step * 64 * c.kblocks : (int64_t)step;
   const uint32_t dcode = kBwd ? (uint32_t)((int64_t)step * 64 * (c.g.cols >> 1)) : (uint32_t)(step * 32);
-  int64_t n_ok_rows = c.g.rows - (kBwd ? (int64_t)step * 64 : 0);
-  r.ok = in && c.w_row_ok && (!kBwd || (c.tid & 63) < n_ok_rows);
+  const int64_t n_ok_rows = c.g.rows - (kBwd ? (int64_t)step * 64 : 0);
+  r.ok = in && c.w_row_ok && (!kBwd || c.wrow < n_ok_rows);
   const uint32_t scode = in ? dcode : kOOB;
   const int64_t blk = c.blk0 + dblk;
-  const __amdgpu_buffer_rsrc_t codes_rs = make_rsrc(c.g.codes, c.codes_bytes);
-  r.c0 = __builtin_bit_cast(u32x4_t,
-                            __builtin_amdgcn_raw_buffer_load_b128(codes_rs, c.code_voff, scode, 0));
-  r.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                         codes_rs, c.code_voff + 16, scode, 0));
+  r.c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                        make_rsrc(c.g.codes, c.codes_bytes), c.code_voff, scode, 0));
   r.code8 = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(c.g.code8, c.code8_bytes),
                                                 r.ok ? (uint32_t)blk : kOOB, 0, 0);
   r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -203,22 +211,46 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
                                        r.ok ? (uint32_t)((blk >> 8) * 4) : kOOB, 0, 0));
 }
 
+// Table of this lane pair's block.  Forward: lane half h = lane & 1 forms
+// entries 8h .. 8h+7 (kq = those levels) as byte planes, the neighbour lane
+// supplies the other 8 (DPP quad_perm [1,0,3,2]); lanes with h = 1 hold the
+// two halves swapped and flip bit 3 of their codes instead (code_flip).
+// Backward: the whole table per lane.
 template <bool kBwd>
 __device__ __forceinline__ Nf4Lut lut_of(const GemmCtx<kBwd>& c, const CodeRegs& r) {
   const float cp = block_constant_or_zero(r.ok, r.code8, r.s2, c.mu);   // 0: rows past the end
-  return make_lut(cp);
+  if (kBwd) return make_lut(cp);
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pack_bf16x2(__fmul_rn(c.kq[2 * j], cp), __fmul_rn(c.kq[2 * j + 1], cp));
+  uint32_t own[4], nb[4];
+  own[0] = perm(p[1], p[0], 0x06040200u);   // low bytes of own entries 0..3
+  own[1] = perm(p[3], p[2], 0x06040200u);   // low bytes of own entries 4..7
+  own[2] = perm(p[1], p[0], 0x07050301u);   // high bytes
+  own[3] = perm(p[3], p[2], 0x07050301u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    nb[q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)own[q], 0xB1, 0xF, 0xF, false);
+  Nf4Lut t;
+  t.lo[0] = own[0];
+  t.lo[1] = own[1];
+  t.lo[2] = nb[0];
+  t.lo[3] = nb[1];
+  t.hi[0] = own[2];
+  t.hi[1] = own[3];
+  t.hi[2] = nb[2];
+  t.hi[3] = nb[3];
+  return t;
 }
 
-// dequantise words (2w, 2w+1) of `r` into weight stage `bs`
+// dequantise word w of `r` (8 weights) into weight stage `bs`
 template <bool kBwd>
 __device__ __forceinline__ void store_w(const GemmCtx<kBwd>& c, uint16_t* bs, const Nf4Lut& lut,
                                         const CodeRegs& r, int w) {
-  const u32x4_t& src = (w < 2) ? r.c0 : r.c1;
-  uint32_t d0[4], d1[4];
-  dequant8(lut, src[(2 * w) & 3], d0);
-  dequant8(lut, src[(2 * w + 1) & 3], d1);
-  *reinterpret_cast<u32x4_t*>(bs + c.w_store[2 * w]) = u32x4_t{d0[0], d0[1], d0[2], d0[3]};
-  *reinterpret_cast<u32x4_t*>(bs + c.w_store[2 * w + 1]) = u32x4_t{d1[0], d1[1], d1[2], d1[3]};
+  uint32_t d[4];
+  dequant8(lut, kBwd ? r.c[w] : (r.c[w] ^ c.code_flip), d);
+  *reinterpret_cast<u32x4_t*>(bs + c.w_store[w]) = u32x4_t{d[0], d[1], d[2], d[3]};
 }
 
 // MFMA fragments of slice s from stages (as, bs)
@@ -229,26 +261,26 @@ __device__ __forceinline__ void load_frags(const GemmCtx<kBwd>& c, const uint16_
   for (int i = 0; i < 4; ++i) fa[i] = ld_lds16(as + c.a_frag[s] + 32 * i * BK);
   if (!kBwd) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = ld_lds16(bs + c.b_frag[s] + 32 * j * BK);
+    for (int j = 0; j < 2; ++j) fb[j] = ld_lds16(bs + c.b_frag[s] + 32 * j * BK);
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       fb[j] = ld_lds_tr(bs + c.b_frag[2 * j] + 16 * s * BN, bs + c.b_frag[2 * j + 1] + 16 * s * BN);
   }
 }
 
-// Interleave pattern of one 16-MFMA slice: each MFMA is followed by `v`
-// VALU ops; the first 8 also carry one LDS read (next slice's fragments),
-// two of the later ones an LDS store, and the first four one VMEM load.
-template <int V, bool kVmem>
+// Interleave pattern of one 8-MFMA slice: each MFMA is followed by `V`
+// VALU ops; the first NR also carry one LDS read (next slice's fragments),
+// the first NM one VMEM load, and MFMA 5 the LDS store.
+template <int V, int NR, int NM>
 __device__ __forceinline__ void slice_schedule() {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < 8; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (q < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    if (kVmem && q < 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (q < NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-    if (q == 9 || q == 13) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (q == 5) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   }
 }
 
@@ -256,10 +288,11 @@ __device__ __forceinline__ void slice_schedule() {
 // fa[0], fb[0] hold slice 0 of this step and `cur` the codes of step+1; on
 // exit fa[0], fb[0] hold slice 0 of step+1 and `cur` the codes of step+2.
 template <bool kBwd, int SA, int SB>
-__device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][4],
-                                          u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][4],
+__device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][2],
+                                          u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][2],
                                           CodeRegs& cur, CodeRegs& nxt) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins; the host pass needs no body
+  constexpr int kReads = kBwd ? 8 : 6;   // LDS read instructions per slice
   const uint16_t* as = c.A[SA];
   const uint16_t* bs = c.B[SB];
   uint16_t* as_next = c.A[(SA + 1) % kAStages];
@@ -276,44 +309,43 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
     store_w(c, bs_next, lut, cur, s);
     if (s == 0)
-      slice_schedule<6, true>();
+      slice_schedule<8, kReads, kVmemPerStep>();
     else
-      slice_schedule<4, false>();
+      slice_schedule<4, kReads, 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
-  // slice 3: 12 MFMAs with the last word pair, barrier, next step's first
-  // fragments under the remaining 4 MFMAs
+  // slice 3: 6 MFMAs with the last word, barrier, next step's first
+  // fragments under the remaining 2 MFMAs
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
   store_w(c, bs_next, lut, cur, 3);
 #pragma unroll
-  for (int q = 0; q < 12; ++q) {
+  for (int q = 0; q < 6; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    if (q == 5 || q == 9) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (q == 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   barrier_keep_vmem<kVmemPerStep>();   // stage step+1 complete and visible
-  u32x4_t ga[4], gb[4];
+  u32x4_t ga[4], gb[2];
   load_frags(c, as_next, bs_next, 0, ga, gb);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
+  for (int j = 0; j < 2; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[0][i] = ga[i];
-    fb[0][i] = gb[i];
-  }
+  for (int i = 0; i < 4; ++i) fa[0][i] = ga[i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[0][j] = gb[j];
   cur = nxt;
 #endif
 }
 
 template <bool kBwd>
-__global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[kStageElems];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[kStageElems];
   __shared__ __attribute__((aligned(1024))) uint16_t sa2[kStageElems];
@@ -326,8 +358,10 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   // wave index through readfirstlane: provably uniform, so the DMA scalar
   // offsets and LDS bases derived from it stay in SGPRs
   c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
-  c.wm = c.wave >> 1;
-  c.wn = c.wave & 1;
+  const int simd = c.wave & 3;   // waves w and w + 4 share a SIMD
+  c.wm = simd >> 1;
+  c.wn = simd & 1;
+  c.wg = c.wave >> 2;            // which 64-column half of the quadrant
   c.l32 = c.lane & 31;
   c.lhi = c.lane >> 5;
   c.red_len = kBwd ? g.rows : g.cols;
@@ -342,6 +376,7 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   c.kblocks = g.cols >> 6;
   c.mu = g.mu[0];
   const int64_t rows_here = (g.T - c.m0) < BM ? (g.T - c.m0) : BM;
+  const int col0 = 128 * c.wn + 64 * c.wg;   // first output column of this wave in the tile
   {
     // activation DMA lane offsets (see issue_act): row-in-block = lane / 8,
     // swizzle ((row >> 1) & 7) with row bit 3 = parity of the load index
@@ -352,33 +387,43 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
       const int ch = (c.lane & 7) ^ ((row >> 1) & 7);
       c.act_voff[par] = (uint32_t)((rl * c.red_len + 8 * ch) * 2);
     }
+    // weight block of this lane pair: b = tid / 2, half h = tid % 2
+    const int b = c.tid >> 1;
+    const int h = c.tid & 1;
+    if (!kBwd) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c.kq[j] = h ? kNF4[8 + j] : kNF4[j];
+    }
+    c.code_flip = (!kBwd && h) ? 0x88888888u : 0u;
     int64_t n, kc;
     if (!kBwd) {
-      n = c.n0 + c.tid;
-      kc = 0;
+      n = c.n0 + b;              // W row
+      kc = 32 * h;               // column within the step's block
+      c.wrow = 0;
     } else {
-      n = c.tid & 63;
-      kc = c.n0 + 64 * (c.tid >> 6);
+      n = b & 63;                // W row within the step
+      kc = c.n0 + 64 * (b >> 6) + 32 * h;
+      c.wrow = b & 63;
     }
     c.w_row_ok = kBwd ? kc < g.cols : n < g.rows;   // backward rows are checked per step
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) c.a_frag[sl] = swz_a(128 * c.wm + c.l32, 2 * sl + c.lhi);
     if (!kBwd) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) c.b_frag[sl] = swz_a(128 * c.wn + c.l32, 2 * sl + c.lhi);
+      for (int sl = 0; sl < 4; ++sl) c.b_frag[sl] = swz_a(col0 + c.l32, 2 * sl + c.lhi);
 #pragma unroll
-      for (int w = 0; w < 8; ++w) c.w_store[w] = swz_a(c.tid, w);
+      for (int w = 0; w < 4; ++w) c.w_store[w] = swz_a(b, 4 * h + w);
     } else {
-      // tr16 source lane: row 8 lhi + 4 rr + (lane % 16) / 4, columns col0 .. col0 + 3
+      // tr16 source lane: row 8 lhi + 4 rr + (lane % 16) / 4, columns cc .. cc + 3
       const int r0 = 8 * c.lhi + ((c.lane & 15) >> 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col0 = 128 * c.wn + 32 * j + 16 * ((c.lane >> 4) & 1) + 4 * (c.lane & 3);
-        c.b_frag[2 * j] = swz_bt(r0, col0 >> 3) + (col0 & 7);
-        c.b_frag[2 * j + 1] = swz_bt(r0 + 4, col0 >> 3) + (col0 & 7);
+      for (int j = 0; j < 2; ++j) {
+        const int cc = col0 + 32 * j + 16 * ((c.lane >> 4) & 1) + 4 * (c.lane & 3);
+        c.b_frag[2 * j] = swz_bt(r0, cc >> 3) + (cc & 7);
+        c.b_frag[2 * j + 1] = swz_bt(r0 + 4, cc >> 3) + (cc & 7);
       }
 #pragma unroll
-      for (int w = 0; w < 8; ++w) c.w_store[w] = swz_bt(c.tid & 63, 8 * (c.tid >> 6) + w);
+      for (int w = 0; w < 4; ++w) c.w_store[w] = swz_bt(b & 63, 8 * (b >> 6) + 4 * h + w);
     }
     c.code_voff = c.w_row_ok ? (uint32_t)((n * g.cols + kc) >> 1) : kOOB;
     c.blk0 = n * (g.cols >> 6) + (kc >> 6);
@@ -388,36 +433,35 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   c.codes_bytes = (uint32_t)((g.rows * g.cols) >> 1);
   c.code8_bytes = (uint32_t)(g.rows * c.kblocks);
   c.s2_bytes = (uint32_t)(((g.rows * c.kblocks + 255) >> 8) * 4);
-  const int lane = c.lane, l32 = c.l32, lhi = c.lhi, wm = c.wm, wn = c.wn;
+  const int l32 = c.l32, lhi = c.lhi, wm = c.wm;
   const int64_t m0 = c.m0, n0 = c.n0;
 
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   for (int p0 = 0; p0 < g.r; p0 += 16) {
     const int p = p0 + 8 * lhi;
-    u32x4_t af[4], bf[4];
+    u32x4_t af[4], bf[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = m0 + 128 * wm + 32 * i + l32;
       af[i] = row < g.T ? ld_global16(g.lora_l + row * g.r + p) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + 128 * wn + 32 * j + l32;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + col0 + 32 * j + l32;
       bf[j] = col < out_len ? ld_global16(g.lora_r + col * g.r + p) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
   }
-  (void)lane;
 
   // ---- prologue ------------------------------------------------------------
   CodeRegs cur, nxt;
@@ -433,7 +477,7 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
   cur = nxt;
   barrier_keep_vmem<kVmemPerStep>();   // activation stage 0 complete
 
-  u32x4_t fa[2][4], fb[2][4];
+  u32x4_t fa[2][4], fb[2][2];
   load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
 
   for (int step = 0; step < c.nsteps; step += 6) {
@@ -454,8 +498,8 @@ __global__ __launch_bounds__(256, 1) void qlora_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + 128 * wn + 32 * j + l32;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + col0 + 32 * j + l32;
       if (col < out_len) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -473,14 +517,14 @@ static unsigned num_tiles(int64_t T, int64_t out_len) {
 }
 
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(qlora_gemm_kernel<false>, dim3(num_tiles(a.T, a.rows)), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL(qlora_gemm_kernel<false>, dim3(num_tiles(a.T, a.rows)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(qlora_gemm_kernel<true>, dim3(num_tiles(a.T, a.cols)), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL(qlora_gemm_kernel<true>, dim3(num_tiles(a.T, a.cols)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
