@@ -14,37 +14,51 @@ namespace qlora {
 
 // ---------------------------------------------------------------------------
 // Quantise: one workgroup per group of 256 blocks (16384 weights, 64 KB of
-// float32).  A wave owns 64 consecutive blocks; per iteration 8 lanes share
-// a block, each lane reading 8 consecutive weights (2 x 16 B) and writing the
-// 8 packed codes as one 32-bit word.  The block absmax is an 8-lane xor
-// butterfly.  The quotient RN32(w / c) is computed as Markstein's corrected
-// product with the correctly rounded reciprocal of c's significand (one IEEE
-// division per block); with y = RN(1/c) and q0 = RN(w y) within an ulp, the
-// residual w - q0 c is exact and q0 + residual * y rounds to RN(w / c).
-// Scaling both w and c by 2^-e (e = exponent of c) keeps y normal for any
-// finite c, denormals included.
+// float32).  A wave owns 64 consecutive blocks; per iteration 8 lanes share a
+// block: lane s reads the 16-byte chunks s and s + 8 of the block's 256
+// bytes, so each of the two load instructions covers whole 128-byte lines.
+// The block absmax is an 8-lane xor butterfly.  The quotient RN32(w / c) is
+// computed as Markstein's corrected product with the correctly rounded
+// reciprocal of c's significand (one IEEE division per block); with
+// y = RN(1/c) and q0 = RN(w y) within an ulp, the residual w - q0 c is exact
+// and q0 + residual * y rounds to RN(w / c).  Scaling both w and c by 2^-e
+// (e = exponent of c) keeps y normal for any finite c, denormals included.
+// Lane s holds elements 4s .. 4s+3 and 32 + 4s .. 32 + 4s + 3; a neighbour
+// exchange (DPP) assembles the 8-element code words: even lanes store words
+// 0..3, odd lanes words 4..7.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t nf4_code(float r, const float* thr) {
-  uint32_t i = (r > thr[7]) ? 8u : 0u;
-  i += (r > thr[i + 3]) ? 4u : 0u;
-  i += (r > thr[i + 1]) ? 2u : 0u;
-  i += (r > thr[i]) ? 1u : 0u;
-  return i;
+
+// Nearest-level index by a 4-step binary search over the 15 decision
+// thresholds; the thresholds of each step are picked with selects from
+// constants (scalar registers), so no step waits on a memory read.
+__device__ __forceinline__ uint32_t nf4_code(float r) {
+  const bool b8 = r > kNF4Thr[7];
+  const bool b4 = r > (b8 ? kNF4Thr[11] : kNF4Thr[3]);
+  const float t2lo = b4 ? kNF4Thr[5] : kNF4Thr[1];
+  const float t2hi = b4 ? kNF4Thr[13] : kNF4Thr[9];
+  const bool b2 = r > (b8 ? t2hi : t2lo);
+  // threshold index 8 b8 + 4 b4 + 2 b2 (even indices 0 .. 14)
+  const float t00 = b2 ? kNF4Thr[2] : kNF4Thr[0];
+  const float t04 = b2 ? kNF4Thr[6] : kNF4Thr[4];
+  const float t08 = b2 ? kNF4Thr[10] : kNF4Thr[8];
+  const float t12 = b2 ? kNF4Thr[14] : kNF4Thr[12];
+  const float tl = b4 ? t04 : t00;
+  const float th = b4 ? t12 : t08;
+  const bool b1 = r > (b8 ? th : tl);
+  return (b8 ? 8u : 0u) | (b4 ? 4u : 0u) | (b2 ? 2u : 0u) | (b1 ? 1u : 0u);
 }
 
 __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
     const float* __restrict__ W, int64_t n_b, uint32_t* __restrict__ codes,
     float* __restrict__ cblk, double* __restrict__ gpart) {
-  __shared__ float thr[16];
   __shared__ double wsum[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  if (tid < 15) thr[tid] = kNF4Thr[tid];
-  __syncthreads();
 
   const int64_t blk0 = (int64_t)blockIdx.x * kGroup + wave * 64;
   const int sub = lane & 7;
+  const bool odd = sub & 1;
   float c_keep = 0.0f;
 #pragma unroll 2
   for (int it = 0; it < 8; ++it) {
@@ -52,9 +66,9 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
     const bool valid = b < n_b;
     float v[8];
     if (valid) {
-      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(W + b * kBlock + sub * 8);
-      const f32x4_t x0 = __builtin_nontemporal_load(p);
-      const f32x4_t x1 = __builtin_nontemporal_load(p + 1);
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(W + b * kBlock) + sub;
+      const f32x4_t x0 = __builtin_nontemporal_load(p);       // elements 4s .. 4s+3
+      const f32x4_t x1 = __builtin_nontemporal_load(p + 8);   // elements 32 + 4s ..
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] = x0[e];
@@ -71,24 +85,31 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
     m = fmaxf(m, __shfl_xor(m, 2));
     m = fmaxf(m, __shfl_xor(m, 4));
 
-    uint32_t word;
+    uint32_t h0, h1;                         // codes of v[0..3], v[4..7]
     if (m == 0.0f) {
-      word = 0x77777777u;                    // all-zero block: the zero level
+      h0 = h1 = 0x7777u;                     // all-zero block: the zero level
     } else {
       int ex;
       const float cm = frexpf(m, &ex);       // m = cm * 2^ex, cm in [0.5, 1)
       const float y = __fdiv_rn(1.0f, cm);
-      word = 0u;
+      uint32_t hh[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float wm = ldexpf(v[e], -ex);
         const float q0 = wm * y;
         const float rem = fmaf(-q0, cm, wm);
         const float r = fmaf(rem, y, q0);
-        word |= nf4_code(r, thr) << (4 * e);
+        hh[e >> 2] |= nf4_code(r) << (4 * (e & 3));
       }
+      h0 = hh[0];
+      h1 = hh[1];
     }
-    if (valid) codes[b * 8 + sub] = word;
+    // even lane 2p: word p = h0 | (h0 of lane 2p+1) << 16
+    // odd lane 2p+1: word 4 + p = (h1 of lane 2p) | h1 << 16
+    const uint32_t send = odd ? h0 : h1;
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    const uint32_t word = odd ? (got | (h1 << 16)) : (h0 | (got << 16));
+    if (valid) codes[b * 8 + (odd ? 4 : 0) + (sub >> 1)] = word;
     if (sub == it) c_keep = m;   // lane l keeps block (l & 7) * 8 + (l >> 3)
   }
   // lane j <- block j of this wave
@@ -108,56 +129,87 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
 // Mean of the block constants: perfect binary float64 tree over the group
 // partials (which are its level-8 nodes), zero-padded to a power of two.
 // One workgroup of 1024 threads; thread t first folds an aligned run of
-// `per` leaves with a binary-counter cascade (same tree), then the 1024 run
-// sums are folded pairwise in shared memory.
+// `per` leaves (same tree), then the 1024 run sums are folded pairwise.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void dq_mean_kernel(const double* __restrict__ gpart,
                                                        int64_t n_g, int64_t n_b, int64_t per,
                                                        float* __restrict__ mu_out) {
-  __shared__ double sh[1024];
+  __shared__ double sh[16];
   const int t = threadIdx.x;
+  // The run's leaves are read 16 at a time and folded as a perfect tree
+  // (zero padding beyond `per` only adds +0 to a subtree that is already
+  // complete, `per` being a power of two); runs longer than 16 combine the
+  // 16-leaf sums with a binary-counter cascade, which continues the same tree.
   double stack[40];
   int sp = 0;
-  for (int64_t i = 0; i < per; ++i) {
-    const int64_t idx = (int64_t)t * per + i;
-    double v = idx < n_g ? gpart[idx] : 0.0;
-    for (int64_t k = i; k & 1; k >>= 1) v = stack[--sp] + v;
-    stack[sp++] = v;
+  for (int64_t i0 = 0; i0 < per; i0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t idx = (int64_t)t * per + i0 + j;
+      v[j] = (i0 + j < per && idx < n_g) ? gpart[idx] : 0.0;
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2 * w) v[j] = v[j] + v[j + w];
+    double acc = v[0];
+    for (int64_t k = i0 >> 4; k & 1; k >>= 1) acc = stack[--sp] + acc;
+    stack[sp++] = acc;
   }
-  sh[t] = stack[0];
+  // the 1024 run sums: a tree over each wave's 64 (shuffles), then over the
+  // 16 wave sums -- the same perfect tree
+  double v = stack[0];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v += __shfl_down(v, d);
+  if ((t & 63) == 0) sh[t >> 6] = v;
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    if ((t & (2 * d - 1)) == 0) sh[t] = sh[t] + sh[t + d];
-    __syncthreads();
+  if (t < 64) {
+    double u = t < 16 ? sh[t] : 0.0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) u += __shfl_down(u, d);
+    if (t == 0) mu_out[0] = (float)(u / (double)n_b);
   }
-  if (t == 0) mu_out[0] = (float)(sh[0] / (double)n_b);
 }
 
 // ---------------------------------------------------------------------------
-// Double-quantisation codes: one workgroup (256 threads) per group.
-// d = RN32(c - mu); s2 = max |d|; code8 = E4M3_RNE(RN32(d / s2) * 256).
+// Double-quantisation codes: one workgroup (256 threads) per 4 groups; thread
+// t handles block t of each.  d = RN32(c - mu); s2 = max |d| over the group;
+// code8 = E4M3_RNE(RN32(d / s2) * 256).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ cblk,
                                                         const float* __restrict__ mu_p,
                                                         int64_t n_b, uint8_t* __restrict__ code8,
                                                         float* __restrict__ s2_out) {
-  __shared__ float wmax[4];
+  __shared__ float wmax[4][4];
   const int t = threadIdx.x;
-  const int64_t b = (int64_t)blockIdx.x * kGroup + t;
-  const bool valid = b < n_b;
+  const int64_t g0 = (int64_t)blockIdx.x * 4;
   const float mu = mu_p[0];
-  const float d = valid ? __fsub_rn(cblk[b], mu) : 0.0f;
-  float a = fabsf(d);
+  float d[4];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-  if ((t & 63) == 0) wmax[t >> 6] = a;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t b = (g0 + k) * kGroup + t;
+    d[k] = b < n_b ? __fsub_rn(cblk[b], mu) : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float a = fabsf(d[k]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if ((t & 63) == 0) wmax[k][t >> 6] = a;
+  }
   __syncthreads();
-  const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  if (t == 0) s2_out[blockIdx.x] = s2;
-  if (valid) {
-    uint32_t code = 0u;
-    if (s2 > 0.0f) code = e4m3_encode_rne(__fdiv_rn(d, s2) * 256.0f);
-    code8[b] = (uint8_t)code;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t g = g0 + k;
+    const int64_t b = g * kGroup + t;
+    const float s2 = fmaxf(fmaxf(wmax[k][0], wmax[k][1]), fmaxf(wmax[k][2], wmax[k][3]));
+    if (t == 0 && g * kGroup < n_b) s2_out[g] = s2;
+    if (b < n_b) {
+      uint32_t code = 0u;
+      if (s2 > 0.0f) code = e4m3_encode_rne(__fdiv_rn(d[k], s2) * 256.0f);
+      code8[b] = (uint8_t)code;
+    }
   }
 }
 
@@ -218,8 +270,8 @@ hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t*
   while (pow2 < n_g) pow2 <<= 1;
   const int64_t per = pow2 > 1024 ? pow2 / 1024 : 1;
   hipLaunchKernelGGL(dq_mean_kernel, dim3(1), dim3(1024), 0, stream, gpart, n_g, n_b, per, mu);
-  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)n_g), dim3(256), 0, stream, cblk, mu, n_b,
-                     code8, s2);
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((n_g + 3) / 4)), dim3(256), 0, stream, cblk,
+                     mu, n_b, code8, s2);
   return hipGetLastError();
 }
 

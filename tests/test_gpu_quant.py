@@ -124,3 +124,24 @@ def test_bulk_8192x22016_full_constants_sampled_rows():
     ref_bits = O.dequantize_sampled_bits(ref)
     got_bits = bits_host(out[torch.from_numpy(sel).to(out.device)])
     assert np.array_equal(got_bits, ref_bits)
+
+
+def test_double_quant_constants_past_16384_groups():
+    """A weight with more than 16384 groups of block constants (16448 x 16384:
+    16448 groups), so the mean's tree folds runs of 32 group sums per thread:
+    the mean, every second-level scale and every 8-bit constant code must
+    equal the oracle's."""
+    quantize, _ = _lib()
+    rows, cols = 16448, 16384
+    w = WL.weight(rows, cols, seed=6)
+    print(f"[quant] long mean tree shape={w.shape}", flush=True)
+    wq = quantize(f32_dev(w))
+    torch.cuda.synchronize()
+    got = state_host(wq)
+    del wq
+    c = O.block_absmax(w)
+    del w
+    code8, s2, mu = O.double_quantize(c)
+    assert np.float32(got["absmax_offset"][0]) == mu
+    assert np.array_equal(got["absmax_scale"].view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(got["absmax_code"], code8)
