@@ -368,6 +368,44 @@ def dequantize_sampled_bits(state: dict) -> np.ndarray:
     return _decode_bits(codes, cprime.reshape(-1)).reshape(sel.size, cols)
 
 
+def quantize_sampled_cols(w: np.ndarray, sel) -> dict:
+    """quantize() of the whole weight, keeping the NF4 codes of the 64-wide
+    blocks that contain columns `sel` (every row).  The constants and their
+    double quantisation cover every block, exactly as quantize()'s.
+    """
+    w = np.asarray(w, dtype=F32)
+    rows, cols = w.shape
+    assert cols % BLOCK == 0, "cols must be a multiple of 64"
+    sel = np.asarray(sel, dtype=np.int64).reshape(-1)
+    kb = cols // BLOCK
+    c = block_absmax(w)
+    code8, s2, mu = double_quantize(c)
+    bsel = np.unique(sel // BLOCK)
+    wb = w.reshape(rows, kb, BLOCK)[:, bsel, :]
+    cb = c.reshape(rows, kb)[:, bsel]
+    codes = nf4_encode(wb.reshape(-1, BLOCK), cb.reshape(-1))
+    return {
+        "rows": rows, "cols": cols, "sel": sel, "block_cols": bsel,
+        "codes": pack_nibbles(codes),
+        "absmax_code": code8,
+        "absmax_scale": s2,
+        "absmax_offset": np.array([mu], dtype=F32),
+    }
+
+
+def dequantize_sampled_cols_bits(state: dict) -> np.ndarray:
+    """dequantize_bits() restricted to the columns of a quantize_sampled_cols()
+    state: uint16 [rows, len(sel)]."""
+    rows, cols, sel, bsel = state["rows"], state["cols"], state["sel"], state["block_cols"]
+    kb = cols // BLOCK
+    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
+                                     state["absmax_offset"][0]).reshape(rows, kb)[:, bsel]
+    codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
+    bits = _decode_bits(codes, cprime.reshape(-1)).reshape(rows, bsel.size * BLOCK)
+    pos = np.searchsorted(bsel, sel // BLOCK) * BLOCK + sel % BLOCK
+    return bits[:, pos]
+
+
 def dequantize(state: dict) -> np.ndarray:
     """Dequantised weight as float64 values of the bf16 results."""
     return bf16_bits_to_f32(dequantize_bits(state)).astype(F64)
@@ -416,16 +454,34 @@ def linear_backward(x: np.ndarray, dy: np.ndarray, w_hat: np.ndarray, a: np.ndar
       dA = s G^T X
       dB = s dY^T (X A^T)
     """
+    dx = linear_input_grad(dy, w_hat, a, b, alpha, r)
+    da, db = lora_grads(x, dy, a, b, alpha, r)
+    return dx, da, db
+
+
+def linear_input_grad(dy: np.ndarray, w_hat: np.ndarray, a: np.ndarray, b: np.ndarray,
+                      alpha: float, r: int) -> np.ndarray:
+    """dX = dY W_hat + s (dY B) A (the dX part of linear_backward).  Columns of
+    W_hat and A may be any subset of the input features: dX is then the same
+    subset of its columns."""
+    dy = np.asarray(dy, dtype=F64)
+    s = F64(alpha) / F64(r)
+    g = dy @ np.asarray(b, dtype=F64)
+    return dy @ np.asarray(w_hat, dtype=F64) + s * (g @ np.asarray(a, dtype=F64))
+
+
+def lora_grads(x: np.ndarray, dy: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float,
+               r: int):
+    """dA = s (dY B)^T X and dB = s dY^T (X A^T) (the adapter part of
+    linear_backward; W does not enter)."""
     x = np.asarray(x, dtype=F64)
     dy = np.asarray(dy, dtype=F64)
     a = np.asarray(a, dtype=F64)
-    b = np.asarray(b, dtype=F64)
     s = F64(alpha) / F64(r)
-    g = dy @ b
-    dx = dy @ np.asarray(w_hat, dtype=F64) + s * (g @ a)
+    g = dy @ np.asarray(b, dtype=F64)
     da = s * (g.T @ x)
     db = s * (dy.T @ (x @ a.T))
-    return dx, da, db
+    return da, db
 
 
 def lora_param_count(d: int, k: int, r: int) -> int:

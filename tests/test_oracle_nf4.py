@@ -225,3 +225,13 @@ def test_sampled_rows_equal_full_quantize_rows():
         assert np.array_equal(np.asarray(part[k]).view(np.uint8), np.asarray(full[k]).view(np.uint8))
     assert np.array_equal(part["codes"], full["codes"].reshape(96, 352)[sel])
     assert np.array_equal(O.dequantize_sampled_bits(part), O.dequantize_bits(full)[sel])
+
+
+def test_sampled_cols_equal_full_dequantize_cols():
+    """The sampled-column helpers agree with the full dequantisation on every
+    selected column (columns in shared and separate blocks, first and last)."""
+    w = WL.weight(96, 704, seed=14, outliers=True)
+    sel = np.array([0, 3, 63, 64, 130, 131, 500, 703])
+    full = O.dequantize_bits(O.quantize(w))
+    part = O.quantize_sampled_cols(w, sel)
+    assert np.array_equal(O.dequantize_sampled_cols_bits(part), full[:, sel])
