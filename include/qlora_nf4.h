@@ -136,8 +136,12 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
  *   X      [T, cols] bf16        A [r, cols] bf16        B [rows, r] bf16
  *   Y      [T, rows] bf16 (written)
  *   U_save [T, r] bf16 (written; X A^T for the backward) or NULL
- * T >= 1, r % 16 == 0, 16 <= r <= 128.  Accumulation is float32 on bf16 MFMA;
- * the packed weight is only read.
+ * T >= 1, r % 16 == 0, 16 <= r <= 128; T * rows and T * cols below 2^30,
+ * rows * cols below 2^32, rows and cols at most 2^22 (QLORA_ERR_SHAPE
+ * otherwise).  Accumulation is float32 on bf16 MFMA; the packed weight is
+ * only read.  For T <= 64 (generation-sized batches, ta-paperlens 落とし穴)
+ * the call takes the skinny path, which streams the packed weight once and
+ * forms X A^T in the same pass; the workspace size reflects the path.
  */
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
                               const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
@@ -165,7 +169,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
  * call that launches kernel group `which` records `start_event` on the
  * caller's stream right before that group and `stop_event` right after it
  * (hipEvent_t handles passed as void*, created by the caller; NULL, NULL
- * turns it off).  Groups: QLORA_TIMING_FWD_GEMM (the fused forward GEMM),
+ * turns it off).  Groups: QLORA_TIMING_FWD_GEMM (the fused forward GEMM,
+ * or for T <= 64 the two kernels of the skinny forward),
  * QLORA_TIMING_DX_GEMM (the fused backward-dX GEMM), QLORA_TIMING_QUANTIZE
  * (the three quantisation kernels), QLORA_TIMING_DEQUANT.  Returns
  * QLORA_ERR_SHAPE for an unknown group.
