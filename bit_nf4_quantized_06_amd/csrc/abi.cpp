@@ -158,9 +158,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
   }
   uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * X A^T)
   float* P = ws_ptr<float>(ws, L.proj_off);
-  hipError_t e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
-  if (e == hipSuccess)
-    e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, U_save, Us, scale, nullptr, 0, st);
+  hipError_t e = launch_lora_proj_partial(X, A, false, T, d.cols, r, L.s_proj_x, P, st);
+  if (e == hipSuccess) {
+    TransposeJobs none;
+    none.n = 0;
+    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale, nullptr, 0},
+                                none, st);
+  }
   if (e == hipSuccess) {
     GemmArgs g;
     g.act = X;
@@ -199,30 +203,33 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = alpha / (float)r;
 
-  uint16_t* Bt = ws_ptr<uint16_t>(ws, L.bt_off);    // [r, rows]
   uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
   uint16_t* Gs = ws_ptr<uint16_t>(ws, L.g_off);     // [T, r] bf16(s * dY B)
-  uint16_t* Gt = ws_ptr<uint16_t>(ws, L.gt_off);    // [r, t_pad]
-  uint16_t* Ut = ws_ptr<uint16_t>(ws, L.ut_off);    // [r, t_pad]
+  uint16_t* Gn = ws_ptr<uint16_t>(ws, L.gn_off);    // [T, r] bf16(dY B)
+  uint16_t* Un = ws_ptr<uint16_t>(ws, L.un_off);    // [T, r] bf16(X A^T) if not given
   float* P = ws_ptr<float>(ws, L.proj_off);
-  float* PG = ws_ptr<float>(ws, L.grad_off);
 
-  // B^T, A^T and (if the forward's U is given) U^T in one launch
-  TransposeJobs tj;
-  tj.n = 0;
-  tj.job[tj.n++] = TransposeJob{B, d.rows, r, Bt, d.rows};
-  tj.job[tj.n++] = TransposeJob{A, r, d.cols, At, r};
-  if (U_saved) tj.job[tj.n++] = TransposeJob{U_saved, T, r, Ut, L.t_pad};
-  hipError_t e = launch_transposes(tj, st);
-  // G = dY B: (s G) for the dX seed, G^T for dA
-  if (e == hipSuccess) e = launch_lora_proj_partial(dY, Bt, T, d.rows, r, L.s_proj_dy, P, st);
-  if (e == hipSuccess)
-    e = launch_lora_proj_reduce(P, T, r, L.s_proj_dy, nullptr, Gs, scale, Gt, L.t_pad, st);
-  // U^T for dB when the forward's U was not kept: recompute X A^T
+  // G = dY B (B read in place as [rows, r]); its reduction writes (s G) for
+  // the dX seed and G for dA, and the same launch transposes A for the dX seed
+  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, st);
+  if (e == hipSuccess) {
+    TransposeJobs tj;
+    tj.n = 1;
+    tj.job[0] = TransposeJob{A, r, d.cols, At, r};
+    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale, nullptr, 0}, tj,
+                                st);
+  }
+  // U for dB when the forward's U was not kept: recompute X A^T
+  const uint16_t* U = U_saved;
   if (e == hipSuccess && !U_saved) {
-    e = launch_lora_proj_partial(X, A, T, d.cols, r, L.s_proj_x, P, st);
-    if (e == hipSuccess)
-      e = launch_lora_proj_reduce(P, T, r, L.s_proj_x, nullptr, nullptr, 0.0f, Ut, L.t_pad, st);
+    e = launch_lora_proj_partial(X, A, false, T, d.cols, r, L.s_proj_x, P, st);
+    if (e == hipSuccess) {
+      TransposeJobs none;
+      none.n = 0;
+      e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, nullptr, 0},
+                                  none, st);
+    }
+    U = Un;
   }
   // dX = dY dequant(W) + (s G) A
   if (e == hipSuccess) {
@@ -241,13 +248,13 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
     g.T = T;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
-  // dA = s G^T X and dB = s (U^T dY)^T: partials of both in one launch, then
-  // one fixed-order reduction
+  // dA = s G^T X and dB = s dY^T U: partials of both in one launch, then one
+  // fixed-order reduction
   if (e == hipSuccess) {
     GradJobs gj;
     gj.n = 2;
-    gj.job[0] = GradJob{Gt, L.t_pad, X, d.cols, PG, dA, 0};
-    gj.job[1] = GradJob{Ut, L.t_pad, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
+    gj.job[0] = GradJob{Gn, X, d.cols, ws_ptr<float>(ws, L.grad_off), dA, 0};
+    gj.job[1] = GradJob{U, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
     e = launch_lora_grad_partial(gj, T, r, L.s_grad, st);
     if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
   }

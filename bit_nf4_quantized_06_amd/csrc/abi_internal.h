@@ -37,9 +37,8 @@ struct LinearWs {
   int s_proj_x;     // split count of X A^T over cols
   int s_proj_dy;    // split count of dY B over rows
   int s_grad;       // split count of G^T X and U^T dY over tokens
-  int64_t t_pad;    // token stride of the transposed G / U (multiple of 32)
   int s_gemv;       // split count of the skinny forward (0: fused GEMM path)
-  size_t proj_off, u_off, gemv_off, gemv_u_off, bt_off, at_off, g_off, gt_off, ut_off, grad_off, grad_b_off, total;
+  size_t proj_off, u_off, gemv_off, gemv_u_off, at_off, g_off, gn_off, un_off, grad_off, grad_b_off, total;
 };
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd);
 

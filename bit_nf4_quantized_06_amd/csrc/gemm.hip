@@ -64,10 +64,7 @@ constexpr int kThreads = 512;                  // 8 waves
 constexpr int kActLoads = 4;                   // activation DMAs per wave and step
 constexpr int kVmemPerStep = kActLoads + 3;    // + codes, 8-bit code, group scale
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ int swz_a(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);

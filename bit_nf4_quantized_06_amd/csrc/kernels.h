@@ -58,20 +58,15 @@ struct GemvArgs {
 hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream);
 
 // --- LoRA side products (lora.hip) ----------------------------------------
-// Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k],
-// L [T, red] bf16, R [r, red] bf16, P float32 [S][T][r].
-int lora_proj_splits(int64_t T, int64_t red);
-hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_t T,
-                                    int64_t red, int32_t r, int splits, float* P,
+// Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R(p, k),
+// L [T, red] bf16, P float32 [S][T][r]; R is [r, red] (R(p, k) = R[p][k]) or,
+// with r_by_rows, [red, r] (R(p, k) = R[k][p]), read in place.
+int lora_proj_splits(int64_t T, int64_t red, int32_t r);
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
                                     hipStream_t stream);
-// v = sum_s P (fixed order).  Each output may be NULL: out_rm[t][p] = bf16(v),
-// out_sc[t][p] = bf16(scale * v), out_tr[p][t] = bf16(v) with row stride ld_tr
-// and zeros for T <= t < ld_tr.
-hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
-                                   uint16_t* out_rm, uint16_t* out_sc, float scale,
-                                   uint16_t* out_tr, int64_t ld_tr, hipStream_t stream);
-// Up to three bf16 transposes in one launch: out[c][r'] = in[r'][c] for an
-// [R, C] input; out has row stride ld_out and is zero for R <= r' < ld_out.
+// bf16 transposes: out[c][r'] = in[r'][c] for an [R, C] input; out has row
+// stride ld_out and is zero for R <= r' < ld_out.
 struct TransposeJob {
   const uint16_t* in;
   int64_t R, C;
@@ -83,15 +78,29 @@ struct TransposeJobs {
   int tiles[3];   // filled by the launcher
   int n;
 };
-hipError_t launch_transposes(TransposeJobs jobs, hipStream_t stream);
+// v = sum_s P[s] (fixed order s = 0, 1, ...).  Each output may be NULL:
+// out_rm[t][p] = bf16(v), out_sc[t][p] = bf16(scale * v), out_tr[p][t] =
+// bf16(v) with row stride ld_tr and zeros for T <= t < ld_tr.  The same
+// launch runs the transposes of `tj` (tj.n may be 0).
+struct ProjReduce {
+  const float* P;
+  int64_t T;
+  int32_t r;
+  int32_t splits;
+  uint16_t* out_rm;
+  uint16_t* out_sc;
+  float scale;
+  uint16_t* out_tr;
+  int64_t ld_tr;
+};
+hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream);
 
 // Adapter-gradient partials and their reduction, up to two problems per
-// launch: P[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q] with St [r, ld_st]
-// bf16 (zero for t >= T), L [T, Q] bf16; then out = scale * sum_s P[s],
-// as [r, Q] (transposed == 0) or [Q, r] (transposed != 0).
+// launch: P[s] = sum_{t in chunk s} S[t][p] L[t][q] with S [T, r] and L [T, Q]
+// bf16 (token-major), stored [r, Q] (transposed == 0) or [Q, r]
+// (transposed != 0); then out = scale * sum_s P[s] in the same layout.
 struct GradJob {
-  const uint16_t* St;
-  int64_t ld_st;
+  const uint16_t* S;
   const uint16_t* L;
   int64_t Q;
   float* P;

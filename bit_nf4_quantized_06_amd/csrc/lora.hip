@@ -28,50 +28,195 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 // ---------------------------------------------------------------------------
-// P[s][t][p] = sum_{k in chunk s} L[t][k] R[p][k]   (L [T, red], R [r, red])
-// Workgroup = 4 waves over 128 rows of L; a wave owns 32 rows (two MFMA
-// 16x16x32 row groups) and all r = 16 NJ columns, and walks its reduction
-// chunk 128 at a time with all 8 L loads and 4 NJ R loads issued first.
+// P[s][t][p] = sum_{k in chunk s} L[t][k] R(p, k), L [T, red] bf16 and R the
+// rank-r operand, stored either [r, red] (R(p, k) = R[p][k], the forward's
+// A) or [red, r] (kRT: R(p, k) = R[k][p], the backward's B, read in place).
+//
+// Workgroup = 4 waves over 128 tokens; wave w owns tokens 32 w .. 32 w + 31
+// (two MFMA 16x16x32 row groups) and all r columns, and walks the split's
+// reduction chunk 128 at a time.  The 128-wide slice of R is shared by the
+// four waves: it goes straight into LDS by buffer loads (no registers), one
+// of three stages; the L operand goes to registers, three buffers.  Both
+// run two iterations ahead, so every wave keeps 16 L loads of 1 KB in
+// flight.  The stage and buffer indices are compile-time constants (the
+// loop is unrolled by 3), so the DMA into one stage never makes the compiler
+// wait before reading another.
+//
+// R stage layouts (bf16 elements):
+//   [r, red] source: r rows x 16 chunks of 8, chunk' = chunk ^ (row & 15),
+//       so the 16 rows one fragment read touches land in 16 distinct chunks;
+//   [red, r] source: 128 rows x r, exactly as in memory (the rows of one
+//       slice are contiguous); fragments come from ds_read_b64_tr_b16, which
+//       hands each lane 4 consecutive rows of one column.
 // ---------------------------------------------------------------------------
-template <int NJ>
+template <int NJ, bool kRT>
+struct ProjCtx {
+  __amdgpu_buffer_rsrc_t lr, rr;
+  uint32_t x_off[2];        // per row group: lane's L byte offset at k = 0
+  bool x_ok[2];             // token row inside L
+  int64_t kb, ke;           // this split's reduction range
+  int64_t red;
+  uint32_t r_off[NJ];       // kRT == false: lane's R offset at k = 0 per DMA
+  int r_row[NJ];            // kRT == false: R row of that DMA lane
+  int r_chunk[NJ];          // kRT == false: logical chunk of that DMA lane
+  uint32_t rt_byte[NJ];     // kRT: byte of the slice this DMA lane fetches
+  int wave, lane;
+};
+
+template <int NJ, bool kRT>
+__device__ __forceinline__ void proj_load_x(const ProjCtx<NJ, kRT>& c, int it, u32x4_t (&x)[4][2]) {
+  const int64_t k0 = c.kb + (int64_t)it * 128 + 8 * (c.lane >> 4);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t k = k0 + 32 * u;
+    const bool kin = k < c.ke;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      x[u][g] = bload16(c.lr, kin && c.x_ok[g] ? c.x_off[g] + (uint32_t)(k * 2) : kOOB);
+  }
+}
+
+template <int NJ, bool kRT>
+__device__ __forceinline__ void proj_load_r(const ProjCtx<NJ, kRT>& c, int it, uint16_t* stage) {
+  const int64_t k0 = c.kb + (int64_t)it * 128;
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int q = c.wave * NJ + i;   // 1 KB piece of the 4 NJ KB stage
+    uint32_t off;
+    if (!kRT) {
+      const int64_t k = k0 + 8 * c.r_chunk[i];
+      off = k < c.ke ? c.r_off[i] + (uint32_t)(k * 2) : kOOB;
+    } else {
+      const int64_t row = k0 + (int64_t)(c.rt_byte[i] / (32 * NJ));
+      off = row < c.ke ? (uint32_t)(k0 * 32 * NJ) + c.rt_byte[i] : kOOB;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rr, (lds_void_t*)(stage + q * 512), 16, off, 0, 0,
+                                             0);
+  }
+}
+
+// B-operand fragment (16 columns p, 32 reduction indices) j of slice u
+template <int NJ, bool kRT>
+__device__ __forceinline__ u32x4_t proj_frag(const ProjCtx<NJ, kRT>& c, const uint16_t* stage,
+                                             int u, int j) {
+  if (!kRT) {
+    const int p = 16 * j + (c.lane & 15);
+    const int ch = (4 * u + (c.lane >> 4)) ^ (p & 15);
+    return *reinterpret_cast<const u32x4_t*>(stage + p * 128 + 8 * ch);
+  } else {
+    const int row = 32 * u + 8 * (c.lane >> 4) + ((c.lane & 15) >> 2);
+    const int col = 16 * j + 4 * (c.lane & 3);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(stage + row * (16 * NJ) + col));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(stage + (row + 4) * (16 * NJ) + col));
+    const uint2 l = __builtin_bit_cast(uint2, lo);
+    const uint2 h = __builtin_bit_cast(uint2, hi);
+    return u32x4_t{l.x, l.y, h.x, h.y};
+  }
+}
+
+// One 128-wide iteration on R stage SI and L buffer SI.  kMore: also issue
+// L(it + 2) and R(it + 2).  Vector-memory issue order is pinned by
+// scheduling barriers, so the wait before the workgroup barrier can count
+// the loads issued after this wave's share of R(it): in the unrolled loop
+// L(it + 1), R(it + 1) and L(it + 2); in the two iterations after it, which
+// issue nothing, L(it + 1) and R(it + 1) for the first and none for the
+// second (kTail = 1, 2).
+template <int NJ, bool kRT, int SI, bool kMore, int kTail>
+__device__ __forceinline__ void proj_iter(const ProjCtx<NJ, kRT>& c, int it, uint16_t* const (&st)[3],
+                                          u32x4_t (&xb)[3][4][2], f32x4_t (&acc)[2][NJ]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (kMore) proj_load_x(c, it + 2, xb[(SI + 2) % 3]);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int N = kMore ? 16 + NJ : (kTail == 1 ? 8 + NJ : 0);
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
+  if (kMore) proj_load_r(c, it + 2, st[(SI + 2) % 3]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4_t rf[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) rf[j] = proj_frag(c, st[SI], u, j);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[g][j] = mfma16(xb[SI][u][g], rf[j], acc[g][j]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+template <int NJ, bool kRT>
 __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ R, int64_t T, int64_t red,
     int64_t chunk, float* __restrict__ P) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 128 + wave * 32;
-  const int64_t kb = (int64_t)blockIdx.y * chunk;
-  const int64_t ke = kb + chunk < red ? kb + chunk : red;
-  const __amdgpu_buffer_rsrc_t lr = rsrc(L, (uint64_t)T * red * 2);
-  const __amdgpu_buffer_rsrc_t rr = rsrc(R, (uint64_t)(16 * NJ) * red * 2);
-  const int kl = 8 * (lane >> 4);
+  constexpr int kStage = 16 * NJ * 128;   // bf16 elements
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[kStage];
+  uint16_t* const st[3] = {s0, s1, s2};
+  ProjCtx<NJ, kRT> c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.red = red;
+  const int64_t m0 = (int64_t)blockIdx.x * 128 + 32 * c.wave;
+  c.kb = (int64_t)blockIdx.y * chunk;
+  c.ke = c.kb + chunk < red ? c.kb + chunk : red;
+  const int nit = c.ke > c.kb ? (int)((c.ke - c.kb + 127) / 128) : 0;
+  c.lr = rsrc(L, (uint64_t)T * red * 2);
+  c.rr = rsrc(R, (uint64_t)(16 * NJ) * red * 2);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t t = m0 + 16 * g + (c.lane & 15);
+    c.x_ok[g] = t < T;
+    c.x_off[g] = c.x_ok[g] ? (uint32_t)(t * red * 2) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int q = c.wave * NJ + i;
+    if (!kRT) {
+      // piece q = rows 4 q .. 4 q + 3 of the stage, lane -> (row, physical chunk)
+      const int row = 4 * q + (c.lane >> 4);
+      const int ch = (c.lane & 15) ^ (row & 15);
+      c.r_row[i] = row;
+      c.r_chunk[i] = ch;
+      c.r_off[i] = (uint32_t)((int64_t)row * red * 2);
+    } else {
+      c.rt_byte[i] = (uint32_t)(1024 * q + 16 * c.lane);
+    }
+  }
   f32x4_t acc[2][NJ];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[g][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = kb; k < ke; k += 128) {
-    u32x4_t a[4][2], b[4][NJ];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t kk = k + 32 * u + kl;
-      const bool ok = kk < ke;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int64_t row = m0 + 16 * g + (lane & 15);
-        a[u][g] = bload16(lr, ok && row < T ? (uint32_t)((row * red + kk) * 2) : kOOB);
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        b[u][j] = bload16(rr, ok ? (uint32_t)(((int64_t)(16 * j + (lane & 15)) * red + kk) * 2)
-                                 : kOOB);
+
+  if (nit > 0) {
+    u32x4_t xb[3][4][2];
+    // prologue in the steady-state issue order: X(0), R(0), X(1), R(1)
+    proj_load_x(c, 0, xb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    proj_load_r(c, 0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    proj_load_x(c, 1, xb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    proj_load_r(c, 1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the unrolled body is one basic block (no early exits for the
+    // compiler to sink the prefetches into); the last nit % 3 iterations
+    // follow the loop
+    const int nit3 = nit - nit % 3;
+    for (int it = 0; it < nit3; it += 3) {
+      proj_iter<NJ, kRT, 0, true, 0>(c, it, st, xb, acc);
+      proj_iter<NJ, kRT, 1, true, 0>(c, it + 1, st, xb, acc);
+      proj_iter<NJ, kRT, 2, true, 0>(c, it + 2, st, xb, acc);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[g][j] = mfma16(a[u][g], b[u][j], acc[g][j]);
+    if (nit3 < nit) proj_iter<NJ, kRT, 0, false, 1>(c, nit3, st, xb, acc);
+    if (nit3 + 1 < nit) proj_iter<NJ, kRT, 1, false, 2>(c, nit3 + 1, st, xb, acc);
+    // the loads issued past the end read nothing; let them land before exit
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0xF << 8));
   }
   float* out = P + (int64_t)blockIdx.y * T * (16 * NJ);
 #pragma unroll
@@ -80,8 +225,8 @@ __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t t = m0 + 16 * g + 4 * (lane >> 4) + e;
-        if (t < T) out[t * (16 * NJ) + 16 * j + (lane & 15)] = acc[g][j][e];
+        const int64_t t = m0 + 16 * g + 4 * (c.lane >> 4) + e;
+        if (t < T) out[t * (16 * NJ) + 16 * j + (c.lane & 15)] = acc[g][j][e];
       }
 }
 
@@ -90,16 +235,20 @@ static int64_t proj_chunk(int64_t red, int splits) {
   return (c + 127) / 128 * 128;
 }
 
-hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_t T,
-                                    int64_t red, int32_t r, int splits, float* P,
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
                                     hipStream_t stream) {
   const int64_t chunk = proj_chunk(red, splits);
   const dim3 grid((unsigned)((T + 127) / 128), (unsigned)splits);
-  switch (r >> 4) {
+  switch ((r >> 4) * 2 + (r_by_rows ? 1 : 0)) {
 #define QLORA_PROJ_CASE(NJ)                                                                   \
-  case NJ:                                                                                    \
-    hipLaunchKernelGGL(lora_proj_partial_kernel<NJ>, grid, dim3(256), 0, stream, L, R, T, red, \
-                       chunk, P);                                                             \
+  case 2 * NJ:                                                                                \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, false>), grid, dim3(256), 0, stream, L,  \
+                       R, T, red, chunk, P);                                                  \
+    break;                                                                                    \
+  case 2 * NJ + 1:                                                                            \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, true>), grid, dim3(256), 0, stream, L,   \
+                       R, T, red, chunk, P);                                                  \
     break;
     QLORA_PROJ_CASE(1) QLORA_PROJ_CASE(2) QLORA_PROJ_CASE(3) QLORA_PROJ_CASE(4)
     QLORA_PROJ_CASE(5) QLORA_PROJ_CASE(6) QLORA_PROJ_CASE(7) QLORA_PROJ_CASE(8)
@@ -109,69 +258,18 @@ hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, int64_
   return hipGetLastError();
 }
 
-// Fixed-order sum of the split partials.  Writes any of: out_rm[t][p] =
-// bf16(v), out_sc[t][p] = bf16(scale * v) (the pre-scaled operand the fused
-// GEMM seeds its accumulators with), out_tr[p][t] = bf16(v) with row stride
-// ld_tr and zeros for T <= t < ld_tr.
-// 64 outputs (t, p) per workgroup; wave q adds splits q, q + 4, q + 8, ...
-// (loads issued 8 at a time), then the four wave sums are added in order q =
-// 0..3: a fixed order for any launch.
-__global__ __launch_bounds__(256) void lora_proj_reduce_kernel(
-    const float* __restrict__ P, int64_t T, int r, int splits, uint16_t* __restrict__ out_rm,
-    uint16_t* __restrict__ out_sc, float scale, uint16_t* __restrict__ out_tr, int64_t ld_tr,
-    int64_t rows_total) {
-  __shared__ float part[4][64];
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
-  const bool live = i < rows_total * r;
-  const int64_t t = live ? i / r : 0;
-  const int p = live ? (int)(i - t * r) : 0;
-  float v = 0.0f;
-  if (live && t < T) {
-    const float* src = P + t * r + p;
-    const int64_t stride = T * r;
-    int s = q;
-    for (; s + 28 < splits; s += 32) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + 4 * j) * stride];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v += x[j];
-    }
-    for (; s < splits; s += 4) v += src[(int64_t)s * stride];
-  }
-  part[q][lane] = v;
-  __syncthreads();
-  if (q != 0 || !live) return;
-  v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-  const uint16_t b = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-  if (t < T) {
-    if (out_rm) out_rm[t * r + p] = b;
-    if (out_sc) out_sc[t * r + p] = (uint16_t)(pack_bf16x2(v * scale, 0.0f) & 0xFFFFu);
-  }
-  if (out_tr) out_tr[(int64_t)p * ld_tr + t] = b;
-}
-
-hipError_t launch_lora_proj_reduce(const float* P, int64_t T, int32_t r, int splits,
-                                   uint16_t* out_rm, uint16_t* out_sc, float scale,
-                                   uint16_t* out_tr, int64_t ld_tr, hipStream_t stream) {
-  const int64_t rows_total = out_tr ? ld_tr : T;
-  const int64_t n = rows_total * r;
-  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0,
-                     stream, P, T, r, splits, out_rm, out_sc, scale, out_tr, ld_tr, rows_total);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-// Up to three bf16 transposes in one launch: out[c][r'] = in[r'][c] for an
-// [R, C] input; out has row stride ld_out and is zero for R <= r' < ld_out.
-// 32 x 32 tiles through shared memory; workgroups are assigned to jobs by
-// the tile counts of the jobs before them.
+// Fixed-order sum of the split partials, v = P[0] + P[1] + ... + P[S-1], for
+// four consecutive outputs (t, p .. p + 3) per thread (16-byte loads, 8
+// splits in flight).  Writes any of: out_rm[t][p] = bf16(v), out_sc[t][p] =
+// bf16(scale * v) (the pre-scaled operand the fused GEMM seeds its
+// accumulators with), out_tr[p][t] = bf16(v) with row stride ld_tr and zeros
+// for T <= t < ld_tr.  Workgroups past the reduction run the bf16 transposes
+// of `tj` (32 x 32 tiles through LDS), so small layout changes the next
+// kernels need ride along in the same launch.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs jobs) {
+__device__ void transpose_tile(const TransposeJobs& jobs, int b) {
   __shared__ uint16_t tile[32][33];
-  int b = blockIdx.x;
   int jdx = 0;
   while (jdx < jobs.n - 1 && b >= jobs.tiles[jdx]) {
     b -= jobs.tiles[jdx];
@@ -198,118 +296,256 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJobs jobs)
   }
 }
 
-hipError_t launch_transposes(TransposeJobs jobs, hipStream_t stream) {
-  int total = 0;
-  for (int i = 0; i < jobs.n; ++i) {
-    const TransposeJob& j = jobs.job[i];
-    jobs.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
-    total += jobs.tiles[i];
+__global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, TransposeJobs tj,
+                                                               unsigned reduce_blocks) {
+  if (blockIdx.x >= reduce_blocks) {
+    transpose_tile(tj, (int)(blockIdx.x - reduce_blocks));
+    return;
   }
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)total), dim3(256), 0, stream, jobs);
+  const int64_t rows_total = a.out_tr ? a.ld_tr : a.T;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= rows_total * a.r) return;
+  const int64_t t = i / a.r;
+  const int p = (int)(i - t * a.r);
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (t < a.T) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.P + i);
+    const int64_t stride = a.T * a.r / 4;
+    int s = 0;
+    for (; s + 8 <= a.splits; s += 8) {
+      f32x4_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += x[j];
+    }
+    for (; s < a.splits; ++s) v += src[(int64_t)s * stride];
+  }
+  uint16_t b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b[e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu);
+  if (t < a.T) {
+    if (a.out_rm)
+      *reinterpret_cast<uint2*>(a.out_rm + i) =
+          uint2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+    if (a.out_sc)
+      *reinterpret_cast<uint2*>(a.out_sc + i) =
+          uint2{pack_bf16x2(v[0] * a.scale, v[1] * a.scale), pack_bf16x2(v[2] * a.scale, v[3] * a.scale)};
+  }
+  if (a.out_tr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a.out_tr[(int64_t)(p + e) * a.ld_tr + t] = b[e];
+  }
+}
+
+hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream) {
+  const int64_t rows_total = a.out_tr ? a.ld_tr : a.T;
+  const unsigned nred = (unsigned)((rows_total * a.r / 4 + 255) / 256);
+  int ttiles = 0;
+  for (int i = 0; i < tj.n; ++i) {
+    const TransposeJob& j = tj.job[i];
+    tj.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
+    ttiles += tj.tiles[i];
+  }
+  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3(nred + (unsigned)ttiles), dim3(256), 0, stream,
+                     a, tj, nred);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// C[s][p][q] = sum_{t in chunk s} St[p][t] L[t][q], for up to two problems at
-// once (blockIdx.z): the dA partials (St = G^T, L = X) and the dB^T partials
-// (St = U^T, L = dY).  Workgroup = 4 waves over the same 128 columns q; the
-// waves take interleaved 64-token slices of the chunk and their partials are
-// added in a fixed order through shared memory.  The B operand needs 8
-// consecutive tokens of one column per lane while L is token-major: each lane
-// loads an 8 x 8 tile (8 rows, 16 B each; 16 lanes cover 256 contiguous bytes
-// of a row) and transposes it in registers, which yields operands for 8
-// columns q = q0 + 8 (lane % 16) + v, v = 0..7 (one MFMA per v).
+// C[s][p][q] = sum_{t in chunk s} S[t][p] L[t][q] for up to two problems per
+// launch (blockIdx.z): the dA partials (S = G, L = X) and the dB partials
+// (S = U, L = dY).  S [T, r] and L [T, Q] are bf16 in their natural
+// token-major layout.  The reduction runs over tokens, so both MFMA operands
+// need 8 consecutive tokens of one column per lane: every 64-token slice of
+// L (128 columns) and of S goes straight into LDS by buffer loads, whole
+// 256-byte row pieces at a time, and ds_read_b64_tr_b16 hands each lane 4
+// consecutive rows of one column -- no register transposes.
+//
+// Workgroup = 4 waves over 128 columns q; wave w owns q0 + 32 w .. + 31 and
+// all r rows p, so the four waves share each staged slice and need no
+// reduction among themselves.  Three stages, loads two slices ahead.
+// L stage: 64 rows x 16 chunks of 8, chunk' = chunk ^ f(row) with f(row) =
+// 4 (row & 3) + 2 ((row >> 3) & 1), so the 4 rows x 2 chunks one 16-lane
+// group of a transposed read touches, and the same for the next group, sit
+// in 16 distinct chunks.  S stage: 64 rows x r, as in memory.
+// Partials are written [p][q], or [q][p] for a transposed job (dB, kept as
+// [Q, r]), so the reduction reads and writes contiguously in both cases.
 // ---------------------------------------------------------------------------
+template <int NP>
+struct GradCtx {
+  __amdgpu_buffer_rsrc_t lr, sr;
+  uint32_t l_voff[4];   // L DMA i of this wave: byte offset at t = 0 (column part)
+  int l_row[4];         // its row within the slice
+  bool l_cok[4];        // its 8 columns lie inside Q (Q % 16 == 0: all or none)
+  int64_t Q, tb, te;
+  int wave, lane;
+};
+
+constexpr int kGradSD(int NP) { return (2 * NP + 3) / 4; }   // S DMAs per wave
+
+template <int NP>
+__device__ __forceinline__ void grad_load(const GradCtx<NP>& c, int it, uint16_t* lst,
+                                          uint16_t* sst, uint16_t* dummy) {
+  const int64_t t0 = c.tb + (int64_t)it * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + c.l_row[i];
+    const uint32_t off = (t < c.te && c.l_cok[i]) ? (uint32_t)(t * c.Q * 2) + c.l_voff[i] : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.lr, (lds_void_t*)(lst + (4 * c.wave + i) * 512), 16,
+                                             off, 0, 0, 0);
+  }
+  // the S slice is 64 rows x r = 2 NP pieces of 1 KB; pieces past it land
+  // in a dummy area (their source is out of range: zeros)
+#pragma unroll
+  for (int i = 0; i < kGradSD(NP); ++i) {
+    const int q = c.wave * kGradSD(NP) + i;
+    const uint32_t byte = (uint32_t)(1024 * q + 16 * c.lane);
+    const int64_t t = t0 + byte / (32 * NP);
+    const bool real = q < 2 * NP;
+    const uint32_t off = (real && t < c.te) ? (uint32_t)(t0 * 32 * NP) + byte : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.sr, (lds_void_t*)(real ? sst + q * 512 : dummy), 16,
+                                             off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p1));
+  const uint2 l = __builtin_bit_cast(uint2, lo);
+  const uint2 h = __builtin_bit_cast(uint2, hi);
+  return u32x4_t{l.x, l.y, h.x, h.y};
+}
+
+template <int NP, int SI>
+__device__ __forceinline__ void grad_iter(const GradCtx<NP>& c, int it, uint16_t* const (&ls)[3],
+                                          uint16_t* const (&ss)[3], uint16_t* dummy,
+                                          f32x4_t (&acc)[NP][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // slice it landed: the newer loads are slice it+1's (4 + kGradSD per wave)
+  constexpr int N = 4 + kGradSD(NP);
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
+  grad_load(c, it + 2, ls[(SI + 2) % 3], ss[(SI + 2) % 3], dummy);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* L = ls[SI];
+  const uint16_t* S = ss[SI];
+  const int a = (c.lane & 15) >> 2;      // row within the 4-row group
+  const int b = c.lane & 3;              // 4-column piece
+  const int g = c.lane >> 4;             // 16-lane group: rows + 8 g
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int row = 32 * ks + 8 * g + a;
+    u32x4_t lf[2], sf[NP];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      const int col = 32 * c.wave + 16 * cg + 4 * b;          // within the 128
+      const int ch = col >> 3;
+      const int f = 4 * (row & 3) + 2 * ((row >> 3) & 1);     // same for row + 4
+      const int e0 = row * 128 + ((ch ^ f) << 3) + (col & 7);
+      const int e1 = (row + 4) * 128 + ((ch ^ f) << 3) + (col & 7);
+      lf[cg] = ld_tr_pair(L + e0, L + e1);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int col = 16 * j + 4 * b;
+      sf[j] = ld_tr_pair(S + row * (16 * NP) + col, S + (row + 4) * (16 * NP) + col);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) acc[j][cg] = mfma16(sf[j], lf[cg], acc[j][cg]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 template <int NP>
 __global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, int64_t T,
                                                                int64_t chunk) {
-  __shared__ f32x4_t red_buf[NP * 8 * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t l0[64 * 128];
+  __shared__ __attribute__((aligned(1024))) uint16_t l1[64 * 128];
+  __shared__ __attribute__((aligned(1024))) uint16_t l2[64 * 128];
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[64 * 16 * NP];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[64 * 16 * NP];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[64 * 16 * NP];
+  __shared__ __attribute__((aligned(1024))) uint16_t dummy[512];
+  uint16_t* const ls[3] = {l0, l1, l2};
+  uint16_t* const ss[3] = {s0, s1, s2};
   const GradJob& jb = jobs.job[blockIdx.z];
-  const int64_t Q = jb.Q;
+  GradCtx<NP> c;
+  c.Q = jb.Q;
   const int64_t q0 = (int64_t)blockIdx.x * 128;
-  if (q0 >= Q) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t tb = (int64_t)blockIdx.y * chunk;
-  const int64_t te = tb + chunk < T ? tb + chunk : T;
-  const int64_t qc = q0 + 8 * (lane & 15);
-  const __amdgpu_buffer_rsrc_t lr = rsrc(jb.L, (uint64_t)T * Q * 2);
-  const __amdgpu_buffer_rsrc_t sr = rsrc(jb.St, (uint64_t)(16 * NP) * jb.ld_st * 2);
-  f32x4_t acc[NP][8];
+  if (q0 >= c.Q) return;   // whole workgroup: before any barrier
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.tb = (int64_t)blockIdx.y * chunk;
+  c.te = c.tb + chunk < T ? c.tb + chunk : T;
+  const int nit = c.te > c.tb ? (int)((c.te - c.tb + 63) / 64) : 0;
+  c.lr = rsrc(jb.L, (uint64_t)T * c.Q * 2);
+  c.sr = rsrc(jb.S, (uint64_t)T * (16 * NP) * 2);
+  {
+    // L DMA i of wave w fills rows 4 (4 w + i) .. + 3: lane -> row + lane / 16,
+    // physical chunk lane % 16, which holds logical chunk (lane % 16) ^ f(row)
+    const int ph = c.lane & 15;
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[p][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t t0 = tb + 64 * wave; t0 < te; t0 += 256) {
-    u32x4_t in[2][8];
-    u32x4_t sa[2][NP];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t tl = t0 + 32 * h + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        in[h][i] = bload16(lr, (tl + i < te && qc < Q) ? (uint32_t)(((tl + i) * Q + qc) * 2) : kOOB);
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        sa[h][p] = bload16(sr, (uint32_t)(((int64_t)(16 * p + (lane & 15)) * jb.ld_st + tl) * 2));
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4_t bop[8];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          bop[2 * c][d] = perm(in[h][2 * d + 1][c], in[h][2 * d][c], 0x05040100u);
-          bop[2 * c + 1][d] = perm(in[h][2 * d + 1][c], in[h][2 * d][c], 0x07060302u);
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) acc[p][v] = mfma16(sa[h][p], bop[v], acc[p][v]);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (4 * c.wave + i) + (c.lane >> 4);
+      const int f = 4 * (row & 3) + 2 * ((row >> 3) & 1);
+      const int lc = ph ^ f;
+      c.l_row[i] = row;
+      c.l_voff[i] = (uint32_t)((q0 + 8 * lc) * 2);
+      c.l_cok[i] = q0 + 8 * lc < c.Q;
     }
   }
-  // fixed-order sum of the 4 waves: ((w0 + w1) + w2) + w3
-  for (int w = 1; w < 4; ++w) {
-    if (wave == w) {
+  f32x4_t acc[NP][2];
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
+  for (int j = 0; j < NP; ++j)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) red_buf[(p * 8 + v) * 64 + lane] = acc[p][v];
+    for (int cg = 0; cg < 2; ++cg) acc[j][cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (nit > 0) {
+    grad_load(c, 0, l0, s0, dummy);
+    __builtin_amdgcn_sched_barrier(0);
+    grad_load(c, 1, l1, s1, dummy);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nit3 = nit - nit % 3;
+    for (int it = 0; it < nit3; it += 3) {
+      grad_iter<NP, 0>(c, it, ls, ss, dummy, acc);
+      grad_iter<NP, 1>(c, it + 1, ls, ss, dummy, acc);
+      grad_iter<NP, 2>(c, it + 2, ls, ss, dummy, acc);
     }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) acc[p][v] += red_buf[(p * 8 + v) * 64 + lane];
-    }
-    __syncthreads();
+    if (nit3 < nit) grad_iter<NP, 0>(c, nit3, ls, ss, dummy, acc);
+    if (nit3 + 1 < nit) grad_iter<NP, 1>(c, nit3 + 1, ls, ss, dummy, acc);
+    // the loads issued past the end read nothing; let them land before exit
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0xF << 8));
   }
-  if (wave == 0 && qc < Q) {
-    float* out = jb.P + (int64_t)blockIdx.y * (16 * NP) * Q;
+  // acc[j][cg][e] = C[p = 16 j + 4 (lane / 16) + e][q = q0 + 32 w + 16 cg + lane % 16]
+  float* out = jb.P + (int64_t)blockIdx.y * (16 * NP) * c.Q;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
+  for (int cg = 0; cg < 2; ++cg) {
+    const int64_t q = q0 + 32 * c.wave + 16 * cg + (c.lane & 15);
+    if (q >= c.Q) continue;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pr = 16 * p + 4 * (lane >> 4) + e;
-        f32x4_t lo = f32x4_t{acc[p][0][e], acc[p][1][e], acc[p][2][e], acc[p][3][e]};
-        f32x4_t hi = f32x4_t{acc[p][4][e], acc[p][5][e], acc[p][6][e], acc[p][7][e]};
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(out + (int64_t)pr * Q + qc);
-        dst[0] = lo;
-        dst[1] = hi;
+    for (int j = 0; j < NP; ++j) {
+      const int p = 16 * j + 4 * (c.lane >> 4);
+      if (jb.transposed) {
+        *reinterpret_cast<f32x4_t*>(out + q * (16 * NP) + p) = acc[j][cg];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[(int64_t)(p + e) * c.Q + q] = acc[j][cg][e];
       }
     }
   }
 }
 
+static int64_t grad_chunk(int64_t T, int splits) {
+  int64_t c = (T + splits - 1) / splits;
+  return (c + 63) / 64 * 64;
+}
+
 hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
                                     hipStream_t stream) {
-  int64_t chunk = (T + splits - 1) / splits;
-  chunk = (chunk + 255) / 256 * 256;
+  const int64_t chunk = grad_chunk(T, splits);
   int64_t qmax = 0;
   for (int i = 0; i < jobs.n; ++i) qmax = jobs.job[i].Q > qmax ? jobs.job[i].Q : qmax;
   const dim3 grid((unsigned)((qmax + 127) / 128), (unsigned)splits, (unsigned)jobs.n);
@@ -327,11 +563,13 @@ hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int spl
   return hipGetLastError();
 }
 
-// out = scale * sum_s P[s] for each job: transposed == 0 -> out[p][q] ([r, Q]),
-// transposed != 0 -> out[q][p] ([Q, r]).  All jobs in one launch.
+// out[i] = scale * (P[0][i] + P[1][i] + ...) (fixed order) for each job; the
+// partials already have the output's layout ([r, Q], or [Q, r] for a
+// transposed job).  Four outputs per thread, 8 splits in flight; all jobs in
+// one launch.
 __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradJobs jobs, int r, int splits,
                                                                float scale) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   int jdx = 0;
   while (jdx < jobs.n && i >= (int64_t)r * jobs.job[jdx].Q) {
     i -= (int64_t)r * jobs.job[jdx].Q;
@@ -339,24 +577,26 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradJobs jobs, in
   }
   if (jdx >= jobs.n) return;
   const GradJob& jb = jobs.job[jdx];
-  const int64_t Q = jb.Q;
-  float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += jb.P[(int64_t)s * r * Q + i];
-  v *= scale;
-  if (!jb.transposed) {
-    jb.out[i] = v;
-  } else {
-    const int64_t p = i / Q;
-    const int64_t q = i - p * Q;
-    jb.out[q * r + p] = v;
+  const int64_t stride = (int64_t)r * jb.Q / 4;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(jb.P + i);
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    f32x4_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += x[j];
   }
+  for (; s < splits; ++s) v += src[(int64_t)s * stride];
+  *reinterpret_cast<f32x4_t*>(jb.out + i) = v * scale;
 }
 
 hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
                                    hipStream_t stream) {
   int64_t n = 0;
   for (int i = 0; i < jobs.n; ++i) n += (int64_t)r * jobs.job[i].Q;
-  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
                      stream, jobs, r, splits, scale);
   return hipGetLastError();
 }

@@ -7,18 +7,23 @@
 
 namespace qlora {
 
-// Split counts of the LoRA side reductions: about 256 workgroups of 4 waves
-// (one per CU) while keeping the float32 partial buffers small.
-int lora_proj_splits(int64_t T, int64_t red) {
-  const int64_t rb = (T + 127) / 128;
-  int64_t s = (256 + rb - 1) / rb;
-  const int64_t max_s = (red + 127) / 128;
+// Split count of the rank-r projections: about 512 workgroups of 4 waves
+// (two per CU), each split at least two 128-wide iterations long, and the
+// float32 partials (S T r) at most a quarter of the bytes of L (T red bf16).
+int lora_proj_splits(int64_t T, int64_t red, int32_t r) {
+  const int64_t tiles = (T + 127) / 128;
+  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t max_s = (red + 255) / 256;
+  const int64_t by_bytes = red / (8 * (int64_t)(r > 0 ? r : 1));
+  if (max_s > by_bytes) max_s = by_bytes;
   if (s > max_s) s = max_s;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;
 }
 
+// Split count of the adapter gradients: about 256 workgroups of 4 waves
+// (one per CU) while keeping the float32 partial buffers small.
 int lora_grad_splits(int64_t T, int64_t Q) {
   const int64_t qb = (Q + 127) / 128;
   int64_t s = (256 + qb - 1) / qb;
@@ -97,10 +102,9 @@ QuantWs quant_ws_layout(const WeightDims& d) {
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
   LinearWs L;
   memset(&L, 0, sizeof(L));
-  L.s_proj_x = lora_proj_splits(T, d.cols);
-  L.s_proj_dy = lora_proj_splits(T, d.rows);
+  L.s_proj_x = lora_proj_splits(T, d.cols, r);
+  L.s_proj_dy = lora_proj_splits(T, d.rows, r);
   L.s_grad = lora_grad_splits(T, d.cols > d.rows ? d.cols : d.rows);
-  L.t_pad = (T + 31) / 32 * 32;
   L.s_gemv = (!bwd && T <= kGemvMaxTokens) ? gemv_splits(d.rows, d.cols) : 0;
   size_t off = 0;
   const int s_proj = bwd ? (L.s_proj_x > L.s_proj_dy ? L.s_proj_x : L.s_proj_dy) : L.s_proj_x;
@@ -113,16 +117,14 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
   L.gemv_u_off = off;
   off += align_up(sizeof(float) * (size_t)L.s_gemv * (size_t)T * (size_t)r, kWsAlign);
   if (bwd) {
-    L.bt_off = off;
-    off += align_up(2 * (size_t)r * (size_t)d.rows, kWsAlign);
     L.at_off = off;
     off += align_up(2 * (size_t)d.cols * (size_t)r, kWsAlign);
     L.g_off = off;
     off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
-    L.gt_off = off;
-    off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
-    L.ut_off = off;
-    off += align_up(2 * (size_t)r * (size_t)L.t_pad, kWsAlign);
+    L.gn_off = off;
+    off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
+    L.un_off = off;
+    off += align_up(2 * (size_t)T * (size_t)r, kWsAlign);
     L.grad_off = off;
     off += align_up(sizeof(float) * (size_t)L.s_grad * (size_t)r * (size_t)d.cols, kWsAlign);
     L.grad_b_off = off;
