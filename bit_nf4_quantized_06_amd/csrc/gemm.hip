@@ -283,7 +283,9 @@ __device__ __forceinline__ void slice_schedule() {
 
 // One reduction step on activation stage SA and weight stage SB.  On entry
 // fa[0], fb[0] hold slice 0 of this step and `cur` the codes of step+1; on
-// exit fa[0], fb[0] hold slice 0 of step+1 and `cur` the codes of step+2.
+// exit fa[0], fb[0] hold slice 0 of step+1 and `nxt` the codes of step+2
+// (the caller swaps the two register sets for the next step: no copy, so
+// nothing waits for the codes before they are used a step later).
 template <bool kBwd, int SA, int SB>
 __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][2],
                                           u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][2],
@@ -337,7 +339,6 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
   for (int i = 0; i < 4; ++i) fa[0][i] = ga[i];
 #pragma unroll
   for (int j = 0; j < 2; ++j) fb[0][j] = gb[j];
-  cur = nxt;
 #endif
 }
 
@@ -367,6 +368,11 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   const int nt = (int)((out_len + BN - 1) / BN);
   int tm, tn;
   tile_coords(blockIdx.x, mt, nt, tm, tn);
+  // the divisions in tile_coords run on the vector unit; without this the
+  // tile origin, and with it the activation descriptor, would sit in VGPRs
+  // and every DMA would be wrapped in a waterfall loop
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   c.m0 = (int64_t)tm * BM;
   c.n0 = (int64_t)tn * BN;
   c.nsteps = (int)((c.red_len + BK - 1) / BK);
@@ -461,35 +467,38 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   }
 
   // ---- prologue ------------------------------------------------------------
-  CodeRegs cur, nxt;
+  CodeRegs ca, cb;   // codes of even / odd steps
   issue_act(c, sa0, 0);
-  issue_codes(c, 0, cur);
+  issue_codes(c, 0, ca);
   issue_act(c, sa1, 1);
-  issue_codes(c, 1, nxt);
+  issue_codes(c, 1, cb);
   {
-    const Nf4Lut lut = lut_of(c, cur);
+    const Nf4Lut lut = lut_of(c, ca);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, cur, w);
+    for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, ca, w);
   }
-  cur = nxt;
   barrier_keep_vmem<kVmemPerStep>();   // activation stage 0 complete
 
   u32x4_t fa[2][4], fb[2][2];
   load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
 
-  for (int step = 0; step < c.nsteps; step += 6) {
-    gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cur, nxt);
-    if (step + 1 >= c.nsteps) break;
-    gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, cur, nxt);
-    if (step + 2 >= c.nsteps) break;
-    gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cur, nxt);
-    if (step + 3 >= c.nsteps) break;
-    gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, cur, nxt);
-    if (step + 4 >= c.nsteps) break;
-    gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cur, nxt);
-    if (step + 5 >= c.nsteps) break;
-    gemm_step<kBwd, 2, 1>(c, step + 5, acc, fa, fb, cur, nxt);
+  // whole groups of 6 steps (the stage cycle) in a loop without exits, so
+  // each step's tail and the next step's head share one basic block; then
+  // the last nsteps % 6 steps
+  int step = 0;
+  for (; step + 6 <= c.nsteps; step += 6) {
+    gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+    gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+    gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, 2, 1>(c, step + 5, acc, fa, fb, ca, cb);
   }
+  if (step < c.nsteps) gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cb, ca);
+  if (step + 1 < c.nsteps) gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+  if (step + 2 < c.nsteps) gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+  if (step + 3 < c.nsteps) gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+  if (step + 4 < c.nsteps) gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
 
   // ---- epilogue: round to bf16 and store ------------------------------------
 #pragma unroll
