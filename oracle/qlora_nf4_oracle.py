@@ -425,6 +425,37 @@ def storage_bits_per_param(rows: int, cols: int) -> float:
 
 
 # --------------------------------------------------------------------------
+# Merge of the adapter into the dequantised base (deployment step)
+# --------------------------------------------------------------------------
+def merge_values_f32(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float,
+                     r: int) -> np.ndarray:
+    """float32 sum RN32(w_hat + RN32(s * RN32(B A))) before the final rounding.
+
+    [WZ] 26.2 (inference: merge once, W_merged = W + (alpha/r) B A); [PL]
+    落とし穴 and [UL] Kompromisse: the merge happens on the base dequantised
+    to 16 bit.  Reading: the 16-bit base is the bf16 dequantised weight
+    (w_hat_bits, uint16 [rows, cols]); B A is formed exactly (float64 of the
+    bf16 values of B [rows, r] and A [r, cols]) and rounded once to float32;
+    s = RN32(alpha / r) multiplies in float32; the sum with the base is one
+    float32 addition.
+    """
+    base = bf16_bits_to_f32(w_hat_bits)
+    s = np.float32(np.float32(alpha) / np.float32(r))
+    ba = (np.asarray(b, dtype=F64) @ np.asarray(a, dtype=F64)).astype(np.float32)
+    return (base + (s * ba).astype(np.float32)).astype(np.float32)
+
+
+def merge_bits(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float,
+               r: int) -> np.ndarray:
+    """bf16 bit patterns of the merged weight: bf16_RNE of merge_values_f32.
+
+    [PL] 落とし穴: merge on the 16-bit base and, if wanted, quantise the
+    result again (that is quantize() of these values as float32).
+    """
+    return bf16_bits_rne(merge_values_f32(w_hat_bits, a, b, alpha, r))
+
+
+# --------------------------------------------------------------------------
 # (a6-a11) LoRA linear layer, forward and backward, float64
 # --------------------------------------------------------------------------
 def linear_forward(x: np.ndarray, w_hat: np.ndarray, a: np.ndarray, b: np.ndarray,
