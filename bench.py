@@ -31,6 +31,7 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 
 HEADLINE = "attn_4096"
 BULK = "bulk_8192x22016"
+MERGE = "merge_8192x22016"
 
 
 def parse_args():
@@ -231,6 +232,7 @@ def time_steps(ls, ev, steps, warmup, backward=True, kernel_timing=True):
 
 
 def time_bulk(ev, dev, reps):
+    import numpy as np
     import torch
 
     import bit_nf4_quantized_06_amd as q
@@ -240,33 +242,46 @@ def time_bulk(ev, dev, reps):
     stream = torch.cuda.current_stream().cuda_stream
     wl = WL.WORKLOADS[BULK]
     lin = wl.linears[0]
-    w = torch.from_numpy(WL.linear_inputs(wl, 0)["w"]).to(dev)
+    mwl = WL.WORKLOADS[MERGE]          # the same weight with a rank-64 adapter
+    minp = WL.linear_inputs(mwl, 0)
+    w = torch.from_numpy(minp["w"]).to(dev)
+    A = torch.from_numpy(minp["a"].view(np.int16)).to(dev).view(torch.bfloat16)
+    B = torch.from_numpy(minp["b"].view(np.int16)).to(dev).view(torch.bfloat16)
     n = lin.out_features * lin.in_features
     out = q.NF4Weight.empty(lin.out_features, lin.in_features, dev)
     ws = torch.empty(lib.qlora_nf4_quantize_workspace(lin.out_features, lin.in_features),
                      dtype=torch.uint8, device=dev)
     wbf = torch.empty(lin.out_features, lin.in_features, dtype=torch.bfloat16, device=dev)
+    wmg = torch.empty_like(wbf)
     for _ in range(2):
         q.qlora_nf4_quantize(w, out=out, workspace=ws)
         q.qlora_nf4_dequantize(out, out=wbf)
+        q.qlora_nf4_merge(out, A, B, mwl.alpha, out=wmg)
     torch.cuda.synchronize()
-    qp, dp = [], []
+    qp, dp, mp = [], [], []
     for _ in range(reps):
         a = (ev.new(), ev.new())
         b = (ev.new(), ev.new())
+        c = (ev.new(), ev.new())
         lib.qlora_set_timing_events(2, a[0], a[1])
         lib.qlora_set_timing_events(3, b[0], b[1])
+        lib.qlora_set_timing_events(4, c[0], c[1])
         q.qlora_nf4_quantize(w, out=out, workspace=ws)
         q.qlora_nf4_dequantize(out, out=wbf)
+        q.qlora_nf4_merge(out, A, B, mwl.alpha, out=wmg)
         qp.append(a)
         dp.append(b)
+        mp.append(c)
     torch.cuda.synchronize()
-    lib.qlora_set_timing_events(2, None, None)
-    lib.qlora_set_timing_events(3, None, None)
+    for g in (2, 3, 4):
+        lib.qlora_set_timing_events(g, None, None)
     q_ms = sum(ev.ms(a, b) for a, b in qp) / reps
     d_ms = sum(ev.ms(a, b) for a, b in dp) / reps
+    m_ms = sum(ev.ms(a, b) for a, b in mp) / reps
     qbytes = 4 * n + packed_bytes(n)
     dbytes = packed_bytes(n) + 2 * n
+    r = mwl.rank
+    mbytes = packed_bytes(n) + 2 * r * (lin.out_features + lin.in_features) + 2 * n
     return {
         "workload": "bulk_8192x22016: quantize (NF4/64 + DQ/256) and dequantize-to-bf16 of an "
                     "8192x22016 float32 weight with 0.1% outliers x20",
@@ -276,6 +291,11 @@ def time_bulk(ev, dev, reps):
         "dequant_ms": round(d_ms, 4), "dequant_bytes": dbytes,
         "dequant_GBps": round(dbytes / d_ms / 1e6, 1),
         "dequant_hbm_frac": round(dbytes / d_ms / 1e6 / PEAK_HBM_GBPS, 4),
+        "merge_workload": "merge_8192x22016: bf16(dequant(W) + (16/64) B A) of the same weight "
+                          "with a rank-64 adapter",
+        "merge_ms": round(m_ms, 4), "merge_bytes": mbytes,
+        "merge_GBps": round(mbytes / m_ms / 1e6, 1),
+        "merge_hbm_frac": round(mbytes / m_ms / 1e6 / PEAK_HBM_GBPS, 4),
     }
 
 

@@ -111,6 +111,24 @@ def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=N
     return out
 
 
+def qlora_nf4_merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [rows, cols] weight with the adapter folded in (qlora_nf4_merge):
+    bf16(dequant(W) + (alpha/r) B A)."""
+    lib = _lib.load()
+    r = A.shape[0]
+    _need(A, "A", torch.bfloat16, (r, w.cols), w.device)
+    _need(B, "B", torch.bfloat16, (w.rows, r), w.device)
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device)
+    _need(out, "out", torch.bfloat16, (w.rows, w.cols), w.device)
+    desc = w.descriptor()
+    _lib.check("qlora_nf4_merge",
+               lib.qlora_nf4_merge(ctypes.byref(desc), A.data_ptr(), B.data_ptr(), int(r),
+                                   float(alpha), out.data_ptr(), _stream(stream)))
+    return out
+
+
 def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 

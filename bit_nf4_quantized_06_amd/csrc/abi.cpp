@@ -2,6 +2,7 @@
 // the caller's stream.  No allocation, no synchronisation, no retained state
 // other than a per-device "is gfx950" cache.
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -42,7 +43,7 @@ struct TimingPair {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
-thread_local TimingPair g_timing[4];
+thread_local TimingPair g_timing[5];
 
 // Run `launch` between the caller's timing events of group `which` (if set).
 template <typename F>
@@ -69,7 +70,7 @@ extern "C" {
 int qlora_last_hip_error(void) { return g_last_hip_error; }
 
 qlora_status qlora_set_timing_events(int which, void* start_event, void* stop_event) {
-  if (which < 0 || which > 3) return QLORA_ERR_SHAPE;
+  if (which < 0 || which > 4) return QLORA_ERR_SHAPE;
   g_timing[which].start = static_cast<hipEvent_t>(start_event);
   g_timing[which].stop = static_cast<hipEvent_t>(stop_event);
   return QLORA_OK;
@@ -110,6 +111,34 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, v
     return launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n,
                              W_bf16, st);
   });
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_nf4_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B,
+                             int32_t r, float alpha, uint16_t* W_merged, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_descriptor(w, &d);
+  if (s != QLORA_OK) return s;
+  if (!A || !B || !W_merged) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(W_merged)) return QLORA_ERR_ALIGN;
+  if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0 || !isfinite(alpha)) return QLORA_ERR_SHAPE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MergeArgs m;
+  m.codes = w->codes;
+  m.code8 = w->absmax_code;
+  m.s2 = w->absmax_scale;
+  m.mu = w->absmax_offset;
+  m.rows = d.rows;
+  m.cols = d.cols;
+  m.A = A;
+  m.B = B;
+  m.r = r;
+  m.scale = alpha / (float)r;
+  m.out = W_merged;
+  const hipError_t e = timed(QLORA_TIMING_MERGE, st, [&] { return launch_merge(m, st); });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

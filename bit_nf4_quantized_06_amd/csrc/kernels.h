@@ -57,6 +57,22 @@ struct GemvArgs {
 };
 hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream);
 
+// --- adapter merge (merge.hip) ----------------------------------------------
+// out = bf16(w_hat + scale * (B A)), B [rows, r], A [r, cols], out [rows, cols].
+struct MergeArgs {
+  const uint8_t* codes;
+  const uint8_t* code8;
+  const float* s2;
+  const float* mu;
+  int64_t rows, cols;
+  const uint16_t* A;
+  const uint16_t* B;
+  int32_t r;
+  float scale;
+  uint16_t* out;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
 // --- LoRA side products (lora.hip) ----------------------------------------
 // Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R(p, k),
 // L [T, red] bf16, P float32 [S][T][r]; R is [r, red] (R(p, k) = R[p][k]) or,

@@ -124,6 +124,26 @@ qlora_status qlora_nf4_quantize(const float *W, const qlora_nf4_weight *out, voi
  */
 qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream);
 
+/*
+ * Fold the adapter into the dequantised base (the deployment step):
+ *   W_merged = bf16( w_hat + s * (B A) ),  s = alpha / r,
+ * with w_hat the bf16 weight qlora_nf4_dequantize gives, B A accumulated in
+ * float32, s * (B A) rounded to float32, added to w_hat in float32 and the
+ * sum rounded once to bf16 (round to nearest, ties to even).
+ * (waylandz LLM book 26.2: merge once, W + (alpha/r) B A, then inference has
+ * no adapter cost; ta-paperlens 落とし穴 and Ultralytics QLoRA, Kompromisse:
+ * the merge is done on the base dequantised to 16 bit; quantising the merged
+ * weight again is qlora_nf4_quantize of its float32 values.)
+ *   w         packed weight, read only (never written).
+ *   A         [r, cols] bf16, B [rows, r] bf16, read only, 16-byte aligned.
+ *   r         16 .. 128, a multiple of 16; alpha finite.
+ *   W_merged  [rows, cols] bf16, written, 16-byte aligned.
+ * No workspace.  Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN, QLORA_ERR_SHAPE
+ * (bad descriptor, rank or alpha), QLORA_ERR_DEVICE, QLORA_ERR_HIP.
+ */
+qlora_status qlora_nf4_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B,
+                             int32_t r, float alpha, uint16_t *W_merged, void *stream);
+
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
  * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args). */
 size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd);
@@ -172,13 +192,14 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
  * turns it off).  Groups: QLORA_TIMING_FWD_GEMM (the fused forward GEMM,
  * or for T <= 64 the two kernels of the skinny forward),
  * QLORA_TIMING_DX_GEMM (the fused backward-dX GEMM), QLORA_TIMING_QUANTIZE
- * (the three quantisation kernels), QLORA_TIMING_DEQUANT.  Returns
- * QLORA_ERR_SHAPE for an unknown group.
+ * (the three quantisation kernels), QLORA_TIMING_DEQUANT, QLORA_TIMING_MERGE.
+ * Returns QLORA_ERR_SHAPE for an unknown group.
  */
 #define QLORA_TIMING_FWD_GEMM 0
 #define QLORA_TIMING_DX_GEMM 1
 #define QLORA_TIMING_QUANTIZE 2
 #define QLORA_TIMING_DEQUANT 3
+#define QLORA_TIMING_MERGE 4
 qlora_status qlora_set_timing_events(int which, void *start_event, void *stop_event);
 
 /* Static English text for a status code (never NULL). */

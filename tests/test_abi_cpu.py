@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -91,6 +91,27 @@ def test_quantize_validation_order():
     assert lib.qlora_nf4_dequantize(ctypes.byref(_desc()), MISALIGNED, None) == 3
 
 
+def test_merge_validation():
+    """qlora_nf4_merge checks pointers, alignment, rank and alpha on the host
+    (no device is touched: every call here fails before a launch)."""
+    lib = _lib.load()
+    d = ctypes.byref(_desc(1024, 1024))
+    assert lib.qlora_nf4_merge(None, FAKE, FAKE, 16, 32.0, FAKE, None) == 1
+    assert lib.qlora_nf4_merge(d, None, FAKE, 16, 32.0, FAKE, None) == 1
+    assert lib.qlora_nf4_merge(d, FAKE, None, 16, 32.0, FAKE, None) == 1
+    assert lib.qlora_nf4_merge(d, FAKE, FAKE, 16, 32.0, None, None) == 1
+    assert lib.qlora_nf4_merge(d, MISALIGNED, FAKE, 16, 32.0, FAKE, None) == 3
+    assert lib.qlora_nf4_merge(d, FAKE, MISALIGNED, 16, 32.0, FAKE, None) == 3
+    assert lib.qlora_nf4_merge(d, FAKE, FAKE, 16, 32.0, MISALIGNED, None) == 3
+    for bad_r in (0, 8, 24, 144, -16):
+        assert lib.qlora_nf4_merge(d, FAKE, FAKE, bad_r, 32.0, FAKE, None) == 2
+    assert lib.qlora_nf4_merge(d, FAKE, FAKE, 16, float("inf"), FAKE, None) == 2
+    assert lib.qlora_nf4_merge(d, FAKE, FAKE, 16, float("nan"), FAKE, None) == 2
+    bad = _desc()
+    bad.format_version = 2
+    assert lib.qlora_nf4_merge(ctypes.byref(bad), FAKE, FAKE, 16, 32.0, FAKE, None) == 7
+
+
 def test_linear_validation():
     lib = _lib.load()
     d = ctypes.byref(_desc(1024, 1024))
@@ -147,9 +168,9 @@ def test_skinny_forward_workspace():
 
 def test_timing_hook_validation():
     lib = _lib.load()
-    assert lib.qlora_set_timing_events(4, None, None) == 2
+    assert lib.qlora_set_timing_events(5, None, None) == 2
     assert lib.qlora_set_timing_events(-1, None, None) == 2
-    for k in range(4):
+    for k in range(5):
         assert lib.qlora_set_timing_events(k, None, None) == 0
 
 

@@ -61,6 +61,10 @@ WORKLOADS = {
     "bulk_8192x22016": Workload(3, "bulk_8192x22016", 0,
                                 (Linear("mlp", 8192, 22016),), outliers=True,
                                 backward=False),
+    # the bulk weight (same draws) with a rank-64 adapter, for the merge
+    "merge_8192x22016": Workload(3, "merge_8192x22016", 0,
+                                 (Linear("mlp", 8192, 22016),), rank=64, alpha=16.0,
+                                 outliers=True, backward=False),
     "block_65b_decode": Workload(4, "block_65b_decode", 16, _block(8192, 22016),
                                  rank=64, alpha=16.0, backward=False),
     "block_65b_train": Workload(4, "block_65b_train", 2048, _block(8192, 22016),
@@ -116,11 +120,12 @@ def linear_inputs(wl: Workload, li: int, *, seed: int = 0, tokens: int | None = 
     out = {
         "w": weight(n, k, seed=seed, workload=wl.index, linear=li, outliers=wl.outliers),
     }
-    if t > 0:
-        out["x"] = bf16_normal((t, k), 1.0, seed=seed, workload=wl.index, linear=li, kind=KIND_X)
+    if r > 0:
         out["a"] = bf16_normal((r, k), float(np.sqrt(1.0 / r)), seed=seed, workload=wl.index,
                                linear=li, kind=KIND_A)
         out["b"] = bf16_normal((n, r), 0.01, seed=seed, workload=wl.index, linear=li, kind=KIND_B)
+    if t > 0:
+        out["x"] = bf16_normal((t, k), 1.0, seed=seed, workload=wl.index, linear=li, kind=KIND_X)
         if wl.backward:
             out["dy"] = bf16_normal((t, n), 1.0, seed=seed, workload=wl.index, linear=li,
                                     kind=KIND_DY)
