@@ -456,6 +456,71 @@ def merge_bits(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: floa
 
 
 # --------------------------------------------------------------------------
+# Adapter optimizer step (AdamW, 32-bit states)
+# --------------------------------------------------------------------------
+def power_by_squaring(x: float, t: int) -> float:
+    """x^t for an integer t >= 0 by binary exponentiation in float64, a fixed
+    sequence of IEEE multiplications (the library computes the same)."""
+    r, b = 1.0, float(x)
+    while t:
+        if t & 1:
+            r *= b
+        b *= b
+        t >>= 1
+    return r
+
+
+def adamw_scalars(step: int, lr: float, beta1: float, beta2: float, eps: float,
+                  weight_decay: float) -> dict:
+    """float32 constants of step `step` (1-based), each one rounding of a
+    float64 value computed from the float64 hyperparameters: the decay
+    factor 1 - lr*wd, beta1, 1 - beta1, beta2, 1 - beta2, the step size
+    lr / (1 - beta1^step), sqrt(1 - beta2^step) and eps."""
+    f = np.float32
+    lr, b1, b2, wd, e = F64(lr), F64(beta1), F64(beta2), F64(weight_decay), F64(eps)
+    return {
+        "decay": f(1.0 - lr * wd),
+        "b1": f(b1), "omb1": f(1.0 - b1),
+        "b2": f(b2), "omb2": f(1.0 - b2),
+        "step_size": f(lr / (1.0 - power_by_squaring(b1, step))),
+        "bc2_sqrt": f(np.sqrt(1.0 - power_by_squaring(b2, step))),
+        "eps": f(e),
+    }
+
+
+def adamw_step(param, exp_avg, exp_avg_sq, grad, step: int, lr: float, beta1: float,
+               beta2: float, eps: float, weight_decay: float):
+    """One AdamW step on float32 arrays; returns (param, exp_avg, exp_avg_sq,
+    param_bf16_bits).
+
+    [PL] ページ化オプティマイザ and page 2 26.6.4 (paged_adamw_32bit: Adam's two
+    moments per trainable parameter, kept in 32 bit; only the adapters A, B
+    have them).  The update is Adam with decoupled weight decay (Loshchilov &
+    Hutter) and bias-corrected moments, in the form PyTorch's AdamW documents.
+    Reading: float32 master parameters and moments; with the constants of
+    adamw_scalars, every operation one IEEE float32 rounding in this order,
+    no fused multiply-add:
+      p1 = p * decay;  m1 = b1 m + (1-b1) g;  v1 = b2 v + (1-b2) (g g);
+      den = sqrt(v1) / sqrt(bc2) + eps;  p2 = p1 - step_size (m1 / den);
+    the bf16 copy for the next forward is bf16_RNE(p2).
+    """
+    k = adamw_scalars(step, lr, beta1, beta2, eps, weight_decay)
+    f32 = np.float32
+    p = np.asarray(param, f32)
+    m = np.asarray(exp_avg, f32)
+    v = np.asarray(exp_avg_sq, f32)
+    g = np.asarray(grad, f32)
+    p1 = (p * k["decay"]).astype(f32)
+    m1 = ((k["b1"] * m).astype(f32) + (k["omb1"] * g).astype(f32)).astype(f32)
+    gg = (g * g).astype(f32)
+    v1 = ((k["b2"] * v).astype(f32) + (k["omb2"] * gg).astype(f32)).astype(f32)
+    den = ((np.sqrt(v1).astype(f32) / k["bc2_sqrt"]).astype(f32) + k["eps"]).astype(f32)
+    upd = (k["step_size"] * (m1 / den).astype(f32)).astype(f32)
+    p2 = (p1 - upd).astype(f32)
+    return p2, m1, v1, bf16_bits_rne(p2)
+
+
+# --------------------------------------------------------------------------
 # (a6-a11) LoRA linear layer, forward and backward, float64
 # --------------------------------------------------------------------------
 def linear_forward(x: np.ndarray, w_hat: np.ndarray, a: np.ndarray, b: np.ndarray,
