@@ -299,6 +299,45 @@ def time_bulk(ev, dev, reps):
     }
 
 
+def time_adamw(ev, dev, reps):
+    """One AdamW step over the adapters of the 7B block (A and B of its seven
+    linears, r = 64, float32 parameters and moments, bf16 copy written)."""
+    import torch
+
+    import bit_nf4_quantized_06_amd as q
+    import workloads as WL
+    from bit_nf4_quantized_06_amd import _lib
+    lib = _lib.load()
+    wl = WL.WORKLOADS["block_7b"]
+    n = sum(wl.rank * (lin.in_features + lin.out_features) for lin in wl.linears)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    p = torch.randn(n, device=dev, generator=gen) * 0.05
+    g = torch.randn(n, device=dev, generator=gen) * 1e-3
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for step in range(1, 3):
+        q.qlora_adamw_step(p, m, v, g, step, 2e-4, weight_decay=0.01, param_bf16=pb)
+    torch.cuda.synchronize()
+    pairs = []
+    for i in range(reps):
+        a, b = ev.new(), ev.new()
+        lib.qlora_set_timing_events(5, a, b)
+        q.qlora_adamw_step(p, m, v, g, 3 + i, 2e-4, weight_decay=0.01, param_bf16=pb)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    lib.qlora_set_timing_events(5, None, None)
+    ms = sum(ev.ms(a, b) for a, b in pairs) / reps
+    nbytes = 30 * n
+    return {
+        "workload": f"adamw_7b_adapters: one AdamW step on the A and B of the 7B block's seven "
+                    f"linears (r = 64, {n} float32 parameters and moments, bf16 copy)",
+        "params": n, "ms": round(ms, 4), "bytes": nbytes,
+        "GBps": round(nbytes / ms / 1e6, 1),
+        "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
+    }
+
+
 def copy_calibration():
     """A plain device-to-device copy of a known size: its FETCH_SIZE and
     WRITE_SIZE counters give the scale between counter units and bytes."""
@@ -399,6 +438,8 @@ def main():
 
     print("[bench] timing bulk quantize/dequantize", file=sys.stderr, flush=True)
     bulk = time_bulk(ev, dev, args.bulk_reps)
+    print("[bench] timing the adapter AdamW step", file=sys.stderr, flush=True)
+    adamw = time_adamw(ev, dev, args.bulk_reps)
     torch.cuda.empty_cache()
 
     extended = None
@@ -456,6 +497,7 @@ def main():
                      "source_digest": digest},
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
         "bulk": bulk,
+        "adamw": adamw,
         "cpu_baseline": cpu,
     }
     if extended is not None:

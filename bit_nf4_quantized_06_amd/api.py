@@ -129,6 +129,28 @@ def qlora_nf4_merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float
     return out
 
 
+def qlora_adamw_step(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                     grad: torch.Tensor, step: int, lr: float, beta1: float = 0.9,
+                     beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+                     param_bf16: torch.Tensor | None = None, stream=None) -> None:
+    """One AdamW step in place on float32 param / exp_avg / exp_avg_sq
+    (qlora_adamw_step); param_bf16, if given, receives the bf16 copy."""
+    lib = _lib.load()
+    n = param.numel()
+    dev = param.device
+    for t, name in ((param, "param"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"),
+                    (grad, "grad")):
+        _need(t, name, torch.float32, tuple(param.shape), dev)
+    if param_bf16 is not None:
+        _need(param_bf16, "param_bf16", torch.bfloat16, tuple(param.shape), dev)
+    _lib.check("qlora_adamw_step",
+               lib.qlora_adamw_step(param.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(),
+                                    grad.data_ptr(),
+                                    param_bf16.data_ptr() if param_bf16 is not None else None,
+                                    int(n), int(step), float(lr), float(beta1), float(beta2),
+                                    float(eps), float(weight_decay), _stream(stream)))
+
+
 def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 

@@ -43,7 +43,7 @@ struct TimingPair {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
-thread_local TimingPair g_timing[5];
+thread_local TimingPair g_timing[6];
 
 // Run `launch` between the caller's timing events of group `which` (if set).
 template <typename F>
@@ -70,7 +70,7 @@ extern "C" {
 int qlora_last_hip_error(void) { return g_last_hip_error; }
 
 qlora_status qlora_set_timing_events(int which, void* start_event, void* stop_event) {
-  if (which < 0 || which > 4) return QLORA_ERR_SHAPE;
+  if (which < 0 || which > 5) return QLORA_ERR_SHAPE;
   g_timing[which].start = static_cast<hipEvent_t>(start_event);
   g_timing[which].stop = static_cast<hipEvent_t>(stop_event);
   return QLORA_OK;
@@ -139,6 +139,40 @@ qlora_status qlora_nf4_merge(const qlora_nf4_weight* w, const uint16_t* A, const
   m.scale = alpha / (float)r;
   m.out = W_merged;
   const hipError_t e = timed(QLORA_TIMING_MERGE, st, [&] { return launch_merge(m, st); });
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq,
+                              const float* grad, uint16_t* param_bf16, int64_t n, int64_t step,
+                              double lr, double beta1, double beta2, double eps,
+                              double weight_decay, void* stream) {
+  using namespace qlora;
+  if (!param || !exp_avg || !exp_avg_sq || !grad) return QLORA_ERR_NULL;
+  if (!aligned16(param) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
+      (param_bf16 && !aligned16(param_bf16)))
+    return QLORA_ERR_ALIGN;
+  AdamwConsts k;
+  if (n < 1 || !adamw_constants(step, lr, beta1, beta2, eps, weight_decay, &k))
+    return QLORA_ERR_SHAPE;
+  const qlora_status s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AdamwArgs a;
+  a.p = param;
+  a.m = exp_avg;
+  a.v = exp_avg_sq;
+  a.g = grad;
+  a.p_bf16 = param_bf16;
+  a.n = n;
+  a.decay = k.decay;
+  a.b1 = k.b1;
+  a.omb1 = k.omb1;
+  a.b2 = k.b2;
+  a.omb2 = k.omb2;
+  a.step_size = k.step_size;
+  a.bc2_sqrt = k.bc2_sqrt;
+  a.eps = k.eps;
+  const hipError_t e = timed(QLORA_TIMING_ADAMW, st, [&] { return launch_adamw(a, st); });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

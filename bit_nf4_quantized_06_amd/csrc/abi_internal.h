@@ -44,6 +44,14 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd);
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
 
+// Step constants of qlora_adamw_step (float64 arithmetic, one rounding to
+// float32 each); false on invalid hyperparameters.
+struct AdamwConsts {
+  float decay, b1, omb1, b2, omb2, step_size, bc2_sqrt, eps;
+};
+bool adamw_constants(int64_t step, double lr, double beta1, double beta2, double eps,
+                     double weight_decay, AdamwConsts* k);
+
 qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
                                WeightDims* d);
 

@@ -57,6 +57,19 @@ struct GemvArgs {
 };
 hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream);
 
+// --- adapter optimizer step (adamw.hip) -------------------------------------
+// float32 constants of one step (computed on the host from float64 values).
+struct AdamwArgs {
+  float* p;
+  float* m;
+  float* v;
+  const float* g;
+  uint16_t* p_bf16;         // may be NULL
+  int64_t n;
+  float decay, b1, omb1, b2, omb2, step_size, bc2_sqrt, eps;
+};
+hipError_t launch_adamw(const AdamwArgs& a, hipStream_t stream);
+
 // --- adapter merge (merge.hip) ----------------------------------------------
 // out = bf16(w_hat + scale * (B A)), B [rows, r], A [r, cols], out [rows, cols].
 struct MergeArgs {

@@ -134,6 +134,35 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
   return L;
 }
 
+// x^t for an integer t >= 0 by binary exponentiation in float64 (a fixed
+// sequence of IEEE multiplications, so any implementation gets the same bits).
+static double power_by_squaring(double x, int64_t t) {
+  double r = 1.0;
+  while (t) {
+    if (t & 1) r *= x;
+    x *= x;
+    t >>= 1;
+  }
+  return r;
+}
+
+bool adamw_constants(int64_t step, double lr, double beta1, double beta2, double eps,
+                     double weight_decay, AdamwConsts* k) {
+  if (step < 1 || !isfinite(lr) || lr < 0.0 || !isfinite(eps) || eps <= 0.0 ||
+      !isfinite(weight_decay) || weight_decay < 0.0 || !(beta1 >= 0.0 && beta1 < 1.0) ||
+      !(beta2 >= 0.0 && beta2 < 1.0))
+    return false;
+  k->decay = (float)(1.0 - lr * weight_decay);
+  k->b1 = (float)beta1;
+  k->omb1 = (float)(1.0 - beta1);
+  k->b2 = (float)beta2;
+  k->omb2 = (float)(1.0 - beta2);
+  k->step_size = (float)(lr / (1.0 - power_by_squaring(beta1, step)));
+  k->bc2_sqrt = (float)sqrt(1.0 - power_by_squaring(beta2, step));
+  k->eps = (float)eps;
+  return true;
+}
+
 qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
                                WeightDims* d) {
   const qlora_status s = check_descriptor(w, d);

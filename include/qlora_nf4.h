@@ -144,6 +144,33 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight *w, uint16_t *W_bf16, v
 qlora_status qlora_nf4_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B,
                              int32_t r, float alpha, uint16_t *W_merged, void *stream);
 
+/*
+ * One AdamW step on n adapter parameters (A and B of a linear, in one or
+ * several calls), float32 master parameters and moments:
+ *   p1 = p * (1 - lr wd);  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   p  = p1 - lr / (1 - b1^step) * m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * (ta-paperlens ページ化オプティマイザ and waylandz 26.6.4: Adam's two moments
+ * per trainable parameter in 32 bit, only for A and B; Adam with decoupled
+ * weight decay, bias-corrected, in the form PyTorch's AdamW documents.)
+ * The constants are computed on the host in float64 (b^step by binary
+ * exponentiation) and rounded once to float32; each element operation is
+ * one float32 rounding in the order above, no fused multiply-add.
+ *   param, exp_avg, exp_avg_sq  [n] float32, read and written in place.
+ *   grad        [n] float32 (dA or dB of qlora_linear_bwd), read only.
+ *   param_bf16  [n] bf16 copy for the next forward (bf16_RNE of the new
+ *               param), written; may be NULL.
+ *   step        1-based step count; hyperparameters as in PyTorch's AdamW.
+ * All pointers 16-byte aligned.  Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN,
+ * QLORA_ERR_SHAPE (n < 1, step < 1, lr < 0, eps <= 0, weight_decay < 0, a
+ * beta outside [0, 1), any non-finite value), QLORA_ERR_DEVICE, QLORA_ERR_HIP.
+ * (The pages' paging of these states to host memory is not done: the states
+ * of a 65B model's adapters fit in HBM many times over.)
+ */
+qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
+                              const float *grad, uint16_t *param_bf16, int64_t n, int64_t step,
+                              double lr, double beta1, double beta2, double eps,
+                              double weight_decay, void *stream);
+
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
  * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args). */
 size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd);
@@ -192,14 +219,15 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
  * turns it off).  Groups: QLORA_TIMING_FWD_GEMM (the fused forward GEMM,
  * or for T <= 64 the two kernels of the skinny forward),
  * QLORA_TIMING_DX_GEMM (the fused backward-dX GEMM), QLORA_TIMING_QUANTIZE
- * (the three quantisation kernels), QLORA_TIMING_DEQUANT, QLORA_TIMING_MERGE.
- * Returns QLORA_ERR_SHAPE for an unknown group.
+ * (the three quantisation kernels), QLORA_TIMING_DEQUANT, QLORA_TIMING_MERGE,
+ * QLORA_TIMING_ADAMW.  Returns QLORA_ERR_SHAPE for an unknown group.
  */
 #define QLORA_TIMING_FWD_GEMM 0
 #define QLORA_TIMING_DX_GEMM 1
 #define QLORA_TIMING_QUANTIZE 2
 #define QLORA_TIMING_DEQUANT 3
 #define QLORA_TIMING_MERGE 4
+#define QLORA_TIMING_ADAMW 5
 qlora_status qlora_set_timing_events(int which, void *start_event, void *stop_event);
 
 /* Static English text for a status code (never NULL). */

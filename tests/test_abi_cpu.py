@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -112,6 +112,24 @@ def test_merge_validation():
     assert lib.qlora_nf4_merge(ctypes.byref(bad), FAKE, FAKE, 16, 32.0, FAKE, None) == 7
 
 
+def test_adamw_validation():
+    """qlora_adamw_step checks pointers, alignment and hyperparameters on the
+    host (every call here fails before a launch)."""
+    lib = _lib.load()
+    ok = dict(n=1024, step=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0)
+
+    def call(p=FAKE, m=FAKE, v=FAKE, g=FAKE, pb=None, **kw):
+        a = dict(ok, **kw)
+        return lib.qlora_adamw_step(p, m, v, g, pb, a["n"], a["step"], a["lr"], a["b1"],
+                                    a["b2"], a["eps"], a["wd"], None)
+    assert call(p=None) == 1 and call(m=None) == 1 and call(v=None) == 1 and call(g=None) == 1
+    assert call(p=MISALIGNED) == 3 and call(g=MISALIGNED) == 3 and call(pb=MISALIGNED) == 3
+    for bad in (dict(n=0), dict(step=0), dict(lr=-1e-3), dict(eps=0.0), dict(eps=-1.0),
+                dict(wd=-0.1), dict(b1=1.0), dict(b2=-0.1), dict(lr=float("nan")),
+                dict(b1=float("inf"))):
+        assert call(**bad) == 2, bad
+
+
 def test_linear_validation():
     lib = _lib.load()
     d = ctypes.byref(_desc(1024, 1024))
@@ -168,9 +186,9 @@ def test_skinny_forward_workspace():
 
 def test_timing_hook_validation():
     lib = _lib.load()
-    assert lib.qlora_set_timing_events(5, None, None) == 2
+    assert lib.qlora_set_timing_events(6, None, None) == 2
     assert lib.qlora_set_timing_events(-1, None, None) == 2
-    for k in range(5):
+    for k in range(6):
         assert lib.qlora_set_timing_events(k, None, None) == 0
 
 
