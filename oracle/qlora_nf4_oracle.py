@@ -26,7 +26,10 @@ Readings where the pages are silent (each is listed in the design doc):
     d = RN32(c - mu), s2 = max |d| per group of 256 blocks, code8 = OCP E4M3
     round-to-nearest-even of RN32(d / s2) * 256;
   * dequantisation: c' = RN32(RN32(e4m3(code8) * 2^-8 * s2) + mu),
-    w_hat = bf16_RNE(RN32(q[code] * c')).
+    w_hat = bf16_RNE(RN32(q[code] * c'));
+  * lora_dropout acts on the adapter's input only, with keep decisions from
+    Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC11) as dropout_keep_mask
+    states, and inverted scaling 1 / (1 - p).
 """
 
 from __future__ import annotations
@@ -578,6 +581,145 @@ def lora_grads(x: np.ndarray, dy: np.ndarray, a: np.ndarray, b: np.ndarray, alph
     da = s * (g.T @ x)
     db = s * (dy.T @ (x @ a.T))
     return da, db
+
+
+# --------------------------------------------------------------------------
+# lora_dropout: counter-based keep mask, and the layer with dropout
+# --------------------------------------------------------------------------
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers of Philox-4x32
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key increments between rounds
+_U32 = 0xFFFFFFFF
+
+
+def philox4x32_10(counter, key):
+    """Philox-4x32 with 10 rounds on one counter, in Python integers.
+
+    Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+    3" (SC11), the Philox-4x32 bijection: a round forms the 64-bit products of
+    counter words 0 and 2 with the two round multipliers; the new counter is
+    (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)); the first
+    round uses the key as given and each later round the key advanced by the
+    two increments once more (all words modulo 2^32).
+    """
+    x0, x1, x2, x3 = (int(v) & _U32 for v in counter)
+    k0, k1 = (int(v) & _U32 for v in key)
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + PHILOX_W[0]) & _U32
+            k1 = (k1 + PHILOX_W[1]) & _U32
+        p0 = PHILOX_M[0] * x0
+        p1 = PHILOX_M[1] * x2
+        x0, x1, x2, x3 = (p1 >> 32) ^ x1 ^ k0, p1 & _U32, (p0 >> 32) ^ x3 ^ k1, p0 & _U32
+    return x0, x1, x2, x3
+
+
+def philox4x32_10_array(c0, c1, c2, c3, key):
+    """philox4x32_10 on arrays of counters (any integer arrays of 32-bit
+    words, broadcast together) with one key; returns four uint64 arrays.
+    The products of two 32-bit words fit uint64 exactly."""
+    m = np.uint64(_U32)
+    x0, x1, x2, x3 = np.broadcast_arrays(*(np.asarray(v).astype(np.uint64) & m
+                                           for v in (c0, c1, c2, c3)))
+    k0, k1 = (int(v) & _U32 for v in key)
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + PHILOX_W[0]) & _U32
+            k1 = (k1 + PHILOX_W[1]) & _U32
+        p0 = x0 * np.uint64(PHILOX_M[0])
+        p1 = x2 * np.uint64(PHILOX_M[1])
+        x0, x1, x2, x3 = ((p1 >> np.uint64(32)) ^ x1 ^ np.uint64(k0), p1 & m,
+                          (p0 >> np.uint64(32)) ^ x3 ^ np.uint64(k1), p0 & m)
+    return x0, x1, x2, x3
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p 2^32) for 0 <= p < 1: a random word below it drops its
+    element, so an element is kept with probability 1 - floor(p 2^32) / 2^32."""
+    p = F64(p)
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must lie in [0, 1)")
+    return int(np.floor(p * F64(2.0 ** 32)))
+
+
+def dropout_keep_mask(T: int, cols: int, p: float, seed: int, offset: int,
+                      tokens=None) -> np.ndarray:
+    """Keep mask (bool [T, cols], or [len(tokens), cols] for the selected
+    token indices) of the adapter's input dropout.
+
+    [PL] コードで見る and 現場ではこう使う, [WZ] 26.4.2 / 26.5.1 / 26.6.4: the
+    adapter config sets lora_dropout (0.05 in every example); the pages
+    define no random stream.  Reading: element (t, k) of X [T, cols] is kept
+    iff word (t mod 4) of Philox-4x32-10 at counter (k, floor(t / 4),
+    offset mod 2^32, floor(offset / 2^32)) with key (seed mod 2^32,
+    floor(seed / 2^32)) is at least dropout_threshold(p).
+    """
+    thr = dropout_threshold(p)
+    t = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    k = np.arange(cols, dtype=np.int64)
+    words = philox4x32_10_array(k[None, :], (t >> 2)[:, None], offset & _U32,
+                                (offset >> 32) & _U32, (seed & _U32, (seed >> 32) & _U32))
+    w = np.choose((t & 3)[:, None], words)
+    return w >= np.uint64(thr)
+
+
+def dropout_mask_bytes(keep: np.ndarray) -> np.ndarray:
+    """The packed form of a keep mask [T, cols] (cols even): uint8
+    [ceil(T/4), cols/2], the bit of element (t, k) is bit (t mod 4) of the
+    low nibble (k even) or high nibble (k odd) of byte [t // 4, k // 2];
+    bits of tokens past T are 0.  Four consecutive tokens of one feature
+    share a nibble."""
+    keep = np.asarray(keep, dtype=bool)
+    T, cols = keep.shape
+    quads = (T + 3) // 4
+    full = np.zeros((quads * 4, cols), dtype=np.uint8)
+    full[:T] = keep
+    nib = np.zeros((quads, cols), dtype=np.uint8)
+    for j in range(4):
+        nib |= full[j::4] << j
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def dropout_input(x: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """The dropped adapter input before scaling: x where kept, +0 elsewhere
+    (float64 of the bf16 values)."""
+    return np.where(keep, np.asarray(x, dtype=F64), 0.0)
+
+
+def linear_forward_dropout(x: np.ndarray, w_hat: np.ndarray, a: np.ndarray, b: np.ndarray,
+                           alpha: float, r: int, keep: np.ndarray, p: float):
+    """Y = X W^T + s (D(X) A^T) B^T with D(X) = keep * X / (1 - p), float64.
+
+    Reading of lora_dropout (see dropout_keep_mask): dropout acts on the
+    adapter's input only, the frozen path sees X unchanged, and kept elements
+    are scaled by 1 / (1 - p) so the expectation is the undropped layer.
+    Returns (Y, U) with U = D(X) A^T, the tensor the backward needs for dB.
+    """
+    x = np.asarray(x, dtype=F64)
+    xd = dropout_input(x, keep) / (1.0 - F64(p))
+    s = F64(alpha) / F64(r)
+    u = xd @ np.asarray(a, dtype=F64).T
+    y = x @ np.asarray(w_hat, dtype=F64).T + s * (u @ np.asarray(b, dtype=F64).T)
+    return y, u
+
+
+def linear_backward_dropout(x: np.ndarray, dy: np.ndarray, w_hat: np.ndarray, a: np.ndarray,
+                            b: np.ndarray, alpha: float, r: int, keep: np.ndarray, p: float):
+    """Gradients of L = <dY, Y> for linear_forward_dropout; no dW.
+      G  = dY B
+      dX = dY W_hat + keep * (s G A) / (1 - p)
+      dA = s G^T D(X)
+      dB = s dY^T (D(X) A^T)
+    """
+    dy = np.asarray(dy, dtype=F64)
+    a = np.asarray(a, dtype=F64)
+    s = F64(alpha) / F64(r)
+    inv = 1.0 / (1.0 - F64(p))
+    xd = dropout_input(x, keep) * inv
+    g = dy @ np.asarray(b, dtype=F64)
+    dx = dy @ np.asarray(w_hat, dtype=F64) + np.where(keep, s * (g @ a), 0.0) * inv
+    da = s * (g.T @ xd)
+    db = s * (dy.T @ (xd @ a.T))
+    return dx, da, db
 
 
 def lora_param_count(d: int, k: int, r: int) -> int:
