@@ -642,24 +642,26 @@ def dropout_threshold(p: float) -> int:
 
 
 def dropout_keep_mask(T: int, cols: int, p: float, seed: int, offset: int,
-                      tokens=None) -> np.ndarray:
-    """Keep mask (bool [T, cols], or [len(tokens), cols] for the selected
-    token indices) of the adapter's input dropout.
+                      tokens=None, features=None) -> np.ndarray:
+    """Keep mask (bool [T, cols]; [len(tokens), len(features)] for selected
+    token and feature indices) of the adapter's input dropout.
 
     [PL] コードで見る and 現場ではこう使う, [WZ] 26.4.2 / 26.5.1 / 26.6.4: the
     adapter config sets lora_dropout (0.05 in every example); the pages
     define no random stream.  Reading: element (t, k) of X [T, cols] is kept
     iff word (t mod 4) of Philox-4x32-10 at counter (k, floor(t / 4),
     offset mod 2^32, floor(offset / 2^32)) with key (seed mod 2^32,
-    floor(seed / 2^32)) is at least dropout_threshold(p).
+    floor(seed / 2^32)) is at least dropout_threshold(p).  The generator runs
+    once per needed (t // 4, k).
     """
     thr = dropout_threshold(p)
     t = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    k = np.arange(cols, dtype=np.int64)
-    words = philox4x32_10_array(k[None, :], (t >> 2)[:, None], offset & _U32,
+    k = np.arange(cols, dtype=np.int64) if features is None else np.asarray(features, np.int64)
+    quads, inv = np.unique(t >> 2, return_inverse=True)
+    words = philox4x32_10_array(k[None, :], quads[:, None], offset & _U32,
                                 (offset >> 32) & _U32, (seed & _U32, (seed >> 32) & _U32))
-    w = np.choose((t & 3)[:, None], words)
-    return w >= np.uint64(thr)
+    w = np.stack(words)                                  # [4, quads, features]
+    return w[t & 3, inv.reshape(-1)] >= np.uint64(thr)
 
 
 def dropout_mask_bytes(keep: np.ndarray) -> np.ndarray:

@@ -68,6 +68,11 @@ def test_keep_decision_of_single_elements():
         assert keep[t, k] == (words[t % 4] >= thr)
     sel = [10, 2, 7]
     assert np.array_equal(O.dropout_keep_mask(11, 6, p, seed, offset, tokens=sel), keep[sel])
+    feats = [5, 0, 3]
+    assert np.array_equal(O.dropout_keep_mask(11, 6, p, seed, offset, features=feats),
+                          keep[:, feats])
+    assert np.array_equal(O.dropout_keep_mask(11, 6, p, seed, offset, tokens=sel,
+                                              features=feats), keep[sel][:, feats])
 
 
 def test_p_zero_keeps_everything():
