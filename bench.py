@@ -32,6 +32,7 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 HEADLINE = "attn_4096"
 BULK = "bulk_8192x22016"
 MERGE = "merge_8192x22016"
+DROPOUT_P = 0.05              # lora_dropout of the adapter configs on the pages
 
 
 def parse_args():
@@ -142,12 +143,13 @@ def to_dev_bf16(bits, dev):
 class LinearSet:
     """Device-resident inputs, packed weights and outputs of a workload."""
 
-    def __init__(self, wl, dev, tokens=None, backward=True):
+    def __init__(self, wl, dev, tokens=None, backward=True, dropout=None):
         import torch
 
         import bit_nf4_quantized_06_amd as q
         import workloads as WL
         self.wl = wl
+        self.dropout = dropout          # lora_dropout probability, or None
         self.T = wl.tokens if tokens is None else tokens
         self.r, self.alpha = wl.rank, wl.alpha
         self.items = []
@@ -159,21 +161,34 @@ class LinearSet:
             n, k, r, t = lin.out_features, lin.in_features, self.r, self.T
             it["Y"] = torch.empty(t, n, dtype=torch.bfloat16, device=dev)
             it["U"] = torch.empty(t, r, dtype=torch.bfloat16, device=dev)
-            it["wsf"] = torch.empty(q.qlora_linear_workspace(t, n, k, r, False), dtype=torch.uint8,
-                                    device=dev)
+            wsz = q.qlora_linear_workspace if dropout is None else q.qlora_linear_workspace_dropout
+            it["wsf"] = torch.empty(wsz(t, n, k, r, False), dtype=torch.uint8, device=dev)
+            if dropout is not None:
+                it["keep"] = torch.empty((t + 3) // 4, k // 2, dtype=torch.uint8, device=dev)
             if backward and "dy" in inp:
                 it["dY"] = to_dev_bf16(inp["dy"], dev)
                 it["dX"] = torch.empty(t, k, dtype=torch.bfloat16, device=dev)
                 it["dA"] = torch.empty(r, k, dtype=torch.float32, device=dev)
                 it["dB"] = torch.empty(n, r, dtype=torch.float32, device=dev)
-                it["wsb"] = torch.empty(q.qlora_linear_workspace(t, n, k, r, True),
-                                        dtype=torch.uint8, device=dev)
+                it["wsb"] = torch.empty(wsz(t, n, k, r, True), dtype=torch.uint8, device=dev)
             self.items.append(it)
             del inp
         torch.cuda.synchronize()
 
     def step(self, backward=True):
         import bit_nf4_quantized_06_amd as q
+        if self.dropout is not None:
+            for li, it in enumerate(self.items):
+                q.qlora_linear_fwd_dropout(it["wq"], it["X"], it["A"], it["B"], self.alpha,
+                                           self.dropout, 1234, li, Y=it["Y"], U_save=it["U"],
+                                           keep_save=it["keep"], workspace=it["wsf"])
+                if backward and "dY" in it:
+                    q.qlora_linear_bwd_dropout(it["wq"], it["X"], it["dY"], it["A"], it["B"],
+                                               self.alpha, self.dropout, 1234, li,
+                                               keep_saved=it["keep"], U_saved=it["U"],
+                                               dX=it["dX"], dA=it["dA"], dB=it["dB"],
+                                               workspace=it["wsb"])
+            return
         for it in self.items:
             q.qlora_linear_fwd(it["wq"], it["X"], it["A"], it["B"], self.alpha, Y=it["Y"],
                                U_save=it["U"], workspace=it["wsf"])
@@ -338,6 +353,49 @@ def time_adamw(ev, dev, reps):
     }
 
 
+def time_dropout(ev, dev, steps, warmup, reps, p):
+    """The headline workload with lora_dropout p (mask drawn in the forward,
+    kept for the backward), and the mask kernel alone on its X (draws the
+    mask, writes the dropped input)."""
+    import torch
+
+    import bit_nf4_quantized_06_amd as q
+    import workloads as WL
+    from bit_nf4_quantized_06_amd import _lib
+    lib = _lib.load()
+    wl = WL.WORKLOADS[HEADLINE]
+    ls = LinearSet(wl, dev, dropout=p)
+    tm = time_steps(ls, ev, steps, warmup, kernel_timing=False)
+    fl = ls.flops()
+    it = ls.items[0]
+    T, K = ls.T, it["lin"].in_features
+    keep = torch.empty((T + 3) // 4, K // 2, dtype=torch.uint8, device=dev)
+    xd = torch.empty_like(it["X"])
+    for i in range(3):
+        q.qlora_dropout_mask(T, K, p, 1234, i, X=it["X"], X_dropped=xd, keep=keep)
+    torch.cuda.synchronize()
+    pairs = []
+    for i in range(reps):
+        a, b = ev.new(), ev.new()
+        lib.qlora_set_timing_events(6, a, b)
+        q.qlora_dropout_mask(T, K, p, 1234, 3 + i, X=it["X"], X_dropped=xd, keep=keep)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    lib.qlora_set_timing_events(6, None, None)
+    mask_ms = sum(ev.ms(a, b) for a, b in pairs) / reps
+    nbytes = 4 * T * K + ((T + 3) // 4) * (K // 2)
+    del ls
+    return {
+        "workload": f"{HEADLINE} with lora_dropout {p:g} on the adapter input (Philox-4x32-10 "
+                    "keep mask drawn in the forward, kept for the backward)",
+        "p": p, "ms_per_step": round(tm["ms_per_step"], 4),
+        "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2),
+        "mask_ms": round(mask_ms, 4), "mask_bytes": nbytes,
+        "mask_GBps": round(nbytes / mask_ms / 1e6, 1),
+        "mask_hbm_frac": round(nbytes / mask_ms / 1e6 / PEAK_HBM_GBPS, 4),
+    }
+
+
 def copy_calibration():
     """A plain device-to-device copy of a known size: its FETCH_SIZE and
     WRITE_SIZE counters give the scale between counter units and bytes."""
@@ -441,6 +499,10 @@ def main():
     print("[bench] timing the adapter AdamW step", file=sys.stderr, flush=True)
     adamw = time_adamw(ev, dev, args.bulk_reps)
     torch.cuda.empty_cache()
+    print("[bench] timing fwd+bwd with lora_dropout", file=sys.stderr, flush=True)
+    dropout = time_dropout(ev, dev, max(5, args.steps // 2), args.warmup, args.bulk_reps,
+                           DROPOUT_P)
+    torch.cuda.empty_cache()
 
     extended = None
     if args.extended:
@@ -498,6 +560,7 @@ def main():
         "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
         "bulk": bulk,
         "adamw": adamw,
+        "dropout": dropout,
         "cpu_baseline": cpu,
     }
     if extended is not None:

@@ -31,11 +31,21 @@ class Nf4WeightDesc(ctypes.Structure):
     ]
 
 
+class DropoutDesc(ctypes.Structure):
+    """Mirror of the C struct qlora_dropout."""
+    _fields_ = [
+        ("p", ctypes.c_double),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+    ]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 _DESC_P = ctypes.POINTER(Nf4WeightDesc)
+_DROP_P = ctypes.POINTER(DropoutDesc)
 
 SIGNATURES = {
     "qlora_nf4_weight_init": (ctypes.c_int, [_DESC_P, _I64, _I64]),
@@ -53,6 +63,14 @@ SIGNATURES = {
                                         _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_DESC_P, _P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _P, _SZ, _P]),
+    "qlora_dropout_mask_bytes": (_SZ, [_I64, _I64]),
+    "qlora_dropout_mask": (ctypes.c_int, [_DROP_P, _I64, _I64, _P, _P, _P, _P]),
+    "qlora_linear_workspace_dropout": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_int]),
+    "qlora_linear_fwd_dropout": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float,
+                                                _DROP_P, _P, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_bwd_dropout": (ctypes.c_int, [_DESC_P, _P, _P, _I64, _P, _P, _I32,
+                                                ctypes.c_float, _DROP_P, _P, _P, _P, _P, _P,
+                                                _P, _SZ, _P]),
     "qlora_set_timing_events": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_last_hip_error": (ctypes.c_int, []),

@@ -224,3 +224,133 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
                                     dX.data_ptr(), dA.data_ptr(), dB.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return dX, dA, dB
+
+
+# --------------------------------------------------------------------------
+# lora_dropout
+# --------------------------------------------------------------------------
+def _dropout_desc(p: float, seed: int, offset: int) -> _lib.DropoutDesc:
+    return _lib.DropoutDesc(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                            int(offset) & 0xFFFFFFFFFFFFFFFF)
+
+
+def qlora_dropout_mask_bytes(T: int, cols: int) -> int:
+    return int(_lib.load().qlora_dropout_mask_bytes(T, cols))
+
+
+def qlora_dropout_mask(T: int, cols: int, p: float, seed: int, offset: int,
+                       X: torch.Tensor | None = None, X_dropped: torch.Tensor | None = None,
+                       keep: torch.Tensor | None = None, device=None, stream=None):
+    """Packed keep mask (uint8 [ceil(T/4), cols/2]) of lora_dropout and, when
+    X is given, the dropped input (x where kept, +0 elsewhere; the
+    1 / (1 - p) scale not applied) (qlora_dropout_mask).  Returns
+    (keep, X_dropped)."""
+    lib = _lib.load()
+    dev = X.device if X is not None else (device or torch.device("cuda"))
+    quads = (T + 3) // 4
+    if keep is None:
+        keep = torch.empty(quads, cols // 2, dtype=torch.uint8, device=dev)
+    _need(keep, "keep", torch.uint8, (quads, cols // 2), dev)
+    if X is not None:
+        _need(X, "X", torch.bfloat16, (T, cols), dev)
+        if X_dropped is None:
+            X_dropped = torch.empty_like(X)
+        _need(X_dropped, "X_dropped", torch.bfloat16, (T, cols), dev)
+    d = _dropout_desc(p, seed, offset)
+    _lib.check("qlora_dropout_mask",
+               lib.qlora_dropout_mask(ctypes.byref(d), T, cols, _ptr(X), _ptr(X_dropped),
+                                      keep.data_ptr(), _stream(stream)))
+    return keep, X_dropped
+
+
+def qlora_linear_workspace_dropout(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
+    return int(_lib.load().qlora_linear_workspace_dropout(T, rows, cols, r, int(bool(is_bwd))))
+
+
+def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             alpha: float, p: float, seed: int, offset: int,
+                             Y: torch.Tensor | None = None, U_save: torch.Tensor | None = None,
+                             save_u: bool = True, keep_save: torch.Tensor | None = None,
+                             save_keep: bool = True, workspace: torch.Tensor | None = None,
+                             stream=None):
+    """Forward with lora_dropout on the adapter input (qlora_linear_fwd_dropout):
+    Y = X dequant(W)^T + (alpha/r) (D(X) A^T) B^T, D(X) = keep X / (1 - p).
+    Returns (Y, U, keep) with U = D(X) A^T in bf16 and the packed keep mask
+    (each None when not saved)."""
+    lib = _lib.load()
+    T = X.shape[0]
+    r = A.shape[0]
+    dev = w.device
+    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
+    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
+    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    if Y is None:
+        Y = torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
+    _need(Y, "Y", torch.bfloat16, (T, w.rows), dev)
+    if U_save is None and save_u:
+        U_save = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+    if U_save is not None:
+        _need(U_save, "U_save", torch.bfloat16, (T, r), dev)
+    quads = (T + 3) // 4
+    if keep_save is None and save_keep:
+        keep_save = torch.empty(quads, w.cols // 2, dtype=torch.uint8, device=dev)
+    if keep_save is not None:
+        _need(keep_save, "keep_save", torch.uint8, (quads, w.cols // 2), dev)
+    ws_bytes = lib.qlora_linear_workspace_dropout(T, w.rows, w.cols, r, 0)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    desc = w.descriptor()
+    d = _dropout_desc(p, seed, offset)
+    _lib.check("qlora_linear_fwd_dropout",
+               lib.qlora_linear_fwd_dropout(ctypes.byref(desc), X.data_ptr(), T, A.data_ptr(),
+                                            B.data_ptr(), r, float(alpha), ctypes.byref(d),
+                                            Y.data_ptr(), _ptr(U_save), _ptr(keep_save),
+                                            workspace.data_ptr(), workspace.numel(),
+                                            _stream(stream)))
+    return Y, U_save, keep_save
+
+
+def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                             B: torch.Tensor, alpha: float, p: float, seed: int, offset: int,
+                             keep_saved: torch.Tensor | None = None,
+                             U_saved: torch.Tensor | None = None,
+                             dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                             dB: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None):
+    """Backward with lora_dropout (qlora_linear_bwd_dropout): dX (bf16), dA and
+    dB (float32); no dW.  keep_saved / U_saved from the forward, or None to
+    redraw / recompute them."""
+    lib = _lib.load()
+    T = X.shape[0]
+    r = A.shape[0]
+    dev = w.device
+    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
+    _need(dY, "dY", torch.bfloat16, (T, w.rows), dev)
+    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
+    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    if U_saved is not None:
+        _need(U_saved, "U_saved", torch.bfloat16, (T, r), dev)
+    if keep_saved is not None:
+        _need(keep_saved, "keep_saved", torch.uint8, ((T + 3) // 4, w.cols // 2), dev)
+    if dX is None:
+        dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty(r, w.cols, dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty(w.rows, r, dtype=torch.float32, device=dev)
+    _need(dX, "dX", torch.bfloat16, (T, w.cols), dev)
+    _need(dA, "dA", torch.float32, (r, w.cols), dev)
+    _need(dB, "dB", torch.float32, (w.rows, r), dev)
+    ws_bytes = lib.qlora_linear_workspace_dropout(T, w.rows, w.cols, r, 1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    desc = w.descriptor()
+    d = _dropout_desc(p, seed, offset)
+    _lib.check("qlora_linear_bwd_dropout",
+               lib.qlora_linear_bwd_dropout(ctypes.byref(desc), X.data_ptr(), dY.data_ptr(), T,
+                                            A.data_ptr(), B.data_ptr(), r, float(alpha),
+                                            ctypes.byref(d), _ptr(keep_saved), _ptr(U_saved),
+                                            dX.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                            workspace.data_ptr(), workspace.numel(),
+                                            _stream(stream)))
+    return dX, dA, dB

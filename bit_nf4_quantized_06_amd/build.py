@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["quantize.hip", "lora.hip", "gemm.hip", "gemv.hip", "merge.hip", "adamw.hip"]
+HIP_SOURCES = ["quantize.hip", "lora.hip", "gemm.hip", "gemv.hip", "merge.hip", "adamw.hip",
+               "dropout.hip"]
 HOST_SOURCES = ["abi.cpp", "validate.cpp"]
 ARCH = "gfx950"
 

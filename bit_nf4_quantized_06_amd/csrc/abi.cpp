@@ -43,7 +43,7 @@ struct TimingPair {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
-thread_local TimingPair g_timing[6];
+thread_local TimingPair g_timing[7];
 
 // Run `launch` between the caller's timing events of group `which` (if set).
 template <typename F>
@@ -65,12 +65,140 @@ T* ws_ptr(void* ws, size_t off) {
 
 }  // namespace
 
+namespace {
+
+using namespace qlora;
+
+// General forward path: U = inv (Xa A^T) by split reduction (U_save =
+// bf16(U), Us = bf16(s U)), then Y = X dequant(W)^T + Us B^T in the fused
+// GEMM.  Xa is X, or under lora_dropout the dropped input (inv = 1 / (1-p)).
+hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, const uint16_t* X,
+                               const uint16_t* Xa, int64_t T, const uint16_t* A,
+                               const uint16_t* B, int32_t r, float scale, float inv,
+                               uint16_t* Y, uint16_t* U_save, void* ws, const LinearWs& L,
+                               hipStream_t st) {
+  uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * U)
+  float* P = ws_ptr<float>(ws, L.proj_off);
+  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, st);
+  if (e == hipSuccess) {
+    TransposeJobs none;
+    none.n = 0;
+    e = launch_lora_proj_reduce(
+        ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0}, none, st);
+  }
+  if (e == hipSuccess) {
+    GemmArgs g;
+    g.act = X;
+    g.codes = w->codes;
+    g.code8 = w->absmax_code;
+    g.s2 = w->absmax_scale;
+    g.mu = w->absmax_offset;
+    g.rows = d.rows;
+    g.cols = d.cols;
+    g.lora_l = Us;
+    g.lora_r = B;
+    g.r = r;
+    g.out = Y;
+    g.T = T;
+    g.keep = nullptr;
+    e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
+  }
+  return e;
+}
+
+// Backward: G = dY B (Gn = bf16(inv G), Gs = bf16(s inv G)), the A^T
+// transpose, U if not saved, dX = dY dequant(W) + keep * (Gs A) in the fused
+// GEMM, then dA = s Gn^T Xa and dB = s dY^T U.  Without dropout Xa = X,
+// inv = 1 and keep = NULL.
+hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uint16_t* Xa,
+                       const uint16_t* dY, int64_t T, const uint16_t* A, const uint16_t* B,
+                       int32_t r, float scale, float inv, const uint8_t* keep,
+                       const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
+                       const LinearWs& L, hipStream_t st) {
+  uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
+  uint16_t* Gs = ws_ptr<uint16_t>(ws, L.g_off);     // [T, r] bf16(s inv dY B)
+  uint16_t* Gn = ws_ptr<uint16_t>(ws, L.gn_off);    // [T, r] bf16(inv dY B)
+  uint16_t* Un = ws_ptr<uint16_t>(ws, L.un_off);    // [T, r] bf16(inv Xa A^T) if not given
+  float* P = ws_ptr<float>(ws, L.proj_off);
+
+  // G = dY B (B read in place as [rows, r]); its reduction writes the dX
+  // seed's left operand and dA's, and the same launch transposes A for the
+  // dX seed
+  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, st);
+  if (e == hipSuccess) {
+    TransposeJobs tj;
+    tj.n = 1;
+    tj.job[0] = TransposeJob{A, r, d.cols, At, r};
+    e = launch_lora_proj_reduce(
+        ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0}, tj, st);
+  }
+  // U for dB when the forward's U was not kept: recompute inv Xa A^T
+  const uint16_t* U = U_saved;
+  if (e == hipSuccess && !U_saved) {
+    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, st);
+    if (e == hipSuccess) {
+      TransposeJobs none;
+      none.n = 0;
+      e = launch_lora_proj_reduce(
+          ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, inv, nullptr, 0}, none, st);
+    }
+    U = Un;
+  }
+  if (e == hipSuccess) {
+    GemmArgs g;
+    g.act = dY;
+    g.codes = w->codes;
+    g.code8 = w->absmax_code;
+    g.s2 = w->absmax_scale;
+    g.mu = w->absmax_offset;
+    g.rows = d.rows;
+    g.cols = d.cols;
+    g.lora_l = Gs;
+    g.lora_r = At;
+    g.r = r;
+    g.out = dX;
+    g.T = T;
+    g.keep = keep;
+    e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
+  }
+  // dA = s Gn^T Xa and dB = s dY^T U: partials of both in one launch, then
+  // one fixed-order reduction
+  if (e == hipSuccess) {
+    GradJobs gj;
+    gj.n = 2;
+    gj.job[0] = GradJob{Gn, Xa, d.cols, ws_ptr<float>(ws, L.grad_off), dA, 0};
+    gj.job[1] = GradJob{U, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
+    e = launch_lora_grad_partial(gj, T, r, L.s_grad, st);
+    if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
+  }
+  return e;
+}
+
+hipError_t enqueue_dropout(const DropoutConsts& k, int64_t T, int64_t cols, const uint16_t* X,
+                           uint16_t* Xd, uint8_t* keep, bool generate, hipStream_t st) {
+  DropoutArgs a;
+  a.X = X;
+  a.Xd = Xd;
+  a.keep = keep;
+  a.T = T;
+  a.cols = cols;
+  a.thr = k.thr;
+  a.key0 = k.key0;
+  a.key1 = k.key1;
+  a.ctr2 = k.ctr2;
+  a.ctr3 = k.ctr3;
+  a.generate = generate;
+  return timed(QLORA_TIMING_DROPOUT, st, [&] { return launch_dropout(a, st); });
+}
+
+}  // namespace
+
 extern "C" {
 
 int qlora_last_hip_error(void) { return g_last_hip_error; }
 
 qlora_status qlora_set_timing_events(int which, void* start_event, void* stop_event) {
-  if (which < 0 || which > 5) return QLORA_ERR_SHAPE;
+  if (which < 0 || which > QLORA_TIMING_DROPOUT) return QLORA_ERR_SHAPE;
   g_timing[which].start = static_cast<hipEvent_t>(start_event);
   g_timing[which].stop = static_cast<hipEvent_t>(stop_event);
   return QLORA_OK;
@@ -219,31 +347,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
         timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_gemv(ga, st); });
     return e == hipSuccess ? QLORA_OK : hip_fail(e);
   }
-  uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * X A^T)
-  float* P = ws_ptr<float>(ws, L.proj_off);
-  hipError_t e = launch_lora_proj_partial(X, A, false, T, d.cols, r, L.s_proj_x, P, st);
-  if (e == hipSuccess) {
-    TransposeJobs none;
-    none.n = 0;
-    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale, nullptr, 0},
-                                none, st);
-  }
-  if (e == hipSuccess) {
-    GemmArgs g;
-    g.act = X;
-    g.codes = w->codes;
-    g.code8 = w->absmax_code;
-    g.s2 = w->absmax_scale;
-    g.mu = w->absmax_offset;
-    g.rows = d.rows;
-    g.cols = d.cols;
-    g.lora_l = Us;
-    g.lora_r = B;
-    g.r = r;
-    g.out = Y;
-    g.T = T;
-    e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
-  }
+  const hipError_t e =
+      enqueue_fwd_general(w, d, X, X, T, A, B, r, scale, 1.0f, Y, U_save, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -264,63 +369,90 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float scale = alpha / (float)r;
+  const hipError_t e = enqueue_bwd(w, d, X, dY, T, A, B, r, alpha / (float)r, 1.0f, nullptr,
+                                   U_saved, dX, dA, dB, ws, L, st);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
 
-  uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
-  uint16_t* Gs = ws_ptr<uint16_t>(ws, L.g_off);     // [T, r] bf16(s * dY B)
-  uint16_t* Gn = ws_ptr<uint16_t>(ws, L.gn_off);    // [T, r] bf16(dY B)
-  uint16_t* Un = ws_ptr<uint16_t>(ws, L.un_off);    // [T, r] bf16(X A^T) if not given
-  float* P = ws_ptr<float>(ws, L.proj_off);
+qlora_status qlora_dropout_mask(const qlora_dropout* dp, int64_t T, int64_t cols,
+                                const uint16_t* X, uint16_t* X_dropped, uint8_t* keep,
+                                void* stream) {
+  using namespace qlora;
+  DropoutConsts k;
+  qlora_status s = dropout_consts(dp, &k);
+  if (s != QLORA_OK) return s;
+  if (!dropout_dims_ok(T, cols)) return QLORA_ERR_SHAPE;
+  if (!keep || (X == nullptr) != (X_dropped == nullptr)) return QLORA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(keep) & 3u) != 0 || (X && !aligned16(X)) ||
+      (X_dropped && !aligned16(X_dropped)))
+    return QLORA_ERR_ALIGN;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  const hipError_t e =
+      enqueue_dropout(k, T, cols, X, X_dropped, keep, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
 
-  // G = dY B (B read in place as [rows, r]); its reduction writes (s G) for
-  // the dX seed and G for dA, and the same launch transposes A for the dX seed
-  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, st);
-  if (e == hipSuccess) {
-    TransposeJobs tj;
-    tj.n = 1;
-    tj.job[0] = TransposeJob{A, r, d.cols, At, r};
-    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale, nullptr, 0}, tj,
-                                st);
-  }
-  // U for dB when the forward's U was not kept: recompute X A^T
-  const uint16_t* U = U_saved;
-  if (e == hipSuccess && !U_saved) {
-    e = launch_lora_proj_partial(X, A, false, T, d.cols, r, L.s_proj_x, P, st);
-    if (e == hipSuccess) {
-      TransposeJobs none;
-      none.n = 0;
-      e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, nullptr, 0},
-                                  none, st);
-    }
-    U = Un;
-  }
-  // dX = dY dequant(W) + (s G) A
-  if (e == hipSuccess) {
-    GemmArgs g;
-    g.act = dY;
-    g.codes = w->codes;
-    g.code8 = w->absmax_code;
-    g.s2 = w->absmax_scale;
-    g.mu = w->absmax_offset;
-    g.rows = d.rows;
-    g.cols = d.cols;
-    g.lora_l = Gs;
-    g.lora_r = At;
-    g.r = r;
-    g.out = dX;
-    g.T = T;
-    e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
-  }
-  // dA = s G^T X and dB = s dY^T U: partials of both in one launch, then one
-  // fixed-order reduction
-  if (e == hipSuccess) {
-    GradJobs gj;
-    gj.n = 2;
-    gj.job[0] = GradJob{Gn, X, d.cols, ws_ptr<float>(ws, L.grad_off), dA, 0};
-    gj.job[1] = GradJob{U, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
-    e = launch_lora_grad_partial(gj, T, r, L.s_grad, st);
-    if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
-  }
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
+                                      const uint16_t* A, const uint16_t* B, int32_t r,
+                                      float alpha, const qlora_dropout* dp, uint16_t* Y,
+                                      uint16_t* U_save, uint8_t* keep_save, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_linear_args(w, T, r, alpha, &d);
+  if (s != QLORA_OK) return s;
+  DropoutConsts k;
+  s = dropout_consts(dp, &k);
+  if (s != QLORA_OK) return s;
+  if (!X || !A || !B || !Y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
+      (U_save && !aligned16(U_save)) || (keep_save && !aligned16(keep_save)))
+    return QLORA_ERR_ALIGN;
+  const LinearWs L = linear_ws_layout(T, d, r, false, true);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* Xd = ws_ptr<uint16_t>(ws, L.xd_off);
+  uint8_t* keep = keep_save ? keep_save : ws_ptr<uint8_t>(ws, L.keep_off);
+  hipError_t e = enqueue_dropout(k, T, d.cols, X, Xd, keep, true, st);
+  if (e == hipSuccess)
+    e = enqueue_fwd_general(w, d, X, Xd, T, A, B, r, alpha / (float)r, k.inv_keep, Y, U_save,
+                            ws, L, st);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X,
+                                      const uint16_t* dY, int64_t T, const uint16_t* A,
+                                      const uint16_t* B, int32_t r, float alpha,
+                                      const qlora_dropout* dp, const uint8_t* keep_saved,
+                                      const uint16_t* U_saved, uint16_t* dX, float* dA,
+                                      float* dB, void* ws, size_t ws_bytes, void* stream) {
+  using namespace qlora;
+  WeightDims d;
+  qlora_status s = check_linear_args(w, T, r, alpha, &d);
+  if (s != QLORA_OK) return s;
+  DropoutConsts k;
+  s = dropout_consts(dp, &k);
+  if (s != QLORA_OK) return s;
+  if (!X || !dY || !A || !B || !dX || !dA || !dB || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
+      !aligned16(dA) || !aligned16(dB) || !aligned16(ws) || (U_saved && !aligned16(U_saved)) ||
+      (keep_saved && !aligned16(keep_saved)))
+    return QLORA_ERR_ALIGN;
+  const LinearWs L = linear_ws_layout(T, d, r, true, true);
+  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  s = check_device();
+  if (s != QLORA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* Xd = ws_ptr<uint16_t>(ws, L.xd_off);
+  // with a saved mask the kernel only reads it (the pointer is not written)
+  uint8_t* keep = keep_saved ? const_cast<uint8_t*>(keep_saved) : ws_ptr<uint8_t>(ws, L.keep_off);
+  hipError_t e = enqueue_dropout(k, T, d.cols, X, Xd, keep, keep_saved == nullptr, st);
+  if (e == hipSuccess)
+    e = enqueue_bwd(w, d, Xd, dY, T, A, B, r, alpha / (float)r, k.inv_keep, keep, U_saved, dX,
+                    dA, dB, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

@@ -38,11 +38,28 @@ struct LinearWs {
   int s_proj_dy;    // split count of dY B over rows
   int s_grad;       // split count of G^T X and U^T dY over tokens
   int s_gemv;       // split count of the skinny forward (0: fused GEMM path)
-  size_t proj_off, u_off, gemv_off, gemv_u_off, at_off, g_off, gn_off, un_off, grad_off, grad_b_off, total;
+  size_t proj_off, u_off, gemv_off, gemv_u_off, at_off, g_off, gn_off, un_off, grad_off, grad_b_off;
+  size_t xd_off, keep_off;   // lora_dropout: dropped input [T, cols] bf16 and the packed mask
+  size_t total;
 };
-LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd);
+// With dropout the forward always takes the general path and the layout
+// adds the dropped input and the keep mask.
+LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd,
+                          bool dropout = false);
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
+
+// lora_dropout: shape rule of a [T, cols] input (cols % 64 == 0, T * cols
+// bf16 below 2 GiB), bytes of its packed keep mask, and the kernel constants
+// of a qlora_dropout (QLORA_ERR_NULL / QLORA_ERR_SHAPE for a NULL pointer or
+// p outside [0, 1)).
+bool dropout_dims_ok(int64_t T, int64_t cols);
+size_t dropout_mask_bytes(int64_t T, int64_t cols);
+struct DropoutConsts {
+  uint32_t thr, key0, key1, ctr2, ctr3;
+  float inv_keep;   // RN32(1 / (1 - p))
+};
+qlora_status dropout_consts(const qlora_dropout* d, DropoutConsts* k);
 
 // Step constants of qlora_adamw_step (float64 arithmetic, one rounding to
 // float32 each); false on invalid hyperparameters.

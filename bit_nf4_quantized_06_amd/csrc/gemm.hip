@@ -342,8 +342,14 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #endif
 }
 
-template <bool kBwd>
+// kDrop (backward only): the seed is multiplied element-wise by the
+// lora_dropout keep mask (g.keep) before the main loop.
+template <bool kBwd, bool kDrop>
 __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
+  // The body is compiled in the device pass only: the host pass needs just
+  // the kernel's signature, and it cannot instantiate the gfx950
+  // buffer-resource helpers for a second kernel of the same direction.
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[kStageElems];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[kStageElems];
   __shared__ __attribute__((aligned(1024))) uint16_t sa2[kStageElems];
@@ -465,6 +471,47 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
   }
+  if constexpr (kDrop) {
+    // the keep mask has one nibble per 4 tokens x 1 feature, exactly the 4
+    // consecutive rows of one column a lane holds per accumulator group.
+    // One batch of 8 byte loads per row block i (indices clamped, so the
+    // batch issues back to back; clamped rows and columns are never
+    // stored), applied before the next batch: few live registers beside
+    // the accumulators.
+    // (the lane indices pass through an empty asm so these index
+    // expressions are not merged with the epilogue's, which would keep them
+    // live across the main loop)
+    int dl32 = l32, dlhi = lhi;
+    asm volatile("" : "+v"(dl32), "+v"(dlhi));
+    const int64_t quad_bytes = out_len >> 1;
+    int64_t col_off[2];
+    uint32_t col_shift[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int64_t col = n0 + col0 + 32 * j + dl32;
+      col = col < out_len ? col : out_len - 1;
+      col_off[j] = col >> 1;
+      col_shift[j] = 4u * (uint32_t)(col & 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t nib[2][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int64_t row = m0 + 128 * wm + 32 * i + 8 * q + 4 * dlhi;
+        row = row < g.T ? row : g.T - 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          nib[j][q] = (uint32_t)g.keep[(row >> 2) * quad_bytes + col_off[j]] >> col_shift[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc[i][j][e] = ((nib[j][e >> 2] >> (e & 3)) & 1u) ? acc[i][j][e] : 0.0f;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 
   // ---- prologue ------------------------------------------------------------
   CodeRegs ca, cb;   // codes of even / odd steps
@@ -516,6 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
       }
     }
   }
+#endif
 }
 
 static unsigned num_tiles(int64_t T, int64_t out_len) {
@@ -523,14 +571,18 @@ static unsigned num_tiles(int64_t T, int64_t out_len) {
 }
 
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(qlora_gemm_kernel<false>, dim3(num_tiles(a.T, a.rows)), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((qlora_gemm_kernel<false, false>), dim3(num_tiles(a.T, a.rows)),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(qlora_gemm_kernel<true>, dim3(num_tiles(a.T, a.cols)), dim3(kThreads), 0,
-                     stream, a);
+  if (a.keep)
+    hipLaunchKernelGGL((qlora_gemm_kernel<true, true>), dim3(num_tiles(a.T, a.cols)),
+                       dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qlora_gemm_kernel<true, false>), dim3(num_tiles(a.T, a.cols)),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -31,9 +31,27 @@ struct GemmArgs {
   int32_t r;
   uint16_t* out;           // [T, out_len] bf16
   int64_t T;
+  // backward dX only: packed lora_dropout keep mask of [T, cols] (one nibble
+  // per 4 tokens x 1 feature), applied to the seed lora_l * lora_r^T; NULL
+  // for none
+  const uint8_t* keep;
 };
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
+
+// lora_dropout (dropout.hip): draw (generate) or read the packed keep mask
+// of [T, cols] and, when X is set, write Xd = X where kept, +0 elsewhere.
+struct DropoutArgs {
+  const uint16_t* X;       // [T, cols] bf16 or NULL
+  uint16_t* Xd;            // [T, cols] bf16 (with X)
+  uint8_t* keep;           // [ceil(T/4), cols/2] bytes: written or read
+  int64_t T, cols;
+  uint32_t thr;            // floor(p 2^32)
+  uint32_t key0, key1;     // generator key (seed)
+  uint32_t ctr2, ctr3;     // counter words 2, 3 (offset)
+  bool generate;
+};
+hipError_t launch_dropout(const DropoutArgs& a, hipStream_t stream);
 
 // Skinny forward for T <= kGemvMaxTokens (gemv.hip): split partials of
 // X dequant(W)^T (P) and of U = X A^T (PU), then
@@ -108,9 +126,10 @@ struct TransposeJobs {
   int n;
 };
 // v = sum_s P[s] (fixed order s = 0, 1, ...).  Each output may be NULL:
-// out_rm[t][p] = bf16(v), out_sc[t][p] = bf16(scale * v), out_tr[p][t] =
-// bf16(v) with row stride ld_tr and zeros for T <= t < ld_tr.  The same
-// launch runs the transposes of `tj` (tj.n may be 0).
+// out_rm[t][p] = bf16(scale_rm * v), out_sc[t][p] = bf16(scale * v),
+// out_tr[p][t] = bf16(scale_rm * v) with row stride ld_tr and zeros for
+// T <= t < ld_tr.  The same launch runs the transposes of `tj` (tj.n may
+// be 0).
 struct ProjReduce {
   const float* P;
   int64_t T;
@@ -119,6 +138,7 @@ struct ProjReduce {
   uint16_t* out_rm;
   uint16_t* out_sc;
   float scale;
+  float scale_rm;          // 1 except under lora_dropout (1 / (1 - p))
   uint16_t* out_tr;
   int64_t ld_tr;
 };

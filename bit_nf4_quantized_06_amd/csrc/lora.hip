@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, Tra
   }
   uint16_t b[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) b[e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu);
+  for (int e = 0; e < 4; ++e) b[e] = (uint16_t)(pack_bf16x2(v[e] * a.scale_rm, 0.0f) & 0xFFFFu);
   if (t < a.T) {
     if (a.out_rm)
       *reinterpret_cast<uint2*>(a.out_rm + i) =

@@ -75,6 +75,30 @@ bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols) {
   return true;
 }
 
+bool dropout_dims_ok(int64_t T, int64_t cols) {
+  const int64_t kMaxElems16 = (int64_t(1) << 30) - 64;
+  if (T < 1 || cols < 64 || (cols % 64) != 0 || cols > (int64_t(1) << 22)) return false;
+  return T <= kMaxElems16 / cols;
+}
+
+size_t dropout_mask_bytes(int64_t T, int64_t cols) {
+  return (size_t)((T + 3) / 4) * (size_t)(cols / 2);
+}
+
+qlora_status dropout_consts(const qlora_dropout* d, DropoutConsts* k) {
+  if (!d) return QLORA_ERR_NULL;
+  const double p = d->p;
+  if (!(p >= 0.0 && p < 1.0)) return QLORA_ERR_SHAPE;   // also rejects NaN
+  // p * 2^32 is exact in float64 and below 2^32, so its floor fits 32 bits
+  k->thr = (uint32_t)floor(p * 4294967296.0);
+  k->key0 = (uint32_t)(d->seed & 0xFFFFFFFFu);
+  k->key1 = (uint32_t)(d->seed >> 32);
+  k->ctr2 = (uint32_t)(d->offset & 0xFFFFFFFFu);
+  k->ctr3 = (uint32_t)(d->offset >> 32);
+  k->inv_keep = (float)(1.0 / (1.0 - p));
+  return QLORA_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 qlora_status check_descriptor(const qlora_nf4_weight* w, WeightDims* d) {
@@ -99,13 +123,13 @@ QuantWs quant_ws_layout(const WeightDims& d) {
   return q;
 }
 
-LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
+LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, bool dropout) {
   LinearWs L;
   memset(&L, 0, sizeof(L));
   L.s_proj_x = lora_proj_splits(T, d.cols, r);
   L.s_proj_dy = lora_proj_splits(T, d.rows, r);
   L.s_grad = lora_grad_splits(T, d.cols > d.rows ? d.cols : d.rows);
-  L.s_gemv = (!bwd && T <= kGemvMaxTokens) ? gemv_splits(d.rows, d.cols) : 0;
+  L.s_gemv = (!bwd && !dropout && T <= kGemvMaxTokens) ? gemv_splits(d.rows, d.cols) : 0;
   size_t off = 0;
   const int s_proj = bwd ? (L.s_proj_x > L.s_proj_dy ? L.s_proj_x : L.s_proj_dy) : L.s_proj_x;
   L.proj_off = off;
@@ -129,6 +153,12 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd) {
     off += align_up(sizeof(float) * (size_t)L.s_grad * (size_t)r * (size_t)d.cols, kWsAlign);
     L.grad_b_off = off;
     off += align_up(sizeof(float) * (size_t)L.s_grad * (size_t)r * (size_t)d.rows, kWsAlign);
+  }
+  if (dropout) {
+    L.xd_off = off;
+    off += align_up(2 * (size_t)T * (size_t)d.cols, kWsAlign);
+    L.keep_off = off;
+    off += align_up(dropout_mask_bytes(T, d.cols), kWsAlign);
   }
   L.total = off;
   return L;
@@ -215,6 +245,20 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
   if (!qlora::linear_dims_ok(T, rows, cols)) return 0;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
   return qlora::linear_ws_layout(T, d, r, is_bwd != 0).total;
+}
+
+size_t qlora_dropout_mask_bytes(int64_t T, int64_t cols) {
+  if (!qlora::dropout_dims_ok(T, cols)) return 0;
+  return qlora::dropout_mask_bytes(T, cols);
+}
+
+size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int32_t r,
+                                      int is_bwd) {
+  qlora::WeightDims d;
+  if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
+  if (!qlora::linear_dims_ok(T, rows, cols)) return 0;
+  if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
+  return qlora::linear_ws_layout(T, d, r, is_bwd != 0, true).total;
 }
 
 const char* qlora_status_string(qlora_status s) {

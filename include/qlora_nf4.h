@@ -212,6 +212,86 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
                               float *dB, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * lora_dropout: dropout on the adapter's input (ta-paperlens コードで見る and
+ * 現場ではこう使う, waylandz 26.4.2 / 26.5.1 / 26.6.4: LoraConfig sets
+ * lora_dropout, 0.05 in every example).  The frozen path sees X unchanged;
+ * the adapter sees D(X) = keep * X / (1 - p).
+ *
+ * Keep decisions come from Philox-4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC11): element (t, k) of
+ * X [T, cols] is kept iff word (t mod 4) of the generator at counter
+ * (k, t / 4, offset low 32 bits, offset high 32 bits) with key (seed low 32
+ * bits, seed high 32 bits) is at least floor(p * 2^32).  A call with the
+ * same seed and offset reproduces the mask; use a distinct offset per layer
+ * and step.
+ *
+ * Packed mask ("keep", qlora_dropout_mask_bytes(T, cols) bytes): the bit of
+ * element (t, k) is bit (t mod 4) of the low nibble (k even) or high nibble
+ * (k odd) of byte (t / 4) * (cols / 2) + k / 2; bits of tokens past T are 0.
+ */
+typedef struct {
+  double p;          /* drop probability, 0 <= p < 1                          */
+  uint64_t seed;     /* generator key                                         */
+  uint64_t offset;   /* generator counter words 2 and 3                       */
+} qlora_dropout;
+
+/* Bytes of the packed keep mask of T tokens x cols features (0 on bad args). */
+size_t qlora_dropout_mask_bytes(int64_t T, int64_t cols);
+
+/*
+ * Draw the keep mask of X [T, cols] into `keep` (written, 4-byte aligned)
+ * and, when X is given, the dropped input X_dropped [T, cols] bf16 (x where
+ * kept, +0 elsewhere; the 1 / (1 - p) scale is not applied).  X and
+ * X_dropped are both NULL or both set (16-byte aligned).  cols % 64 == 0,
+ * T >= 1, T * cols below 2^30.  Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN,
+ * QLORA_ERR_SHAPE (sizes, or p outside [0, 1)), QLORA_ERR_DEVICE,
+ * QLORA_ERR_HIP.
+ */
+qlora_status qlora_dropout_mask(const qlora_dropout *d, int64_t T, int64_t cols,
+                                const uint16_t *X, uint16_t *X_dropped, uint8_t *keep,
+                                void *stream);
+
+/* Workspace bytes for qlora_linear_fwd_dropout (is_bwd = 0) or
+ * qlora_linear_bwd_dropout (is_bwd = 1) (0 on bad args). */
+size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int32_t r,
+                                      int is_bwd);
+
+/*
+ * Forward with lora_dropout:
+ *   Y = X dequant(W)^T + s (D(X) A^T) B^T,   s = alpha / r.
+ *   U_save     [T, r] bf16, D(X) A^T (what dB needs), written, or NULL.
+ *   keep_save  the packed keep mask, written (16-byte aligned), or NULL (then it lives in the
+ *              workspace only); pass it to the backward to skip the redraw.
+ * Every token count takes the general path (the skinny path of
+ * qlora_linear_fwd serves inference, which has no dropout).  p = 0 gives
+ * the same bits as qlora_linear_fwd's general path.  Other arguments,
+ * shape rules and errors as qlora_linear_fwd, plus QLORA_ERR_NULL for a NULL
+ * d and QLORA_ERR_SHAPE for p outside [0, 1).
+ */
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
+                                      const uint16_t *A, const uint16_t *B, int32_t r,
+                                      float alpha, const qlora_dropout *d, uint16_t *Y,
+                                      uint16_t *U_save, uint8_t *keep_save, void *ws,
+                                      size_t ws_bytes, void *stream);
+
+/*
+ * Backward with lora_dropout (no dW):
+ *   G  = dY B
+ *   dX = dY dequant(W) + keep * (s G A) / (1 - p)
+ *   dA = s G^T D(X)
+ *   dB = s dY^T U,   U = D(X) A^T: U_saved if not NULL, else recomputed.
+ * keep_saved: the forward's keep_save (read), or NULL to redraw the mask
+ * from d (the same seed and offset as the forward).  Other arguments as
+ * qlora_linear_bwd.
+ */
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X,
+                                      const uint16_t *dY, int64_t T, const uint16_t *A,
+                                      const uint16_t *B, int32_t r, float alpha,
+                                      const qlora_dropout *d, const uint8_t *keep_saved,
+                                      const uint16_t *U_saved, uint16_t *dX, float *dA,
+                                      float *dB, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Measurement aid.  On the calling host thread, until changed, every later
  * call that launches kernel group `which` records `start_event` on the
  * caller's stream right before that group and `stop_event` right after it
@@ -220,7 +300,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
  * or for T <= 64 the two kernels of the skinny forward),
  * QLORA_TIMING_DX_GEMM (the fused backward-dX GEMM), QLORA_TIMING_QUANTIZE
  * (the three quantisation kernels), QLORA_TIMING_DEQUANT, QLORA_TIMING_MERGE,
- * QLORA_TIMING_ADAMW.  Returns QLORA_ERR_SHAPE for an unknown group.
+ * QLORA_TIMING_ADAMW, QLORA_TIMING_DROPOUT (the mask kernel).  Returns
+ * QLORA_ERR_SHAPE for an unknown group.
  */
 #define QLORA_TIMING_FWD_GEMM 0
 #define QLORA_TIMING_DX_GEMM 1
@@ -228,6 +309,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, cons
 #define QLORA_TIMING_DEQUANT 3
 #define QLORA_TIMING_MERGE 4
 #define QLORA_TIMING_ADAMW 5
+#define QLORA_TIMING_DROPOUT 6
 qlora_status qlora_set_timing_events(int which, void *start_event, void *stop_event);
 
 /* Static English text for a status code (never NULL). */

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 13
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -34,6 +34,9 @@ def test_header_functions_exported_and_bound():
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(_lib.Nf4WeightDesc) == 4 * 4 + 2 * 8 + 4 * 8
     assert _lib.Nf4WeightDesc.codes.offset == 32
+    assert ctypes.sizeof(_lib.DropoutDesc) == 24
+    assert (_lib.DropoutDesc.p.offset, _lib.DropoutDesc.seed.offset,
+            _lib.DropoutDesc.offset.offset) == (0, 8, 16)
 
 
 def _desc(rows=1024, cols=1024, codes=FAKE):
@@ -184,11 +187,74 @@ def test_skinny_forward_workspace():
     assert ws(64, 8192, 8192, 64, 1) > 0
 
 
+def _drop(p=0.05, seed=1, offset=2):
+    return ctypes.byref(_lib.DropoutDesc(p, seed, offset))
+
+
+def test_dropout_mask_validation_and_size():
+    """Mask bytes ceil(T/4) * cols/2; p outside [0, 1) (NaN included), bad
+    sizes, NULL and misaligned pointers are rejected on the host."""
+    lib = _lib.load()
+    assert lib.qlora_dropout_mask_bytes(4096, 4096) == 1024 * 2048
+    assert lib.qlora_dropout_mask_bytes(5, 64) == 2 * 32
+    assert lib.qlora_dropout_mask_bytes(0, 64) == 0
+    assert lib.qlora_dropout_mask_bytes(8, 96) == 0
+    assert lib.qlora_dropout_mask_bytes((1 << 30) // 64, 64) == 0
+    m = lib.qlora_dropout_mask
+    assert m(None, 8, 64, FAKE, FAKE, FAKE, None) == 1
+    for p in (-0.01, 1.0, 1.5, float("nan"), float("inf")):
+        assert m(_drop(p), 8, 64, FAKE, FAKE, FAKE, None) == 2, p
+    assert m(_drop(), 0, 64, FAKE, FAKE, FAKE, None) == 2
+    assert m(_drop(), 8, 100, FAKE, FAKE, FAKE, None) == 2
+    assert m(_drop(), 8, 64, FAKE, FAKE, None, None) == 1          # no mask
+    assert m(_drop(), 8, 64, FAKE, None, FAKE, None) == 1          # X without X_dropped
+    assert m(_drop(), 8, 64, None, FAKE, FAKE, None) == 1
+    assert m(_drop(), 8, 64, FAKE, FAKE, FAKE + 2, None) == 3
+    assert m(_drop(), 8, 64, MISALIGNED, FAKE, FAKE, None) == 3
+
+
+def test_linear_dropout_validation_and_workspace():
+    lib = _lib.load()
+    d = ctypes.byref(_desc(1024, 1024))
+    T, r = 512, 16
+    wsf = lib.qlora_linear_workspace_dropout(T, 1024, 1024, r, 0)
+    wsb = lib.qlora_linear_workspace_dropout(T, 1024, 1024, r, 1)
+    extra = T * 1024 * 2 + (T // 4) * 512
+    assert wsf >= lib.qlora_linear_workspace(T, 1024, 1024, r, 0) + extra
+    assert wsb >= lib.qlora_linear_workspace(T, 1024, 1024, r, 1) + extra
+    # few tokens: the dropout forward takes the general path (no skinny partials)
+    assert lib.qlora_linear_workspace_dropout(16, 8192, 8192, 64, 0) < \
+        lib.qlora_linear_workspace(16, 8192, 8192, 64, 0)
+    f = lib.qlora_linear_fwd_dropout
+    args = lambda **k: dict(dict(X=FAKE, T=T, r=r, alpha=32.0, drop=_drop(), Y=FAKE, U=None,
+                                 keep=None, ws=FAKE, wsb=wsf), **k)
+    call = lambda a: f(d, a["X"], a["T"], FAKE, FAKE, a["r"], a["alpha"], a["drop"], a["Y"],
+                       a["U"], a["keep"], a["ws"], a["wsb"], None)
+    assert call(args(wsb=wsf - 1)) == 4
+    assert call(args(drop=None)) == 1
+    assert call(args(drop=_drop(1.0))) == 2
+    assert call(args(drop=_drop(float("nan")))) == 2
+    assert call(args(X=None)) == 1
+    assert call(args(r=24)) == 2
+    assert call(args(keep=MISALIGNED)) == 3
+    b = lib.qlora_linear_bwd_dropout
+    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), None, None, FAKE, FAKE, FAKE, FAKE,
+             wsb - 1, None) == 4
+    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, None, None, None, FAKE, FAKE, FAKE, FAKE,
+             wsb, None) == 1
+    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(-0.5), None, None, FAKE, FAKE, FAKE,
+             FAKE, wsb, None) == 2
+    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), MISALIGNED, None, FAKE, FAKE, FAKE,
+             FAKE, wsb, None) == 3
+    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), None, None, FAKE, None, FAKE, FAKE,
+             wsb, None) == 1
+
+
 def test_timing_hook_validation():
     lib = _lib.load()
-    assert lib.qlora_set_timing_events(6, None, None) == 2
+    assert lib.qlora_set_timing_events(7, None, None) == 2
     assert lib.qlora_set_timing_events(-1, None, None) == 2
-    for k in range(6):
+    for k in range(7):
         assert lib.qlora_set_timing_events(k, None, None) == 0
 
 

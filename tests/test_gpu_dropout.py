@@ -1,0 +1,187 @@
+"""GPU parity of lora_dropout against the oracle: the packed keep mask and the
+dropped input bit for bit (the keep decisions are integer work on the
+Philox-4x32-10 stream), and the layer with dropout -- Y, U, dX, dA, dB --
+within the 5e-3 relative Frobenius bound of the float64 oracle, whose mask
+the oracle draws itself from the same seed and offset.  Also: the backward
+that redraws the mask and recomputes U gives the same bits as the one that
+reuses the forward's; p = 0 gives the same bits as the plain general path;
+few tokens take the general path; the attention workload at full size."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from gpu_util import GEMM_TOL, bf16_dev, bits_host, f32_dev, linear_case
+from oracle import qlora_nf4_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _api():
+    import bit_nf4_quantized_06_amd as q
+    return q
+
+
+def _f64(bits):
+    return WL.bf16_bits_value(bits).astype(np.float64)
+
+
+def _val(t):
+    return _f64(bits_host(t))
+
+
+# (name, T, cols, p, seed, offset)
+MASK_CASES = [
+    ("T1_K64", 1, 64, 0.05, 0, 0),
+    ("T7_K128_p05_bigseed", 7, 128, 0.5, (1 << 40) + 3, (1 << 33) + 5),
+    ("T130_K4160_p09", 130, 4160, 0.9, 77, 1),
+    ("T1024_K4096_p005", 1024, 4096, 0.05, 1234, 99),
+    ("T33_K64_p0", 33, 64, 0.0, 5, 6),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[c[0] for c in MASK_CASES])
+def test_mask_and_dropped_input_bit_exact(case):
+    q = _api()
+    name, T, cols, p, seed, offset = case
+    print(f"[dropout] mask case={name}", flush=True)
+    rng = np.random.default_rng(T * 7 + cols)
+    x_bits = WL.to_bf16_bits(rng.standard_normal((T, cols)).astype(np.float32))
+    keep_dev, xd_dev = q.qlora_dropout_mask(T, cols, p, seed, offset, X=bf16_dev(x_bits))
+    keep_only, none = q.qlora_dropout_mask(T, cols, p, seed, offset, device=torch.device("cuda", 0))
+    torch.cuda.synchronize()
+    assert none is None
+    keep = O.dropout_keep_mask(T, cols, p, seed, offset)
+    want = O.dropout_mask_bytes(keep)
+    got = keep_dev.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"mask bytes differ at {bad[:5].tolist()}"
+    assert np.array_equal(keep_only.cpu().numpy(), want)
+    xd_want = np.where(keep, x_bits, np.uint16(0))
+    assert np.array_equal(bits_host(xd_dev), xd_want)
+    print(f"[dropout] {name} kept {keep.mean():.4f}", flush=True)
+
+
+def _oracle(inp, st_bits, r, alpha, keep, p):
+    x, a, b, dy = (_f64(inp[k]) for k in ("x", "a", "b", "dy"))
+    w_hat = O.bf16_bits_to_f32(st_bits).astype(np.float64)
+    y, u = O.linear_forward_dropout(x, w_hat, a, b, alpha, r, keep, p)
+    dx, da, db = O.linear_backward_dropout(x, dy, w_hat, a, b, alpha, r, keep, p)
+    return {"y": y, "u": u, "dx": dx, "da": da, "db": db}
+
+
+def _check(name, got, ref):
+    errs = {k: O.rel_frobenius(got[k], ref[k]) for k in ref}
+    print(f"[dropout] {name} rel_frobenius " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for k, v in errs.items():
+        assert v <= GEMM_TOL, (name, k, v)
+
+
+# (name, T, N, K, r, alpha, p)
+LINEAR_CASES = [
+    ("T300_N1040_K1088_r32_p005", 300, 1040, 1088, 32, 32.0, 0.05),
+    ("T520_N528_K576_r64_p05", 520, 528, 576, 64, 16.0, 0.5),
+    ("T16_N256_K512_r16_p01", 16, 256, 512, 16, 32.0, 0.1),     # few tokens: general path
+    ("T3_N272_K320_r128_p03", 3, 272, 320, 128, 16.0, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=[c[0] for c in LINEAR_CASES])
+def test_linear_dropout_parity(case):
+    q = _api()
+    name, T, N, K, r, alpha, p = case
+    seed, offset = 2024 + T, 17
+    print(f"[dropout] linear case={name}", flush=True)
+    inp = linear_case(T, N, K, r, alpha, seed=12, outliers=True)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
+    Y, U, keep_dev = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, p, seed, offset)
+    dX, dA, dB = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, seed, offset,
+                                            keep_saved=keep_dev, U_saved=U)
+    torch.cuda.synchronize()
+    keep = O.dropout_keep_mask(T, K, p, seed, offset)
+    assert np.array_equal(keep_dev.cpu().numpy(), O.dropout_mask_bytes(keep))
+    ref = _oracle(inp, O.dequantize_bits(O.quantize(inp["w"])), r, alpha, keep, p)
+    got = {"y": _val(Y), "u": _val(U), "dx": _val(dX),
+           "da": dA.cpu().numpy().astype(np.float64), "db": dB.cpu().numpy().astype(np.float64)}
+    _check(name, got, ref)
+
+
+def test_backward_redraw_and_recompute_give_the_same_bits():
+    """Without keep_saved and U_saved the backward redraws the mask from the
+    seed and offset and recomputes U: the same bits as with them."""
+    q = _api()
+    T, N, K, r, alpha, p = 260, 272, 1024, 16, 32.0, 0.25
+    print("[dropout] redraw vs saved", flush=True)
+    inp = linear_case(T, N, K, r, alpha, seed=13)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
+    Y, U, keep = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, p, 9, 10)
+    g1 = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, 9, 10, keep_saved=keep, U_saved=U)
+    g2 = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, 9, 10)
+    g3 = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, 9, 11)   # another offset
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    assert not torch.equal(g1[1], g3[1])                 # dA depends on the mask
+
+
+def test_p_zero_is_the_plain_general_path_bit_for_bit():
+    q = _api()
+    T, N, K, r, alpha = 300, 528, 576, 64, 16.0
+    print("[dropout] p = 0 vs plain", flush=True)
+    inp = linear_case(T, N, K, r, alpha, seed=14)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
+    Y0, U0 = q.qlora_linear_fwd(wq, X, A, B, alpha)
+    g0 = q.qlora_linear_bwd(wq, X, dY, A, B, alpha, U_saved=U0)
+    Y1, U1, keep = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, 0.0, 1, 2)
+    g1 = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, 0.0, 1, 2, keep_saved=keep,
+                                    U_saved=U1)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    assert torch.equal(U0.view(torch.int16), U1.view(torch.int16))
+    assert torch.equal(g0[0].view(torch.int16), g1[0].view(torch.int16))
+    assert torch.equal(g0[1], g1[1]) and torch.equal(g0[2], g1[2])
+
+
+def test_attn_4096_with_dropout_full_size():
+    """The attention workload (4096 tokens, 4096 x 4096, r = 16) with
+    lora_dropout 0.05 in the benchmark's launch configuration: the mask in
+    full, bit for bit; Y and dX on 50 sampled features; U, dA, dB in full."""
+    q = _api()
+    wl = WL.WORKLOADS["attn_4096"]
+    inp = WL.linear_inputs(wl, 0)
+    N, K = inp["w"].shape
+    T, r, alpha, p, seed, offset = wl.tokens, wl.rank, wl.alpha, 0.05, 31337, 4
+    print(f"[dropout] attn_4096 full size p={p}", flush=True)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
+    Y, U, keep_dev = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, p, seed, offset)
+    dX, dA, dB = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, seed, offset,
+                                            keep_saved=keep_dev, U_saved=U)
+    torch.cuda.synchronize()
+    del wq, X, A, B, dY
+    keep = O.dropout_keep_mask(T, K, p, seed, offset)
+    assert np.array_equal(keep_dev.cpu().numpy(), O.dropout_mask_bytes(keep))
+    rng = np.random.default_rng(101)
+    sel_n = np.unique(np.concatenate([rng.choice(N, 48, replace=False), [0, N - 1]]))
+    sel_k = np.unique(np.concatenate([rng.choice(K, 48, replace=False), [0, K - 1]]))
+    w_rows = O.bf16_bits_to_f32(O.dequantize_sampled_bits(
+        O.quantize_sampled_rows(inp["w"], sel_n))).astype(np.float64)
+    w_cols = O.bf16_bits_to_f32(O.dequantize_sampled_cols_bits(
+        O.quantize_sampled_cols(inp["w"], sel_k))).astype(np.float64)
+    x, a, b, dy = (_f64(inp[k]) for k in ("x", "a", "b", "dy"))
+    y_ref, u_ref = O.linear_forward_dropout(x, w_rows, a, b[sel_n], alpha, r, keep, p)
+    # dX on the sampled input features: the mask of those features only
+    dx_ref, _, _ = O.linear_backward_dropout(x[:, sel_k], dy, w_cols, a[:, sel_k], b, alpha, r,
+                                             keep[:, sel_k], p)
+    # dA = s G^T D(X), dB = s dY^T (D(X) A^T): the adapter gradients of the
+    # scaled dropped input
+    da_ref, db_ref = O.lora_grads(O.dropout_input(x, keep) / (1.0 - p), dy, a, b, alpha, r)
+    ref = {"y": y_ref, "u": u_ref, "dx": dx_ref, "da": da_ref, "db": db_ref}
+    got = {"y": _val(Y)[:, sel_n], "u": _val(U), "dx": _val(dX)[:, sel_k],
+           "da": dA.cpu().numpy().astype(np.float64), "db": dB.cpu().numpy().astype(np.float64)}
+    _check("attn_4096 p=0.05", got, ref)
