@@ -14,9 +14,12 @@
 // make one 32-bit mask word (nibble e = feature 8j + e), then the four rows'
 // 16-byte pieces of X are masked and stored.  A wave covers 512 consecutive
 // features, so each row access is 1 KB contiguous and each mask store 256 B.
-// HBM-bound: 4 bytes per element move (X read, X_dropped written) plus 1/8
-// byte of mask; the generator costs 10 rounds of two 32x32->64-bit products
-// per 4 elements.
+// 4 bytes per element move (X read, X_dropped written) plus 1/8 byte of
+// mask, and the generator costs 10 rounds of two 32x32->64-bit products per
+// 4 elements: on 4096 x 4096 the generator alone (mask only) takes about
+// 11 us, the HBM traffic about 9 us; the kernel runs at 15 us.  (A looped
+// variant that prefetches the next unit's rows during the generator was
+// measured no faster.)
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,14 +39,15 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& x0, uint32_t& x1, uint32
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, x0);
-    const uint32_t lo0 = 0xD2511F53u * x0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2);
-    const uint32_t lo1 = 0xCD9E8D57u * x2;
-    x0 = hi1 ^ x1 ^ k0;
-    x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
-    x3 = lo0;
+    // one v_mad_u64_u32 per product and one three-input xor (bitop3 with
+    // truth table 0x96) per new word: 703 instructions for 8 calls instead
+    // of 966 with separate high and low multiplies and two-input xors
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    x0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x1, k0, 0x96);
+    x1 = (uint32_t)p1;
+    x2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x3, k1, 0x96);
+    x3 = (uint32_t)p0;
   }
 }
 
