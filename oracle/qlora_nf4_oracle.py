@@ -67,6 +67,26 @@ def nf4_levels() -> np.ndarray:
     return levels.astype(F32)
 
 
+def int4_levels() -> np.ndarray:
+    """The 16 evenly spaced 4-bit levels -1 + 2i/15 (i = 0 .. 15) as float32.
+
+    [UL] code example under "So funktioniert QLoRA": the comparison codebook
+    of 16 evenly spaced levels from -1 to 1 (no exact zero).  Each level is
+    the exact rational rounded once to float32.
+    """
+    from fractions import Fraction
+    return np.array([float(Fraction(2 * i - 15, 15)) for i in range(16)], dtype=F64).astype(F32)
+
+
+def levels_for(quant_type: str) -> np.ndarray:
+    """Codebook of a quantisation type: "nf4" or "int4" (evenly spaced)."""
+    if quant_type == "nf4":
+        return nf4_levels()
+    if quant_type == "int4":
+        return int4_levels()
+    raise ValueError(f"unknown quantisation type {quant_type!r}")
+
+
 def nf4_midpoints(levels: np.ndarray | None = None) -> np.ndarray:
     """Exact midpoints between neighbouring levels, float64 (15 values).
 
@@ -285,6 +305,34 @@ def bf16_bits_rne(x: np.ndarray) -> np.ndarray:
     return (keep + up.astype(np.uint32)).astype(np.uint16)
 
 
+def f16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns of float32 values, round to nearest even
+    (subnormals kept, overflow to infinity): NumPy's float16 conversion.
+    The compute type of older GPUs ([PL] 落とし穴: compute_dtype FP16 where
+    BF16 is missing; [WZ] 26.6.4 uses float16)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=F32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """float32 value of binary16 bit patterns (exact widening)."""
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(F32)
+
+
+def round16_bits(x: np.ndarray, compute_dtype: str) -> np.ndarray:
+    """Bit patterns of float32 values rounded to the 16-bit compute type."""
+    if compute_dtype == "bf16":
+        return bf16_bits_rne(x)
+    if compute_dtype == "fp16":
+        return f16_bits_rne(x)
+    raise ValueError(f"unknown compute dtype {compute_dtype!r}")
+
+
+def bits16_to_f32(b: np.ndarray, compute_dtype: str) -> np.ndarray:
+    """float32 values of 16-bit patterns of the compute type."""
+    return bf16_bits_to_f32(b) if compute_dtype == "bf16" else f16_bits_to_f32(b)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
 
@@ -292,50 +340,74 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # (a1-a5) quantise and dequantise a weight
 # --------------------------------------------------------------------------
-def quantize(w: np.ndarray) -> dict:
-    """Full NF4 + double quantisation of a float32 [rows, cols] weight.
+def quantize(w: np.ndarray, quant_type: str = "nf4", double_quant: bool = True) -> dict:
+    """Blockwise 4-bit quantisation of a float32 [rows, cols] weight.
 
-    The NF4 codes are taken against the original float32 block constants; the
-    8-bit constant codes are what is stored ([PL] order of presentation:
-    blockwise NF4 first, then the constants are quantised).
+    The codes are taken against the original float32 block constants; with
+    double quantisation the 8-bit constant codes are what is stored ([PL]
+    order of presentation: blockwise NF4 first, then the constants are
+    quantised).  Without it ([PL] 二重量子化, the 4.5-bit count: one float32
+    constant per 64 weights) absmax_scale holds the float32 constants.
+    quant_type "nf4" or "int4" (the evenly spaced comparison codebook).
     """
     w = np.asarray(w, dtype=F32)
     rows, cols = w.shape
     assert cols % BLOCK == 0, "cols must be a multiple of 64"
     c = block_absmax(w)
-    codes = nf4_encode(w, c)
-    code8, s2, mu = double_quantize(c)
-    return {
-        "rows": rows, "cols": cols,
-        "codes": pack_nibbles(codes),
-        "absmax_code": code8,
-        "absmax_scale": s2,
-        "absmax_offset": np.array([mu], dtype=F32),
-        "absmax_fp32": c,
-    }
+    codes = nf4_encode(w, c, levels=levels_for(quant_type))
+    st = {"rows": rows, "cols": cols, "quant_type": quant_type, "double_quant": double_quant,
+          "codes": pack_nibbles(codes), "absmax_fp32": c}
+    if double_quant:
+        code8, s2, mu = double_quantize(c)
+        st.update(absmax_code=code8, absmax_scale=s2, absmax_offset=np.array([mu], dtype=F32))
+    else:
+        st.update(absmax_scale=c.copy())
+    return st
 
 
-def dequantize_bits(state: dict) -> np.ndarray:
-    """bf16 bit patterns of the dequantised weight, uint16 [rows, cols].
+def block_constants(state: dict) -> np.ndarray:
+    """The constants the dequantiser multiplies by: c' from the 8-bit codes
+    (double quantisation) or the stored float32 c."""
+    if state.get("double_quant", True):
+        return block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
+                                       state["absmax_offset"][0])
+    return np.asarray(state["absmax_scale"], dtype=F32)
+
+
+def dequantize_bits(state: dict, compute_dtype: str = "bf16") -> np.ndarray:
+    """16-bit patterns of the dequantised weight, uint16 [rows, cols].
 
     [PL] 量子化を1段落で: restore by table lookup and multiply, x_hat = c * q[index];
-    [PL] 勾配は実際どこへ行くのか: the storage type is NF4, compute is bf16.
+    [PL] 勾配は実際どこへ行くのか: the storage type is NF4, compute is bf16
+    (fp16 where bf16 is missing, [PL] 落とし穴).
     """
     rows, cols = state["rows"], state["cols"]
     codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
-    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
-                                     state["absmax_offset"][0])
-    return _decode_bits(codes, cprime).reshape(rows, cols)
+    return _decode_bits(codes, block_constants(state), state.get("quant_type", "nf4"),
+                        compute_dtype).reshape(rows, cols)
 
 
-def _decode_bits(codes: np.ndarray, cprime: np.ndarray) -> np.ndarray:
-    """bf16_RNE(RN32(q[code] * c')) for codes [n_blocks, 64] and c' [n_blocks]."""
-    q = nf4_levels()
+def _decode_bits(codes: np.ndarray, cprime: np.ndarray, quant_type: str = "nf4",
+                 compute_dtype: str = "bf16") -> np.ndarray:
+    """round16(RN32(q[code] * c')) for codes [n_blocks, 64] and c' [n_blocks]."""
+    q = levels_for(quant_type)
     prod = (q[codes] * np.asarray(cprime, dtype=F32)[:, None]).astype(F32)
-    return bf16_bits_rne(prod)
+    return round16_bits(prod, compute_dtype)
 
 
-def quantize_sampled_rows(w: np.ndarray, sel) -> dict:
+def _constants_state(c: np.ndarray, quant_type: str, double_quant: bool) -> dict:
+    """The stored constants of quantize() for block constants c."""
+    st = {"quant_type": quant_type, "double_quant": double_quant}
+    if double_quant:
+        code8, s2, mu = double_quantize(c)
+        st.update(absmax_code=code8, absmax_scale=s2, absmax_offset=np.array([mu], dtype=F32))
+    else:
+        st.update(absmax_scale=np.asarray(c, dtype=F32).copy())
+    return st
+
+
+def quantize_sampled_rows(w: np.ndarray, sel, quant_type: str = "nf4",
+                          double_quant: bool = True) -> dict:
     """quantize() of the whole weight, keeping the NF4 codes of rows `sel` only.
 
     The block constants and their double quantisation cover every block (they
@@ -349,29 +421,26 @@ def quantize_sampled_rows(w: np.ndarray, sel) -> dict:
     sel = np.asarray(sel, dtype=np.int64).reshape(-1)
     kb = cols // BLOCK
     c = block_absmax(w)
-    code8, s2, mu = double_quantize(c)
-    codes = nf4_encode(w[sel], c.reshape(rows, kb)[sel])
-    return {
-        "rows": rows, "cols": cols, "sel": sel,
-        "codes": pack_nibbles(codes).reshape(sel.size, cols // 2),
-        "absmax_code": code8,
-        "absmax_scale": s2,
-        "absmax_offset": np.array([mu], dtype=F32),
-    }
+    codes = nf4_encode(w[sel], c.reshape(rows, kb)[sel], levels=levels_for(quant_type))
+    st = {"rows": rows, "cols": cols, "sel": sel,
+          "codes": pack_nibbles(codes).reshape(sel.size, cols // 2)}
+    st.update(_constants_state(c, quant_type, double_quant))
+    return st
 
 
-def dequantize_sampled_bits(state: dict) -> np.ndarray:
+def dequantize_sampled_bits(state: dict, compute_dtype: str = "bf16") -> np.ndarray:
     """dequantize_bits() restricted to the rows of a quantize_sampled_rows()
     state: uint16 [len(sel), cols]."""
     rows, cols, sel = state["rows"], state["cols"], state["sel"]
     kb = cols // BLOCK
-    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
-                                     state["absmax_offset"][0]).reshape(rows, kb)[sel]
+    cprime = block_constants(state).reshape(rows, kb)[sel]
     codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
-    return _decode_bits(codes, cprime.reshape(-1)).reshape(sel.size, cols)
+    return _decode_bits(codes, cprime.reshape(-1), state.get("quant_type", "nf4"),
+                        compute_dtype).reshape(sel.size, cols)
 
 
-def quantize_sampled_cols(w: np.ndarray, sel) -> dict:
+def quantize_sampled_cols(w: np.ndarray, sel, quant_type: str = "nf4",
+                          double_quant: bool = True) -> dict:
     """quantize() of the whole weight, keeping the NF4 codes of the 64-wide
     blocks that contain columns `sel` (every row).  The constants and their
     double quantisation cover every block, exactly as quantize()'s.
@@ -382,48 +451,46 @@ def quantize_sampled_cols(w: np.ndarray, sel) -> dict:
     sel = np.asarray(sel, dtype=np.int64).reshape(-1)
     kb = cols // BLOCK
     c = block_absmax(w)
-    code8, s2, mu = double_quantize(c)
     bsel = np.unique(sel // BLOCK)
     wb = w.reshape(rows, kb, BLOCK)[:, bsel, :]
     cb = c.reshape(rows, kb)[:, bsel]
-    codes = nf4_encode(wb.reshape(-1, BLOCK), cb.reshape(-1))
-    return {
-        "rows": rows, "cols": cols, "sel": sel, "block_cols": bsel,
-        "codes": pack_nibbles(codes),
-        "absmax_code": code8,
-        "absmax_scale": s2,
-        "absmax_offset": np.array([mu], dtype=F32),
-    }
+    codes = nf4_encode(wb.reshape(-1, BLOCK), cb.reshape(-1), levels=levels_for(quant_type))
+    st = {"rows": rows, "cols": cols, "sel": sel, "block_cols": bsel,
+          "codes": pack_nibbles(codes)}
+    st.update(_constants_state(c, quant_type, double_quant))
+    return st
 
 
-def dequantize_sampled_cols_bits(state: dict) -> np.ndarray:
+def dequantize_sampled_cols_bits(state: dict, compute_dtype: str = "bf16") -> np.ndarray:
     """dequantize_bits() restricted to the columns of a quantize_sampled_cols()
     state: uint16 [rows, len(sel)]."""
     rows, cols, sel, bsel = state["rows"], state["cols"], state["sel"], state["block_cols"]
     kb = cols // BLOCK
-    cprime = block_constants_from_dq(state["absmax_code"], state["absmax_scale"],
-                                     state["absmax_offset"][0]).reshape(rows, kb)[:, bsel]
+    cprime = block_constants(state).reshape(rows, kb)[:, bsel]
     codes = unpack_nibbles(state["codes"]).reshape(-1, BLOCK)
-    bits = _decode_bits(codes, cprime.reshape(-1)).reshape(rows, bsel.size * BLOCK)
+    bits = _decode_bits(codes, cprime.reshape(-1), state.get("quant_type", "nf4"),
+                        compute_dtype).reshape(rows, bsel.size * BLOCK)
     pos = np.searchsorted(bsel, sel // BLOCK) * BLOCK + sel % BLOCK
     return bits[:, pos]
 
 
-def dequantize(state: dict) -> np.ndarray:
-    """Dequantised weight as float64 values of the bf16 results."""
-    return bf16_bits_to_f32(dequantize_bits(state)).astype(F64)
+def dequantize(state: dict, compute_dtype: str = "bf16") -> np.ndarray:
+    """Dequantised weight as float64 values of the 16-bit results."""
+    return bits16_to_f32(dequantize_bits(state, compute_dtype), compute_dtype).astype(F64)
 
 
-def storage_bits_per_param(rows: int, cols: int) -> float:
+def storage_bits_per_param(rows: int, cols: int, double_quant: bool = True) -> float:
     """Bytes of the packed state * 8 / number of weights.
 
     [PL] 二重量子化: 4 bits per code, 8 bits per 64 weights, 32 bits per
-    64*256 weights; plus one float32 mean per tensor (this build's reading).
+    64*256 weights; plus one float32 mean per tensor (the reading taken
+    here).  Without double quantisation: 4 bits per code and one float32
+    per 64 weights, the page's 4.5 bits.
     """
     n = rows * cols
     n_b = n // BLOCK
     n_g = (n_b + DQ_GROUP - 1) // DQ_GROUP
-    nbytes = n // 2 + n_b + 4 * n_g + 4
+    nbytes = n // 2 + (n_b + 4 * n_g + 4 if double_quant else 4 * n_b)
     return nbytes * 8.0 / n
 
 
@@ -431,7 +498,7 @@ def storage_bits_per_param(rows: int, cols: int) -> float:
 # Merge of the adapter into the dequantised base (deployment step)
 # --------------------------------------------------------------------------
 def merge_values_f32(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float,
-                     r: int) -> np.ndarray:
+                     r: int, compute_dtype: str = "bf16") -> np.ndarray:
     """float32 sum RN32(w_hat + RN32(s * RN32(B A))) before the final rounding.
 
     [WZ] 26.2 (inference: merge once, W_merged = W + (alpha/r) B A); [PL]
@@ -442,20 +509,22 @@ def merge_values_f32(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha
     s = RN32(alpha / r) multiplies in float32; the sum with the base is one
     float32 addition.
     """
-    base = bf16_bits_to_f32(w_hat_bits)
+    base = bits16_to_f32(w_hat_bits, compute_dtype)
     s = np.float32(np.float32(alpha) / np.float32(r))
     ba = (np.asarray(b, dtype=F64) @ np.asarray(a, dtype=F64)).astype(np.float32)
     return (base + (s * ba).astype(np.float32)).astype(np.float32)
 
 
 def merge_bits(w_hat_bits: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float,
-               r: int) -> np.ndarray:
-    """bf16 bit patterns of the merged weight: bf16_RNE of merge_values_f32.
+               r: int, compute_dtype: str = "bf16") -> np.ndarray:
+    """16-bit patterns of the merged weight: merge_values_f32 rounded to the
+    compute type (bf16 or fp16, nearest even).
 
     [PL] 落とし穴: merge on the 16-bit base and, if wanted, quantise the
     result again (that is quantize() of these values as float32).
     """
-    return bf16_bits_rne(merge_values_f32(w_hat_bits, a, b, alpha, r))
+    return round16_bits(merge_values_f32(w_hat_bits, a, b, alpha, r, compute_dtype),
+                        compute_dtype)
 
 
 # --------------------------------------------------------------------------
