@@ -97,23 +97,44 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (torch's CPU conversion, nearest even); uint16 bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def to_16_bits(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Round float32 to the 16-bit type "bf16" or "fp16"; uint16 bits."""
+    return to_f16_bits(x) if dtype == "fp16" else to_bf16_bits(x)
+
+
 def bf16_bits_value(bits: np.ndarray) -> np.ndarray:
     """float32 value of bf16 bit patterns (exact widening)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def bits16_value(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """float32 value of 16-bit patterns of type "bf16" or "fp16" (exact widening)."""
+    if dtype == "fp16":
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return bf16_bits_value(bits)
+
+
 def bf16_normal(shape, std: float, *, seed: int, workload: int, linear: int,
-                kind: int) -> np.ndarray:
-    """bf16 bit patterns of N(0, std^2) draws."""
+                kind: int, dtype: str = "bf16") -> np.ndarray:
+    """16-bit patterns (bf16 unless dtype is "fp16") of N(0, std^2) draws."""
     rng = rng_for(seed, workload, linear, kind)
     x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
     if std != 1.0:
         x *= np.float32(std)
-    return to_bf16_bits(x)
+    return to_16_bits(x, dtype)
 
 
-def linear_inputs(wl: Workload, li: int, *, seed: int = 0, tokens: int | None = None):
-    """All inputs of linear `li` of workload `wl` (numpy; bf16 as uint16 bits)."""
+def linear_inputs(wl: Workload, li: int, *, seed: int = 0, tokens: int | None = None,
+                  dtype: str = "bf16"):
+    """All inputs of linear `li` of workload `wl` (numpy; the 16-bit tensors as
+    uint16 bit patterns of `dtype`, "bf16" or "fp16")."""
     lin = wl.linears[li]
     t = wl.tokens if tokens is None else tokens
     n, k, r = lin.out_features, lin.in_features, wl.rank
@@ -122,11 +143,13 @@ def linear_inputs(wl: Workload, li: int, *, seed: int = 0, tokens: int | None = 
     }
     if r > 0:
         out["a"] = bf16_normal((r, k), float(np.sqrt(1.0 / r)), seed=seed, workload=wl.index,
-                               linear=li, kind=KIND_A)
-        out["b"] = bf16_normal((n, r), 0.01, seed=seed, workload=wl.index, linear=li, kind=KIND_B)
+                               linear=li, kind=KIND_A, dtype=dtype)
+        out["b"] = bf16_normal((n, r), 0.01, seed=seed, workload=wl.index, linear=li, kind=KIND_B,
+                               dtype=dtype)
     if t > 0:
-        out["x"] = bf16_normal((t, k), 1.0, seed=seed, workload=wl.index, linear=li, kind=KIND_X)
+        out["x"] = bf16_normal((t, k), 1.0, seed=seed, workload=wl.index, linear=li, kind=KIND_X,
+                               dtype=dtype)
         if wl.backward:
             out["dy"] = bf16_normal((t, n), 1.0, seed=seed, workload=wl.index, linear=li,
-                                    kind=KIND_DY)
+                                    kind=KIND_DY, dtype=dtype)
     return out
