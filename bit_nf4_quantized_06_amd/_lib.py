@@ -13,6 +13,8 @@ STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QL
 FORMAT_VERSION = 1
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
+QUANT_TYPES = {"nf4": 0, "int4": 1}          # QLORA_QUANT_*
+COMPUTE_DTYPES = {"bf16": 0, "fp16": 1}      # QLORA_COMPUTE_*
 
 
 class Nf4WeightDesc(ctypes.Structure):
@@ -21,7 +23,8 @@ class Nf4WeightDesc(ctypes.Structure):
         ("format_version", ctypes.c_int32),
         ("blocksize", ctypes.c_int32),
         ("dq_blocksize", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("quant_type", ctypes.c_int16),
+        ("compute_dtype", ctypes.c_int16),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
         ("codes", ctypes.c_void_p),
@@ -49,6 +52,11 @@ _DROP_P = ctypes.POINTER(DropoutDesc)
 
 SIGNATURES = {
     "qlora_nf4_weight_init": (ctypes.c_int, [_DESC_P, _I64, _I64]),
+    "qlora_nf4_weight_init_ex": (ctypes.c_int, [_DESC_P, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int]),
+    "qlora_nf4_weight_buffer_sizes": (ctypes.c_int, [_DESC_P, ctypes.POINTER(_SZ),
+                                                     ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
+                                                     ctypes.POINTER(_SZ)]),
     "qlora_nf4_buffer_sizes": (ctypes.c_int, [_I64, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
                                               ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "qlora_nf4_quantize_workspace": (_SZ, [_I64, _I64]),

@@ -37,38 +37,61 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) 
 
 @dataclass
 class NF4Weight:
-    """Packed NF4 weight: the four device buffers of qlora_nf4_weight."""
+    """Packed 4-bit weight: the four device buffers of qlora_nf4_weight and
+    its format (quant_type "nf4" or "int4", double_quant, compute_dtype
+    "bf16" or "fp16").  Without double quantisation absmax_scale holds the
+    float32 block constants and absmax_code, absmax_offset are empty."""
     rows: int
     cols: int
     codes: torch.Tensor          # uint8 [rows * cols / 2]
     absmax_code: torch.Tensor    # uint8 [n_b]     (E4M3 bit patterns)
-    absmax_scale: torch.Tensor   # float32 [n_g]
+    absmax_scale: torch.Tensor   # float32 [n_g]   ([n_b] without double quantisation)
     absmax_offset: torch.Tensor  # float32 [1]
+    quant_type: str = "nf4"
+    double_quant: bool = True
+    compute_dtype: str = "bf16"
 
     @staticmethod
-    def empty(rows: int, cols: int, device=None) -> "NF4Weight":
+    def _init(d, rows, cols, quant_type, double_quant, compute_dtype):
         lib = _lib.load()
+        _lib.check("qlora_nf4_weight_init_ex",
+                   lib.qlora_nf4_weight_init_ex(ctypes.byref(d), rows, cols,
+                                                _lib.QUANT_TYPES[quant_type], int(bool(double_quant)),
+                                                _lib.COMPUTE_DTYPES[compute_dtype]))
+
+    @staticmethod
+    def empty(rows: int, cols: int, device=None, quant_type: str = "nf4",
+              double_quant: bool = True, compute_dtype: str = "bf16") -> "NF4Weight":
+        lib = _lib.load()
+        d = _lib.Nf4WeightDesc()
+        NF4Weight._init(d, rows, cols, quant_type, double_quant, compute_dtype)
         sizes = [ctypes.c_size_t() for _ in range(4)]
-        _lib.check("qlora_nf4_buffer_sizes",
-                   lib.qlora_nf4_buffer_sizes(rows, cols, *[ctypes.byref(s) for s in sizes]))
+        _lib.check("qlora_nf4_weight_buffer_sizes",
+                   lib.qlora_nf4_weight_buffer_sizes(ctypes.byref(d),
+                                                     *[ctypes.byref(s) for s in sizes]))
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         return NF4Weight(
             rows, cols,
             torch.empty(sizes[0].value, dtype=torch.uint8, device=device),
             torch.empty(sizes[1].value, dtype=torch.uint8, device=device),
             torch.empty(sizes[2].value // 4, dtype=torch.float32, device=device),
-            torch.empty(1, dtype=torch.float32, device=device),
+            torch.empty(sizes[3].value // 4, dtype=torch.float32, device=device),
+            quant_type, bool(double_quant), compute_dtype,
         )
 
     @property
     def device(self):
         return self.codes.device
 
+    @property
+    def dtype16(self) -> torch.dtype:
+        """torch dtype of the 16-bit tensors that go with this weight."""
+        return torch.float16 if self.compute_dtype == "fp16" else torch.bfloat16
+
     def descriptor(self) -> _lib.Nf4WeightDesc:
-        lib = _lib.load()
         d = _lib.Nf4WeightDesc()
-        _lib.check("qlora_nf4_weight_init", lib.qlora_nf4_weight_init(ctypes.byref(d), self.rows,
-                                                                       self.cols))
+        NF4Weight._init(d, self.rows, self.cols, self.quant_type, self.double_quant,
+                        self.compute_dtype)
         d.codes = self.codes.data_ptr()
         d.absmax_code = self.absmax_code.data_ptr()
         d.absmax_scale = self.absmax_scale.data_ptr()
@@ -82,12 +105,16 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
 
 
 def qlora_nf4_quantize(W: torch.Tensor, out: NF4Weight | None = None,
-                       workspace: torch.Tensor | None = None, stream=None) -> NF4Weight:
-    """NF4 + double quantisation of a float32 [rows, cols] weight (qlora_nf4_quantize)."""
+                       workspace: torch.Tensor | None = None, stream=None,
+                       quant_type: str = "nf4", double_quant: bool = True,
+                       compute_dtype: str = "bf16") -> NF4Weight:
+    """Blockwise 4-bit quantisation of a float32 [rows, cols] weight
+    (qlora_nf4_quantize): NF4 + double quantisation by default; the format
+    arguments apply when `out` is not given (else out's format is used)."""
     lib = _lib.load()
     rows, cols = W.shape
     if out is None:
-        out = NF4Weight.empty(rows, cols, W.device)
+        out = NF4Weight.empty(rows, cols, W.device, quant_type, double_quant, compute_dtype)
     _need(W, "W", torch.float32, (rows, cols), out.device)
     ws_bytes = lib.qlora_nf4_quantize_workspace(rows, cols)
     if workspace is None:
@@ -100,11 +127,12 @@ def qlora_nf4_quantize(W: torch.Tensor, out: NF4Weight | None = None,
 
 
 def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """bf16 [rows, cols] dequantised weight (qlora_nf4_dequantize)."""
+    """[rows, cols] dequantised weight in the weight's compute dtype
+    (qlora_nf4_dequantize)."""
     lib = _lib.load()
     if out is None:
-        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device)
-    _need(out, "out", torch.bfloat16, (w.rows, w.cols), w.device)
+        out = torch.empty(w.rows, w.cols, dtype=w.dtype16, device=w.device)
+    _need(out, "out", w.dtype16, (w.rows, w.cols), w.device)
     desc = w.descriptor()
     _lib.check("qlora_nf4_dequantize",
                lib.qlora_nf4_dequantize(ctypes.byref(desc), out.data_ptr(), _stream(stream)))
@@ -113,15 +141,16 @@ def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=N
 
 def qlora_nf4_merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """bf16 [rows, cols] weight with the adapter folded in (qlora_nf4_merge):
-    bf16(dequant(W) + (alpha/r) B A)."""
+    """[rows, cols] weight with the adapter folded in (qlora_nf4_merge):
+    round16(dequant(W) + (alpha/r) B A) in the weight's compute dtype."""
     lib = _lib.load()
     r = A.shape[0]
-    _need(A, "A", torch.bfloat16, (r, w.cols), w.device)
-    _need(B, "B", torch.bfloat16, (w.rows, r), w.device)
+    dt = w.dtype16
+    _need(A, "A", dt, (r, w.cols), w.device)
+    _need(B, "B", dt, (w.rows, r), w.device)
     if out is None:
-        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device)
-    _need(out, "out", torch.bfloat16, (w.rows, w.cols), w.device)
+        out = torch.empty(w.rows, w.cols, dtype=dt, device=w.device)
+    _need(out, "out", dt, (w.rows, w.cols), w.device)
     desc = w.descriptor()
     _lib.check("qlora_nf4_merge",
                lib.qlora_nf4_merge(ctypes.byref(desc), A.data_ptr(), B.data_ptr(), int(r),
@@ -168,16 +197,16 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     T, K = X.shape
     r = A.shape[0]
     dev = w.device
-    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
-    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
-    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    _need(A, "A", w.dtype16, (r, w.cols), dev)
+    _need(B, "B", w.dtype16, (w.rows, r), dev)
     if Y is None:
-        Y = torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
-    _need(Y, "Y", torch.bfloat16, (T, w.rows), dev)
+        Y = torch.empty(T, w.rows, dtype=w.dtype16, device=dev)
+    _need(Y, "Y", w.dtype16, (T, w.rows), dev)
     if U_save is None and save_u:
-        U_save = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+        U_save = torch.empty(T, r, dtype=w.dtype16, device=dev)
     if U_save is not None:
-        _need(U_save, "U_save", torch.bfloat16, (T, r), dev)
+        _need(U_save, "U_save", w.dtype16, (T, r), dev)
     ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 0)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -199,19 +228,19 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     T = X.shape[0]
     r = A.shape[0]
     dev = w.device
-    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
-    _need(dY, "dY", torch.bfloat16, (T, w.rows), dev)
-    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
-    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    _need(dY, "dY", w.dtype16, (T, w.rows), dev)
+    _need(A, "A", w.dtype16, (r, w.cols), dev)
+    _need(B, "B", w.dtype16, (w.rows, r), dev)
     if U_saved is not None:
-        _need(U_saved, "U_saved", torch.bfloat16, (T, r), dev)
+        _need(U_saved, "U_saved", w.dtype16, (T, r), dev)
     if dX is None:
-        dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(T, w.cols, dtype=w.dtype16, device=dev)
     if dA is None:
         dA = torch.empty(r, w.cols, dtype=torch.float32, device=dev)
     if dB is None:
         dB = torch.empty(w.rows, r, dtype=torch.float32, device=dev)
-    _need(dX, "dX", torch.bfloat16, (T, w.cols), dev)
+    _need(dX, "dX", w.dtype16, (T, w.cols), dev)
     _need(dA, "dA", torch.float32, (r, w.cols), dev)
     _need(dB, "dB", torch.float32, (w.rows, r), dev)
     ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 1)
@@ -252,10 +281,11 @@ def qlora_dropout_mask(T: int, cols: int, p: float, seed: int, offset: int,
         keep = torch.empty(quads, cols // 2, dtype=torch.uint8, device=dev)
     _need(keep, "keep", torch.uint8, (quads, cols // 2), dev)
     if X is not None:
-        _need(X, "X", torch.bfloat16, (T, cols), dev)
+        # the mask only moves 16-bit patterns: bf16 or fp16
+        _need(X, "X", X.dtype if X.dtype == torch.float16 else torch.bfloat16, (T, cols), dev)
         if X_dropped is None:
             X_dropped = torch.empty_like(X)
-        _need(X_dropped, "X_dropped", torch.bfloat16, (T, cols), dev)
+        _need(X_dropped, "X_dropped", X.dtype, (T, cols), dev)
     d = _dropout_desc(p, seed, offset)
     _lib.check("qlora_dropout_mask",
                lib.qlora_dropout_mask(ctypes.byref(d), T, cols, _ptr(X), _ptr(X_dropped),
@@ -281,16 +311,16 @@ def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: 
     T = X.shape[0]
     r = A.shape[0]
     dev = w.device
-    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
-    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
-    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    _need(A, "A", w.dtype16, (r, w.cols), dev)
+    _need(B, "B", w.dtype16, (w.rows, r), dev)
     if Y is None:
-        Y = torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
-    _need(Y, "Y", torch.bfloat16, (T, w.rows), dev)
+        Y = torch.empty(T, w.rows, dtype=w.dtype16, device=dev)
+    _need(Y, "Y", w.dtype16, (T, w.rows), dev)
     if U_save is None and save_u:
-        U_save = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+        U_save = torch.empty(T, r, dtype=w.dtype16, device=dev)
     if U_save is not None:
-        _need(U_save, "U_save", torch.bfloat16, (T, r), dev)
+        _need(U_save, "U_save", w.dtype16, (T, r), dev)
     quads = (T + 3) // 4
     if keep_save is None and save_keep:
         keep_save = torch.empty(quads, w.cols // 2, dtype=torch.uint8, device=dev)
@@ -324,21 +354,21 @@ def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A:
     T = X.shape[0]
     r = A.shape[0]
     dev = w.device
-    _need(X, "X", torch.bfloat16, (T, w.cols), dev)
-    _need(dY, "dY", torch.bfloat16, (T, w.rows), dev)
-    _need(A, "A", torch.bfloat16, (r, w.cols), dev)
-    _need(B, "B", torch.bfloat16, (w.rows, r), dev)
+    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    _need(dY, "dY", w.dtype16, (T, w.rows), dev)
+    _need(A, "A", w.dtype16, (r, w.cols), dev)
+    _need(B, "B", w.dtype16, (w.rows, r), dev)
     if U_saved is not None:
-        _need(U_saved, "U_saved", torch.bfloat16, (T, r), dev)
+        _need(U_saved, "U_saved", w.dtype16, (T, r), dev)
     if keep_saved is not None:
         _need(keep_saved, "keep_saved", torch.uint8, ((T + 3) // 4, w.cols // 2), dev)
     if dX is None:
-        dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(T, w.cols, dtype=w.dtype16, device=dev)
     if dA is None:
         dA = torch.empty(r, w.cols, dtype=torch.float32, device=dev)
     if dB is None:
         dB = torch.empty(w.rows, r, dtype=torch.float32, device=dev)
-    _need(dX, "dX", torch.bfloat16, (T, w.cols), dev)
+    _need(dX, "dX", w.dtype16, (T, w.cols), dev)
     _need(dA, "dA", torch.float32, (r, w.cols), dev)
     _need(dB, "dB", torch.float32, (w.rows, r), dev)
     ws_bytes = lib.qlora_linear_workspace_dropout(T, w.rows, w.cols, r, 1)

@@ -79,12 +79,13 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
                                hipStream_t st) {
   uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * U)
   float* P = ws_ptr<float>(ws, L.proj_off);
-  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, st);
+  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs none;
     none.n = 0;
     e = launch_lora_proj_reduce(
-        ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0}, none, st);
+        ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0, d.f16}, none,
+        st);
   }
   if (e == hipSuccess) {
     GemmArgs g;
@@ -101,6 +102,8 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
     g.out = Y;
     g.T = T;
     g.keep = nullptr;
+    g.dq = d.dq;
+    g.f16 = d.f16;
     e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
   }
   return e;
@@ -124,23 +127,23 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
   // G = dY B (B read in place as [rows, r]); its reduction writes the dX
   // seed's left operand and dA's, and the same launch transposes A for the
   // dX seed
-  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, st);
+  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs tj;
     tj.n = 1;
     tj.job[0] = TransposeJob{A, r, d.cols, At, r};
     e = launch_lora_proj_reduce(
-        ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0}, tj, st);
+        ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0, d.f16}, tj, st);
   }
   // U for dB when the forward's U was not kept: recompute inv Xa A^T
   const uint16_t* U = U_saved;
   if (e == hipSuccess && !U_saved) {
-    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, st);
+    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
     if (e == hipSuccess) {
       TransposeJobs none;
       none.n = 0;
       e = launch_lora_proj_reduce(
-          ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, inv, nullptr, 0}, none, st);
+          ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, inv, nullptr, 0, d.f16}, none, st);
     }
     U = Un;
   }
@@ -159,6 +162,8 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
     g.out = dX;
     g.T = T;
     g.keep = keep;
+    g.dq = d.dq;
+    g.f16 = d.f16;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
   // dA = s Gn^T Xa and dB = s dY^T U: partials of both in one launch, then
@@ -168,7 +173,7 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
     gj.n = 2;
     gj.job[0] = GradJob{Gn, Xa, d.cols, ws_ptr<float>(ws, L.grad_off), dA, 0};
     gj.job[1] = GradJob{U, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
-    e = launch_lora_grad_partial(gj, T, r, L.s_grad, st);
+    e = launch_lora_grad_partial(gj, T, r, L.s_grad, d.f16, st);
     if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
   }
   return e;
@@ -210,17 +215,19 @@ qlora_status qlora_nf4_quantize(const float* W, const qlora_nf4_weight* out, voi
   WeightDims d;
   qlora_status s = check_descriptor(out, &d);
   if (s != QLORA_OK) return s;
-  if (!W || !ws) return QLORA_ERR_NULL;
-  if (!aligned16(W) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  // without double quantisation the constants go straight to absmax_scale:
+  // no workspace
+  if (!W || (d.dq && !ws)) return QLORA_ERR_NULL;
+  if (!aligned16(W) || (ws && !aligned16(ws))) return QLORA_ERR_ALIGN;
   const QuantWs L = quant_ws_layout(d);
-  if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if (d.dq && ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = timed(QLORA_TIMING_QUANTIZE, st, [&] {
     return launch_quantize(W, d.n_b, out->codes, out->absmax_code, out->absmax_scale,
-                           out->absmax_offset, ws_ptr<float>(ws, L.cblk_off),
-                           ws_ptr<double>(ws, L.gpart_off), st);
+                           out->absmax_offset, d.dq ? ws_ptr<float>(ws, L.cblk_off) : nullptr,
+                           d.dq ? ws_ptr<double>(ws, L.gpart_off) : nullptr, d.qt, d.dq, st);
   });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -237,7 +244,7 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16, v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = timed(QLORA_TIMING_DEQUANT, st, [&] {
     return launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n,
-                             W_bf16, st);
+                             W_bf16, d.qt, d.dq, d.f16, st);
   });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -266,6 +273,9 @@ qlora_status qlora_nf4_merge(const qlora_nf4_weight* w, const uint16_t* A, const
   m.r = r;
   m.scale = alpha / (float)r;
   m.out = W_merged;
+  m.qt = d.qt;
+  m.dq = d.dq;
+  m.f16 = d.f16;
   const hipError_t e = timed(QLORA_TIMING_MERGE, st, [&] { return launch_merge(m, st); });
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -343,6 +353,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
     ga.P = ws_ptr<float>(ws, L.gemv_off);
     ga.PU = ws_ptr<float>(ws, L.gemv_u_off);
     ga.splits = L.s_gemv;
+    ga.dq = d.dq;
+    ga.f16 = d.f16;
     const hipError_t e =
         timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_gemv(ga, st); });
     return e == hipSuccess ? QLORA_OK : hip_fail(e);

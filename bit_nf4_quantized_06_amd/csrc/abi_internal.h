@@ -18,6 +18,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WeightDims {
   int64_t rows, cols, n, n_b, n_g;
+  int qt;      // codebook: QLORA_QUANT_NF4 / QLORA_QUANT_INT4
+  bool dq;     // double-quantised constants (else float32 constants)
+  bool f16;    // compute dtype fp16 (else bf16)
 };
 
 // Shape rules of a packed weight: rows >= 1, rows % 16 == 0, cols >= 64,

@@ -8,6 +8,8 @@ namespace qlora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -38,11 +40,53 @@ __device__ constexpr float kNF4Thr[15] = {
     0x1.ec90c4p-4f,  0x1.a0cfbcp-3f,  0x1.2b05a6p-2f,  0x1.8ea7eep-2f,
     0x1.00da04p-1f,  0x1.491b5ap-1f,  0x1.b913b0p-1f};
 
+// The evenly spaced 4-bit comparison codebook, -1 + 2i/15 rounded once to
+// float32 (Ultralytics glossary "QLoRA", code example: 16 evenly spaced
+// levels from -1 to 1, no exact 0), and its decision thresholds (largest
+// float32 not above the exact midpoint of neighbouring levels; the middle
+// one is exactly 0, so a zero quotient takes the lower level 7).
+__device__ constexpr float kINT4[16] = {
+    -0x1.000000p+0f, -0x1.bbbbbcp-1f, -0x1.777778p-1f, -0x1.333334p-1f,
+    -0x1.dddddep-2f, -0x1.555556p-2f, -0x1.99999ap-3f, -0x1.111112p-4f,
+    0x1.111112p-4f,  0x1.99999ap-3f,  0x1.555556p-2f,  0x1.dddddep-2f,
+    0x1.333334p-1f,  0x1.777778p-1f,  0x1.bbbbbcp-1f,  0x1.000000p+0f};
+__device__ constexpr float kINT4Thr[15] = {
+    -0x1.dddddep-1f, -0x1.99999ap-1f, -0x1.555556p-1f, -0x1.111112p-1f,
+    -0x1.99999ap-2f, -0x1.111112p-2f, -0x1.111112p-3f, 0.0f,
+    0x1.111110p-3f,  0x1.111110p-2f,  0x1.99999ap-2f,  0x1.111110p-1f,
+    0x1.555556p-1f,  0x1.99999ap-1f,  0x1.dddddep-1f};
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v;
   v.x = (__bf16)lo;   // v_cvt_pk_bf16_f32: round to nearest even
   v.y = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// two float32 to binary16, round to nearest even (subnormals kept).  The
+// empty asm makes both inputs opaque: otherwise the compiler fuses the
+// multiply or add that produced them into a mixed-precision FMA (v_fma_mix),
+// which rounds the exact result once to binary16 -- different from rounding
+// to float32 first wherever the float32 value is a binary16 tie.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  asm("" : "+v"(lo), "+v"(hi));
+  f16x2_t v;
+  v.x = (_Float16)lo;
+  v.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// the 16-bit compute type of a kernel instance: bfloat16 or binary16
+template <bool kF16>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+  return kF16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
+// float32 value of the 16-bit pattern in the low half of v
+template <bool kF16>
+__device__ __forceinline__ float lo16_to_f32(uint32_t v) {
+  if (kF16) return (float)__builtin_bit_cast(f16x2_t, v).x;
+  return __uint_as_float(v << 16);
 }
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
@@ -77,6 +121,15 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float x) {
   return sign | mag;
 }
 
+// Block constant of a weight: with double quantisation decoded from the
+// 8-bit code, the group scale and the mean (below); without it the float32
+// constant itself, which kernels load into the group-scale slot (byte offset
+// 4 blk instead of 4 (blk / 256)).
+template <bool kDQ>
+__device__ __forceinline__ uint32_t scale_offset(int64_t blk) {
+  return kDQ ? (uint32_t)((blk >> 8) * 4) : (uint32_t)(blk * 4);
+}
+
 // Decoded block constant c' = RN32(RN32(e4m3(code8) * 2^-8 * s2) + mu), no FMA.
 __device__ __forceinline__ float block_constant(uint32_t code8, float s2, float mu) {
   return __fadd_rn(__fmul_rn(e4m3_decode_scaled(code8), s2), mu);
@@ -90,6 +143,13 @@ __device__ __forceinline__ float block_constant_or_zero(bool ok, uint32_t code8,
   return __uint_as_float(__float_as_uint(v) & (ok ? 0xFFFFFFFFu : 0u));
 }
 
+template <bool kDQ>
+__device__ __forceinline__ float weight_constant_or_zero(bool ok, uint32_t code8, float s2_or_c,
+                                                         float mu) {
+  if (kDQ) return block_constant_or_zero(ok, code8, s2_or_c, mu);
+  return __uint_as_float(__float_as_uint(s2_or_c) & (ok ? 0xFFFFFFFFu : 0u));
+}
+
 // 16-entry bf16 lookup table of one block, q[k] * c' rounded once to bf16,
 // split into byte planes for v_perm lookups:
 //   lo[i] byte j = low byte of entry 4i+j, hi[i] byte j = high byte.
@@ -98,11 +158,12 @@ struct Nf4Lut {
   uint32_t hi[4];
 };
 
+template <bool kF16>
 __device__ __forceinline__ Nf4Lut make_lut(float cprime) {
   uint32_t p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    p[j] = pack_bf16x2(__fmul_rn(kNF4[2 * j], cprime), __fmul_rn(kNF4[2 * j + 1], cprime));
+    p[j] = pack16x2<kF16>(__fmul_rn(kNF4[2 * j], cprime), __fmul_rn(kNF4[2 * j + 1], cprime));
   Nf4Lut t;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -141,9 +202,27 @@ __device__ __forceinline__ void dequant8(const Nf4Lut& t, uint32_t w, uint32_t o
   out[3] = perm(hb, lb, 0x07030602u);
 }
 
+template <bool kF16 = false>
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+typedef float f32x16v_t __attribute__((ext_vector_type(16)));
+
+template <bool kF16 = false>
+__device__ __forceinline__ f32x16v_t mfma32x32(const u32x4_t& a, const u32x4_t& b,
+                                               const f32x16v_t& c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 }  // namespace qlora

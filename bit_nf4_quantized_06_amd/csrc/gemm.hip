@@ -80,9 +80,9 @@ __device__ __forceinline__ u32x4_t ld_lds16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+template <bool kF16>
 __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  return mfma32x32<kF16>(a, b, c);
 }
 
 // two ds_read_b64_tr_b16 -> one 8 x bf16 MFMA operand
@@ -188,7 +188,11 @@ __device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stag
 }
 
 // packed codes and block-constant inputs of this lane's half block at `step`
-template <bool kBwd>
+// kDQ false: the group-scale slot receives the block's float32 constant and
+// the 8-bit code load stays as an out-of-range dummy (it reads 0), so every
+// step issues the same number of memory operations and the explicit wait
+// counts hold for both formats.
+template <bool kBwd, bool kDQ>
 __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, CodeRegs& r) {
   // forward: the block moves along the row (+32 B, +1 block per step);
   // backward: it moves down 64 rows (+64 rows of codes and constants)
@@ -202,10 +206,10 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
   r.c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                         make_rsrc(c.g.codes, c.codes_bytes), c.code_voff, scode, 0));
   r.code8 = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(c.g.code8, c.code8_bytes),
-                                                r.ok ? (uint32_t)blk : kOOB, 0, 0);
+                                                (kDQ && r.ok) ? (uint32_t)blk : kOOB, 0, 0);
   r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        make_rsrc(c.g.s2, c.s2_bytes),
-                                       r.ok ? (uint32_t)((blk >> 8) * 4) : kOOB, 0, 0));
+                                       r.ok ? scale_offset<kDQ>(blk) : kOOB, 0, 0));
 }
 
 // Table of this lane pair's block.  Forward: lane half h = lane & 1 forms
@@ -213,14 +217,15 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
 // supplies the other 8 (DPP quad_perm [1,0,3,2]); lanes with h = 1 hold the
 // two halves swapped and flip bit 3 of their codes instead (code_flip).
 // Backward: the whole table per lane.
-template <bool kBwd>
+template <bool kBwd, bool kDQ, bool kF16>
 __device__ __forceinline__ Nf4Lut lut_of(const GemmCtx<kBwd>& c, const CodeRegs& r) {
-  const float cp = block_constant_or_zero(r.ok, r.code8, r.s2, c.mu);   // 0: rows past the end
-  if (kBwd) return make_lut(cp);
+  // 0: rows past the end
+  const float cp = weight_constant_or_zero<kDQ>(r.ok, r.code8, r.s2, c.mu);
+  if (kBwd) return make_lut<kF16>(cp);
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    p[j] = pack_bf16x2(__fmul_rn(c.kq[2 * j], cp), __fmul_rn(c.kq[2 * j + 1], cp));
+    p[j] = pack16x2<kF16>(__fmul_rn(c.kq[2 * j], cp), __fmul_rn(c.kq[2 * j + 1], cp));
   uint32_t own[4], nb[4];
   own[0] = perm(p[1], p[0], 0x06040200u);   // low bytes of own entries 0..3
   own[1] = perm(p[3], p[2], 0x06040200u);   // low bytes of own entries 4..7
@@ -286,7 +291,7 @@ __device__ __forceinline__ void slice_schedule() {
 // exit fa[0], fb[0] hold slice 0 of step+1 and `nxt` the codes of step+2
 // (the caller swaps the two register sets for the next step: no copy, so
 // nothing waits for the codes before they are used a step later).
-template <bool kBwd, int SA, int SB>
+template <bool kBwd, bool kDQ, bool kF16, int SA, int SB>
 __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][2],
                                           u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][2],
                                           CodeRegs& cur, CodeRegs& nxt) {
@@ -299,8 +304,8 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 
   // slice 0: loads for step+2, the block table for step+1
   issue_act(c, c.A[(SA + 2) % kAStages], step + 2);
-  issue_codes(c, step + 2, nxt);
-  const Nf4Lut lut = lut_of(c, cur);
+  issue_codes<kBwd, kDQ>(c, step + 2, nxt);
+  const Nf4Lut lut = lut_of<kBwd, kDQ, kF16>(c, cur);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const int f = s & 1;
@@ -308,7 +313,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[f][i], fb[f][j], acc[i][j]);
     store_w(c, bs_next, lut, cur, s);
     if (s == 0)
       slice_schedule<8, kReads, kVmemPerStep>();
@@ -321,7 +326,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[1][i], fb[1][j], acc[i][j]);
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[1][i], fb[1][j], acc[i][j]);
   store_w(c, bs_next, lut, cur, 3);
 #pragma unroll
   for (int q = 0; q < 6; ++q) {
@@ -334,7 +339,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
   u32x4_t ga[4], gb[2];
   load_frags(c, as_next, bs_next, 0, ga, gb);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) acc[3][j] = mfma32(fa[1][3], fb[1][j], acc[3][j]);
+  for (int j = 0; j < 2; ++j) acc[3][j] = mfma32<kF16>(fa[1][3], fb[1][j], acc[3][j]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = ga[i];
 #pragma unroll
@@ -343,12 +348,15 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 }
 
 // kDrop (backward only): the seed is multiplied element-wise by the
-// lora_dropout keep mask (g.keep) before the main loop.
-template <bool kBwd, bool kDrop>
+// lora_dropout keep mask (g.keep) before the main loop.  kDQ: double-
+// quantised block constants (else float32 constants); kF16: fp16 operands,
+// tables and output (else bf16).
+template <bool kBwd, bool kDrop, bool kDQ, bool kF16>
 __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // The body is compiled in the device pass only: the host pass needs just
   // the kernel's signature, and it cannot instantiate the gfx950
-  // buffer-resource helpers for a second kernel of the same direction.
+  // buffer-resource helpers for more than one kernel with the same helper
+  // arguments.
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) uint16_t sa0[kStageElems];
   __shared__ __attribute__((aligned(1024))) uint16_t sa1[kStageElems];
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   c.n0 = (int64_t)tn * BN;
   c.nsteps = (int)((c.red_len + BK - 1) / BK);
   c.kblocks = g.cols >> 6;
-  c.mu = g.mu[0];
+  c.mu = kDQ ? g.mu[0] : 0.0f;
   const int64_t rows_here = (g.T - c.m0) < BM ? (g.T - c.m0) : BM;
   const int col0 = 128 * c.wn + 64 * c.wg;   // first output column of this wave in the tile
   {
@@ -441,7 +449,8 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   c.act_bytes = (uint32_t)(rows_here * c.red_len * 2);
   c.codes_bytes = (uint32_t)((g.rows * g.cols) >> 1);
   c.code8_bytes = (uint32_t)(g.rows * c.kblocks);
-  c.s2_bytes = (uint32_t)(((g.rows * c.kblocks + 255) >> 8) * 4);
+  c.s2_bytes = kDQ ? (uint32_t)(((g.rows * c.kblocks + 255) >> 8) * 4)
+                  : (uint32_t)(g.rows * c.kblocks * 4);
   const int l32 = c.l32, lhi = c.lhi, wm = c.wm;
   const int64_t m0 = c.m0, n0 = c.n0;
 
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(af[i], bf[j], acc[i][j]);
   }
   if constexpr (kDrop) {
     // the keep mask has one nibble per 4 tokens x 1 feature, exactly the 4
@@ -516,11 +525,11 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // ---- prologue ------------------------------------------------------------
   CodeRegs ca, cb;   // codes of even / odd steps
   issue_act(c, sa0, 0);
-  issue_codes(c, 0, ca);
+  issue_codes<kBwd, kDQ>(c, 0, ca);
   issue_act(c, sa1, 1);
-  issue_codes(c, 1, cb);
+  issue_codes<kBwd, kDQ>(c, 1, cb);
   {
-    const Nf4Lut lut = lut_of(c, ca);
+    const Nf4Lut lut = lut_of<kBwd, kDQ, kF16>(c, ca);
 #pragma unroll
     for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, ca, w);
   }
@@ -534,18 +543,18 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // the last nsteps % 6 steps
   int step = 0;
   for (; step + 6 <= c.nsteps; step += 6) {
-    gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
-    gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
-    gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, 2, 1>(c, step + 5, acc, fa, fb, ca, cb);
+    gemm_step<kBwd, kDQ, kF16, 0, 0>(c, step, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, kDQ, kF16, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+    gemm_step<kBwd, kDQ, kF16, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, kDQ, kF16, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+    gemm_step<kBwd, kDQ, kF16, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
+    gemm_step<kBwd, kDQ, kF16, 2, 1>(c, step + 5, acc, fa, fb, ca, cb);
   }
-  if (step < c.nsteps) gemm_step<kBwd, 0, 0>(c, step, acc, fa, fb, cb, ca);
-  if (step + 1 < c.nsteps) gemm_step<kBwd, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
-  if (step + 2 < c.nsteps) gemm_step<kBwd, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
-  if (step + 3 < c.nsteps) gemm_step<kBwd, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
-  if (step + 4 < c.nsteps) gemm_step<kBwd, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
+  if (step < c.nsteps) gemm_step<kBwd, kDQ, kF16, 0, 0>(c, step, acc, fa, fb, cb, ca);
+  if (step + 1 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+  if (step + 2 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+  if (step + 3 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+  if (step + 4 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
 
   // ---- epilogue: round to bf16 and store ------------------------------------
 #pragma unroll
@@ -558,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
         for (int e = 0; e < 16; ++e) {
           const int64_t row = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lhi + (e & 3);
           if (row < g.T)
-            g.out[row * out_len + col] = (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
+            g.out[row * out_len + col] = (uint16_t)(pack16x2<kF16>(acc[i][j][e], 0.0f) & 0xFFFFu);
         }
       }
     }
@@ -570,19 +579,32 @@ static unsigned num_tiles(int64_t T, int64_t out_len) {
   return (unsigned)(((T + BM - 1) / BM) * ((out_len + BN - 1) / BN));
 }
 
+template <bool kBwd, bool kDrop>
+static void launch_fmt(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.dq && !a.f16)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, false>), grid, dim3(kThreads), 0,
+                       stream, a);
+  else if (a.dq)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, true>), grid, dim3(kThreads), 0,
+                       stream, a);
+  else if (!a.f16)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, false>), grid, dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, true>), grid, dim3(kThreads), 0,
+                       stream, a);
+}
+
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qlora_gemm_kernel<false, false>), dim3(num_tiles(a.T, a.rows)),
-                     dim3(kThreads), 0, stream, a);
+  launch_fmt<false, false>(a, dim3(num_tiles(a.T, a.rows)), stream);
   return hipGetLastError();
 }
 
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.keep)
-    hipLaunchKernelGGL((qlora_gemm_kernel<true, true>), dim3(num_tiles(a.T, a.cols)),
-                       dim3(kThreads), 0, stream, a);
+    launch_fmt<true, true>(a, dim3(num_tiles(a.T, a.cols)), stream);
   else
-    hipLaunchKernelGGL((qlora_gemm_kernel<true, false>), dim3(num_tiles(a.T, a.cols)),
-                       dim3(kThreads), 0, stream, a);
+    launch_fmt<true, false>(a, dim3(num_tiles(a.T, a.cols)), stream);
   return hipGetLastError();
 }
 

@@ -53,10 +53,10 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+template <bool kF16>
 __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b,
                                            const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  return mfma32x32<kF16>(a, b, c);
 }
 
 // 8 codes of one word (element i in bits 4i..4i+3) to bf16, slot order
@@ -86,11 +86,12 @@ __device__ __forceinline__ u32x4_t act_eo(const u32x4_t& d) {
 // Table of one row's block, lanes l and l + 32 holding the same c': lane half
 // h forms entries 8h .. 8h+7 (kq = the levels 8h .. 8h+7) as byte planes and
 // the halves are exchanged.
+template <bool kF16>
 __device__ __forceinline__ Nf4Lut make_lut_pair(float cp, const float kq[8]) {
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    p[j] = pack_bf16x2(__fmul_rn(kq[2 * j], cp), __fmul_rn(kq[2 * j + 1], cp));
+    p[j] = pack16x2<kF16>(__fmul_rn(kq[2 * j], cp), __fmul_rn(kq[2 * j + 1], cp));
   const uint32_t lo_a = perm(p[1], p[0], 0x06040200u);
   const uint32_t lo_b = perm(p[3], p[2], 0x06040200u);
   const uint32_t hi_a = perm(p[1], p[0], 0x07050301u);
@@ -123,7 +124,7 @@ struct GemvStage {
 
 // acc[tg][ng] += X[tokens of tg][k] * Wrow[ng][k] over the blocks st0 + wave,
 // st0 + wave + 4, ... below st1.
-template <int TG, bool kLora>
+template <int TG, bool kLora, bool kDQ, bool kF16>
 __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t st0,
                                           int64_t st1, int wave, int lane,
                                           f32x16_t (&acc)[TG][2]) {
@@ -135,9 +136,13 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
   const __amdgpu_buffer_rsrc_t wr =
       kLora ? rsrc_v(g.A, (uint64_t)g.r * K * 2) : rsrc_v(g.codes, (uint64_t)(g.rows * K) >> 1);
   const __amdgpu_buffer_rsrc_t c8r = rsrc_v(g.code8, (uint64_t)(g.rows * kblocks));
+  // without double quantisation the group-scale slot holds each block's
+  // float32 constant; the 8-bit code load then reads nothing (offset out of
+  // range) so both formats issue the same loads
   const __amdgpu_buffer_rsrc_t s2r =
-      rsrc_v(g.s2, (uint64_t)((g.rows * kblocks + 255) >> 8) * 4);
-  const float mu = kLora ? 0.0f : g.mu[0];
+      rsrc_v(g.s2, kDQ ? (uint64_t)((g.rows * kblocks + 255) >> 8) * 4
+                       : (uint64_t)(g.rows * kblocks) * 4);
+  const float mu = (kLora || !kDQ) ? 0.0f : g.mu[0];
 
   bool row_ok[2];
   int64_t row[2];
@@ -169,10 +174,11 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
       } else {
         const int64_t blk = row[ng] * kblocks + st;
         s.w[ng][0] = load16(wr, v ? (uint32_t)(blk * 32 + 16 * half) : kOOBv);
-        s.c8[ng] = __builtin_amdgcn_raw_buffer_load_b8(c8r, v ? (uint32_t)blk : kOOBv, 0, 0);
+        s.c8[ng] = __builtin_amdgcn_raw_buffer_load_b8(c8r, (kDQ && v) ? (uint32_t)blk : kOOBv,
+                                                       0, 0);
         s.s2[ng] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
-                       s2r, v ? (uint32_t)((blk >> 8) * 4) : kOOBv, 0, 0));
+                       s2r, v ? scale_offset<kDQ>(blk) : kOOBv, 0, 0));
       }
     }
 #pragma unroll
@@ -200,16 +206,16 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
         for (int q = 0; q < 4; ++q) {
           const u32x4_t b = act_eo(cur.w[ng][kLora ? q : 0]);
 #pragma unroll
-          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
+          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32<kF16>(a[tg][q], b, acc[tg][ng]);
         }
       } else {
-        const float cp = block_constant_or_zero(row_ok[ng], cur.c8[ng], cur.s2[ng], mu);
-        const Nf4Lut lt = make_lut_pair(cp, kq);
+        const float cp = weight_constant_or_zero<kDQ>(row_ok[ng], cur.c8[ng], cur.s2[ng], mu);
+        const Nf4Lut lt = make_lut_pair<kF16>(cp, kq);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4_t b = dequant8_eo(lt, cur.w[ng][0][q]);
 #pragma unroll
-          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32(a[tg][q], b, acc[tg][ng]);
+          for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32<kF16>(a[tg][q], b, acc[tg][ng]);
         }
       }
     }
@@ -220,9 +226,11 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
 }  // namespace
 
 // Grid: (w_tiles + LoRA tiles, splits); TG = token groups of 32.
-template <int TG>
+template <int TG, bool kDQ, bool kF16>
 __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemvArgs g, int w_tiles,
                                                                  int steps_per) {
+  // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) float red[3 * TG * 2 * 16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -243,9 +251,9 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemvArgs g, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[tg][ng][e] = 0.0f;
   if (lora)
-    gemv_tile<TG, true>(g, n0, st0, st1, wave, lane, acc);
+    gemv_tile<TG, true, kDQ, kF16>(g, n0, st0, st1, wave, lane, acc);
   else
-    gemv_tile<TG, false>(g, n0, st0, st1, wave, lane, acc);
+    gemv_tile<TG, false, kDQ, kF16>(g, n0, st0, st1, wave, lane, acc);
 
   // ---- fixed-order sum of the four waves' tiles, one split partial -------
   if (wave > 0) {
@@ -277,11 +285,14 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemvArgs g, int
         }
       }
   }
+#endif
 }
 
 // Grid: ceil(rows / 128); wave w owns rows 128 blockIdx.x + 32 w .. + 31.
-template <int TG>
+template <int TG, bool kF16>
 __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
+  // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint16_t us[64 * 128];   // bf16(s U) [t][p]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -320,9 +331,9 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int64_t e = e0 + tid + 256 * j;
       if (e < TR) {
-        us[e] = (uint16_t)(pack_bf16x2(u[j] * g.scale, 0.0f) & 0xFFFFu);
+        us[e] = (uint16_t)(pack16x2<kF16>(u[j] * g.scale, 0.0f) & 0xFFFFu);
         if (blockIdx.x == 0 && g.U_save)
-          g.U_save[e] = (uint16_t)(pack_bf16x2(u[j], 0.0f) & 0xFFFFu);
+          g.U_save[e] = (uint16_t)(pack16x2<kF16>(u[j], 0.0f) & 0xFFFFu);
       }
     }
   }
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
       // rows that are never stored
       const int t = 32 * tg + (lane & 31);
       const u32x4_t a = *reinterpret_cast<const u32x4_t*>(us + t * r + p);
-      acc[tg] = mfma32(a, b, acc[tg]);
+      acc[tg] = mfma32<kF16>(a, b, acc[tg]);
     }
   }
   if (n >= N) return;
@@ -379,9 +390,21 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
-      if (t < T) g.Y[t * N + n] = (uint16_t)(pack_bf16x2(v[e] + acc[tg][e], 0.0f) & 0xFFFFu);
+      if (t < T) g.Y[t * N + n] = (uint16_t)(pack16x2<kF16>(v[e] + acc[tg][e], 0.0f) & 0xFFFFu);
     }
   }
+#endif
+}
+
+template <int TG, bool kDQ, bool kF16>
+static hipError_t gemv_launch(const GemvArgs& a, dim3 grid, dim3 fgrid, int w_tiles, int per,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL((qlora_gemv_partial_kernel<TG, kDQ, kF16>), grid, dim3(256), 0, stream, a,
+                     w_tiles, per);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((qlora_gemv_finish_kernel<TG, kF16>), fgrid, dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream) {
@@ -395,17 +418,15 @@ hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(w_tiles + l_tiles), (unsigned)a.splits);
   const dim3 fgrid((unsigned)((a.rows + 127) / 128));
   if (a.T <= 32) {
-    hipLaunchKernelGGL(qlora_gemv_partial_kernel<1>, grid, dim3(256), 0, stream, a, w_tiles, per);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(qlora_gemv_finish_kernel<1>, fgrid, dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(qlora_gemv_partial_kernel<2>, grid, dim3(256), 0, stream, a, w_tiles, per);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(qlora_gemv_finish_kernel<2>, fgrid, dim3(256), 0, stream, a);
+    if (a.dq && !a.f16) return gemv_launch<1, true, false>(a, grid, fgrid, w_tiles, per, stream);
+    if (a.dq) return gemv_launch<1, true, true>(a, grid, fgrid, w_tiles, per, stream);
+    if (!a.f16) return gemv_launch<1, false, false>(a, grid, fgrid, w_tiles, per, stream);
+    return gemv_launch<1, false, true>(a, grid, fgrid, w_tiles, per, stream);
   }
-  return hipGetLastError();
+  if (a.dq && !a.f16) return gemv_launch<2, true, false>(a, grid, fgrid, w_tiles, per, stream);
+  if (a.dq) return gemv_launch<2, true, true>(a, grid, fgrid, w_tiles, per, stream);
+  if (!a.f16) return gemv_launch<2, false, false>(a, grid, fgrid, w_tiles, per, stream);
+  return gemv_launch<2, false, true>(a, grid, fgrid, w_tiles, per, stream);
 }
 
 }  // namespace qlora

@@ -9,11 +9,15 @@
 namespace qlora {
 
 // --- bulk path (quantize.hip) ---------------------------------------------
+// qt: codebook (0 NF4, 1 evenly spaced INT4); dq: double quantisation
+// (otherwise s2 holds the n_b float32 block constants and code8, mu, cblk,
+// gpart are unused); f16: fp16 output instead of bf16.
 hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t* code8,
-                           float* s2, float* mu, float* cblk, double* gpart,
+                           float* s2, float* mu, float* cblk, double* gpart, int qt, bool dq,
                            hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* code8, const float* s2,
-                             const float* mu, int64_t n, uint16_t* out, hipStream_t stream);
+                             const float* mu, int64_t n, uint16_t* out, int qt, bool dq, bool f16,
+                             hipStream_t stream);
 
 // --- fused dequant GEMMs (gemm.hip) ---------------------------------------
 // out[T, out_len] = act[T, red_len] * Wop + lora_l[T, r] * lora_r[out_len, r]^T
@@ -35,6 +39,8 @@ struct GemmArgs {
   // per 4 tokens x 1 feature), applied to the seed lora_l * lora_r^T; NULL
   // for none
   const uint8_t* keep;
+  bool dq;                 // double-quantised constants (else s2 = float32 c per block)
+  bool f16;                // fp16 compute (else bf16)
 };
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
@@ -72,6 +78,8 @@ struct GemvArgs {
   float* P;                // [splits][T][rows]
   float* PU;               // [splits][T][r]
   int32_t splits;
+  bool dq;                 // double-quantised constants (else s2 = float32 c per block)
+  bool f16;                // fp16 compute (else bf16)
 };
 hipError_t launch_qlora_gemv(const GemvArgs& a, hipStream_t stream);
 
@@ -101,6 +109,9 @@ struct MergeArgs {
   int32_t r;
   float scale;
   uint16_t* out;
+  int qt;                  // codebook (0 NF4, 1 evenly spaced INT4)
+  bool dq;                 // double-quantised constants (else s2 = float32 c per block)
+  bool f16;                // fp16 (else bf16) A, B, base and result
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
@@ -111,7 +122,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 int lora_proj_splits(int64_t T, int64_t red, int32_t r);
 hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
                                     int64_t T, int64_t red, int32_t r, int splits, float* P,
-                                    hipStream_t stream);
+                                    bool f16, hipStream_t stream);
 // bf16 transposes: out[c][r'] = in[r'][c] for an [R, C] input; out has row
 // stride ld_out and is zero for R <= r' < ld_out.
 struct TransposeJob {
@@ -141,6 +152,7 @@ struct ProjReduce {
   float scale_rm;          // 1 except under lora_dropout (1 / (1 - p))
   uint16_t* out_tr;
   int64_t ld_tr;
+  bool f16;                // outputs fp16 (else bf16)
 };
 hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream);
 
@@ -161,7 +173,7 @@ struct GradJobs {
   int n;
 };
 int lora_grad_splits(int64_t T, int64_t Q);
-hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
+hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits, bool f16,
                                     hipStream_t stream);
 hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
                                    hipStream_t stream);

@@ -123,7 +123,7 @@ __device__ __forceinline__ u32x4_t proj_frag(const ProjCtx<NJ, kRT>& c, const ui
 // L(it + 1), R(it + 1) and L(it + 2); in the two iterations after it, which
 // issue nothing, L(it + 1) and R(it + 1) for the first and none for the
 // second (kTail = 1, 2).
-template <int NJ, bool kRT, int SI, bool kMore, int kTail>
+template <int NJ, bool kRT, bool kF16, int SI, bool kMore, int kTail>
 __device__ __forceinline__ void proj_iter(const ProjCtx<NJ, kRT>& c, int it, uint16_t* const (&st)[3],
                                           u32x4_t (&xb)[3][4][2], f32x4_t (&acc)[2][NJ]) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -142,16 +142,18 @@ __device__ __forceinline__ void proj_iter(const ProjCtx<NJ, kRT>& c, int it, uin
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[g][j] = mfma16(xb[SI][u][g], rf[j], acc[g][j]);
+      for (int j = 0; j < NJ; ++j) acc[g][j] = mfma16<kF16>(xb[SI][u][g], rf[j], acc[g][j]);
   }
   __builtin_amdgcn_sched_barrier(0);
 #endif
 }
 
-template <int NJ, bool kRT>
+template <int NJ, bool kRT, bool kF16>
 __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ R, int64_t T, int64_t red,
     int64_t chunk, float* __restrict__ P) {
+  // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kStage = 16 * NJ * 128;   // bf16 elements
   __shared__ __attribute__((aligned(1024))) uint16_t s0[kStage];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[kStage];
@@ -209,12 +211,12 @@ __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
     // follow the loop
     const int nit3 = nit - nit % 3;
     for (int it = 0; it < nit3; it += 3) {
-      proj_iter<NJ, kRT, 0, true, 0>(c, it, st, xb, acc);
-      proj_iter<NJ, kRT, 1, true, 0>(c, it + 1, st, xb, acc);
-      proj_iter<NJ, kRT, 2, true, 0>(c, it + 2, st, xb, acc);
+      proj_iter<NJ, kRT, kF16, 0, true, 0>(c, it, st, xb, acc);
+      proj_iter<NJ, kRT, kF16, 1, true, 0>(c, it + 1, st, xb, acc);
+      proj_iter<NJ, kRT, kF16, 2, true, 0>(c, it + 2, st, xb, acc);
     }
-    if (nit3 < nit) proj_iter<NJ, kRT, 0, false, 1>(c, nit3, st, xb, acc);
-    if (nit3 + 1 < nit) proj_iter<NJ, kRT, 1, false, 2>(c, nit3 + 1, st, xb, acc);
+    if (nit3 < nit) proj_iter<NJ, kRT, kF16, 0, false, 1>(c, nit3, st, xb, acc);
+    if (nit3 + 1 < nit) proj_iter<NJ, kRT, kF16, 1, false, 2>(c, nit3 + 1, st, xb, acc);
     // the loads issued past the end read nothing; let them land before exit
     __builtin_amdgcn_s_waitcnt((7 << 4) | (0xF << 8));
   }
@@ -228,6 +230,7 @@ __global__ __launch_bounds__(256) void lora_proj_partial_kernel(
         const int64_t t = m0 + 16 * g + 4 * (c.lane >> 4) + e;
         if (t < T) out[t * (16 * NJ) + 16 * j + (c.lane & 15)] = acc[g][j][e];
       }
+#endif
 }
 
 static int64_t proj_chunk(int64_t red, int splits) {
@@ -235,20 +238,21 @@ static int64_t proj_chunk(int64_t red, int splits) {
   return (c + 127) / 128 * 128;
 }
 
-hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
-                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
-                                    hipStream_t stream) {
+template <bool kF16>
+static hipError_t proj_partial_dispatch(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                        int64_t T, int64_t red, int32_t r, int splits, float* P,
+                                        hipStream_t stream) {
   const int64_t chunk = proj_chunk(red, splits);
   const dim3 grid((unsigned)((T + 127) / 128), (unsigned)splits);
   switch ((r >> 4) * 2 + (r_by_rows ? 1 : 0)) {
 #define QLORA_PROJ_CASE(NJ)                                                                   \
   case 2 * NJ:                                                                                \
-    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, false>), grid, dim3(256), 0, stream, L,  \
-                       R, T, red, chunk, P);                                                  \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, false, kF16>), grid, dim3(256), 0, stream, \
+                       L, R, T, red, chunk, P);                                               \
     break;                                                                                    \
   case 2 * NJ + 1:                                                                            \
-    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, true>), grid, dim3(256), 0, stream, L,   \
-                       R, T, red, chunk, P);                                                  \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, true, kF16>), grid, dim3(256), 0, stream, \
+                       L, R, T, red, chunk, P);                                               \
     break;
     QLORA_PROJ_CASE(1) QLORA_PROJ_CASE(2) QLORA_PROJ_CASE(3) QLORA_PROJ_CASE(4)
     QLORA_PROJ_CASE(5) QLORA_PROJ_CASE(6) QLORA_PROJ_CASE(7) QLORA_PROJ_CASE(8)
@@ -256,6 +260,13 @@ hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
+                                    bool f16, hipStream_t stream) {
+  return f16 ? proj_partial_dispatch<true>(L, R, r_by_rows, T, red, r, splits, P, stream)
+             : proj_partial_dispatch<false>(L, R, r_by_rows, T, red, r, splits, P, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -323,14 +334,19 @@ __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, Tra
   }
   uint16_t b[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) b[e] = (uint16_t)(pack_bf16x2(v[e] * a.scale_rm, 0.0f) & 0xFFFFu);
+  for (int e = 0; e < 4; ++e)
+    b[e] = (uint16_t)((a.f16 ? pack_f16x2(v[e] * a.scale_rm, 0.0f)
+                             : pack_bf16x2(v[e] * a.scale_rm, 0.0f)) & 0xFFFFu);
   if (t < a.T) {
     if (a.out_rm)
       *reinterpret_cast<uint2*>(a.out_rm + i) =
           uint2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
     if (a.out_sc)
       *reinterpret_cast<uint2*>(a.out_sc + i) =
-          uint2{pack_bf16x2(v[0] * a.scale, v[1] * a.scale), pack_bf16x2(v[2] * a.scale, v[3] * a.scale)};
+          a.f16 ? uint2{pack_f16x2(v[0] * a.scale, v[1] * a.scale),
+                        pack_f16x2(v[2] * a.scale, v[3] * a.scale)}
+                : uint2{pack_bf16x2(v[0] * a.scale, v[1] * a.scale),
+                        pack_bf16x2(v[2] * a.scale, v[3] * a.scale)};
   }
   if (a.out_tr) {
 #pragma unroll
@@ -417,7 +433,7 @@ __device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t
   return u32x4_t{l.x, l.y, h.x, h.y};
 }
 
-template <int NP, int SI>
+template <int NP, bool kF16, int SI>
 __device__ __forceinline__ void grad_iter(const GradCtx<NP>& c, int it, uint16_t* const (&ls)[3],
                                           uint16_t* const (&ss)[3], uint16_t* dummy,
                                           f32x4_t (&acc)[NP][2]) {
@@ -454,15 +470,17 @@ __device__ __forceinline__ void grad_iter(const GradCtx<NP>& c, int it, uint16_t
 #pragma unroll
     for (int j = 0; j < NP; ++j)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) acc[j][cg] = mfma16(sf[j], lf[cg], acc[j][cg]);
+      for (int cg = 0; cg < 2; ++cg) acc[j][cg] = mfma16<kF16>(sf[j], lf[cg], acc[j][cg]);
   }
   __builtin_amdgcn_sched_barrier(0);
 #endif
 }
 
-template <int NP>
+template <int NP, bool kF16>
 __global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, int64_t T,
                                                                int64_t chunk) {
+  // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) uint16_t l0[64 * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t l1[64 * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t l2[64 * 128];
@@ -510,12 +528,12 @@ __global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, i
     __builtin_amdgcn_sched_barrier(0);
     const int nit3 = nit - nit % 3;
     for (int it = 0; it < nit3; it += 3) {
-      grad_iter<NP, 0>(c, it, ls, ss, dummy, acc);
-      grad_iter<NP, 1>(c, it + 1, ls, ss, dummy, acc);
-      grad_iter<NP, 2>(c, it + 2, ls, ss, dummy, acc);
+      grad_iter<NP, kF16, 0>(c, it, ls, ss, dummy, acc);
+      grad_iter<NP, kF16, 1>(c, it + 1, ls, ss, dummy, acc);
+      grad_iter<NP, kF16, 2>(c, it + 2, ls, ss, dummy, acc);
     }
-    if (nit3 < nit) grad_iter<NP, 0>(c, nit3, ls, ss, dummy, acc);
-    if (nit3 + 1 < nit) grad_iter<NP, 1>(c, nit3 + 1, ls, ss, dummy, acc);
+    if (nit3 < nit) grad_iter<NP, kF16, 0>(c, nit3, ls, ss, dummy, acc);
+    if (nit3 + 1 < nit) grad_iter<NP, kF16, 1>(c, nit3 + 1, ls, ss, dummy, acc);
     // the loads issued past the end read nothing; let them land before exit
     __builtin_amdgcn_s_waitcnt((7 << 4) | (0xF << 8));
   }
@@ -536,6 +554,7 @@ __global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, i
       }
     }
   }
+#endif
 }
 
 static int64_t grad_chunk(int64_t T, int splits) {
@@ -544,7 +563,7 @@ static int64_t grad_chunk(int64_t T, int splits) {
 }
 
 hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
-                                    hipStream_t stream) {
+                                    bool f16, hipStream_t stream) {
   const int64_t chunk = grad_chunk(T, splits);
   int64_t qmax = 0;
   for (int i = 0; i < jobs.n; ++i) qmax = jobs.job[i].Q > qmax ? jobs.job[i].Q : qmax;
@@ -552,8 +571,12 @@ hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int spl
   switch (r >> 4) {
 #define QLORA_GRAD_CASE(NP)                                                                  \
   case NP:                                                                                   \
-    hipLaunchKernelGGL(lora_grad_partial_kernel<NP>, grid, dim3(256), 0, stream, jobs, T,    \
-                       chunk);                                                               \
+    if (f16)                                                                                 \
+      hipLaunchKernelGGL((lora_grad_partial_kernel<NP, true>), grid, dim3(256), 0, stream,   \
+                         jobs, T, chunk);                                                    \
+    else                                                                                     \
+      hipLaunchKernelGGL((lora_grad_partial_kernel<NP, false>), grid, dim3(256), 0, stream,  \
+                         jobs, T, chunk);                                                    \
     break;
     QLORA_GRAD_CASE(1) QLORA_GRAD_CASE(2) QLORA_GRAD_CASE(3) QLORA_GRAD_CASE(4)
     QLORA_GRAD_CASE(5) QLORA_GRAD_CASE(6) QLORA_GRAD_CASE(7) QLORA_GRAD_CASE(8)

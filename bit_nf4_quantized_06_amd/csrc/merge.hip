@@ -4,7 +4,8 @@
 //
 // w_hat the bf16 dequantised weight, B [rows, r] and A [r, cols] bf16, the
 // product accumulated in float32, scaled and added in float32, rounded once
-// to bf16.  (waylandz LLM book 26.2: at inference the adapter is folded into
+// to bf16.  (Variants: fp16 in place of bf16 throughout, float32 block
+// constants without double quantisation, the evenly spaced INT4 codebook.)  (waylandz LLM book 26.2: at inference the adapter is folded into
 // the weight once, W + (alpha/r) B A; ta-paperlens 落とし穴 and the
 // Ultralytics QLoRA page, Kompromisse: the merge is done on the base
 // dequantised to 16 bit, and the result may be quantised again.)
@@ -41,10 +42,10 @@ constexpr int kDStride = 36;      // floats per consumer thread in the delta buf
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+template <bool kF16>
 __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b,
                                            const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  return mfma32x32<kF16>(a, b, c);
 }
 
 __device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t* p1) {
@@ -55,9 +56,10 @@ __device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t
   return u32x4_t{l.x, l.y, h.x, h.y};
 }
 
-// float32 value of bf16_RNE(x)
-__device__ __forceinline__ float bf16_round(float x) {
-  return __uint_as_float(pack_bf16x2(x, 0.0f) << 16);
+// float32 value of x rounded to the 16-bit compute type (nearest even)
+template <bool kF16>
+__device__ __forceinline__ float round16(float x) {
+  return lo16_to_f32<kF16>(pack16x2<kF16>(x, 0.0f));
 }
 
 }  // namespace
@@ -92,7 +94,9 @@ struct MergeCtx {
   bool wok[4];              // chunk w lies inside the weight
 };
 
-template <int NP>
+// kDQ false: s2[w] receives chunk w's block constant itself (float32, one
+// per block) and there is no 8-bit code.
+template <int NP, bool kDQ>
 __device__ __forceinline__ void merge_load(const MergeArgs& a, const MergeCtx& c, int64_t n0,
                                            MergePass<NP>& m) {
   const int64_t last = a.rows - 1;
@@ -102,8 +106,13 @@ __device__ __forceinline__ void merge_load(const MergeArgs& a, const MergeCtx& c
   for (int w = 0; w < 4; ++w) {
     const int64_t e0 = rowe + c.kclamp[w];
     m.cw[w] = *reinterpret_cast<const uint32_t*>(a.codes + e0 / 2);
-    m.c8[w] = a.code8[e0 >> 6];
-    m.s2[w] = a.s2[e0 >> 14];
+    if (kDQ) {
+      m.c8[w] = a.code8[e0 >> 6];
+      m.s2[w] = a.s2[e0 >> 14];
+    } else {
+      m.c8[w] = 0u;
+      m.s2[w] = a.s2[e0 >> 6];
+    }
   }
   const int64_t bn = n0 + c.l32 < last ? n0 + c.l32 : last;
 #pragma unroll
@@ -114,10 +123,10 @@ __device__ __forceinline__ void merge_load(const MergeArgs& a, const MergeCtx& c
 // One 32-row pass from `cur`; the loads of the pass after it go to `nxt`
 // first.  The two register sets alternate between passes (no copy, so
 // nothing waits for the loads or for the previous pass's stores).
-template <int NP>
+template <int NP, bool kDQ, bool kF16>
 __device__ __forceinline__ void merge_pass(const MergeArgs& a, const MergeCtx& c, int64_t n0,
                                            const MergePass<NP>& cur, MergePass<NP>& nxt) {
-  merge_load(a, c, n0 + kTileRows, nxt);
+  merge_load<NP, kDQ>(a, c, n0 + kTileRows, nxt);
   f32x16_t acc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -128,7 +137,7 @@ __device__ __forceinline__ void merge_pass(const MergeArgs& a, const MergeCtx& c
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint16_t* p = c.as + (16 * j + c.prow) * kASlice + c.acol[t];
-      acc[t] = mfma32(cur.bf[j], ld_tr_pair(p, p + 4 * kASlice), acc[t]);
+      acc[t] = mfma32<kF16>(cur.bf[j], ld_tr_pair(p, p + 4 * kASlice), acc[t]);
     }
   }
   // acc[t][e] = (B A)[row 8 (e / 4) + 4 lhi + e % 4][column 64 wave + 32 t + l32];
@@ -153,16 +162,16 @@ __device__ __forceinline__ void merge_pass(const MergeArgs& a, const MergeCtx& c
   const bool row_ok = n < a.rows;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float cp = block_constant(cur.c8[w], cur.s2[w], c.mu);
+    const float cp = kDQ ? block_constant(cur.c8[w], cur.s2[w], c.mu) : cur.s2[w];
     u32x4_t o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 8 * w + 2 * e;   // element index within the 32
-      const float lo = bf16_round(__fmul_rn(c.q[(cur.cw[w] >> (8 * e)) & 15u], cp));
-      const float hi = bf16_round(__fmul_rn(c.q[(cur.cw[w] >> (8 * e + 4)) & 15u], cp));
+      const float lo = round16<kF16>(__fmul_rn(c.q[(cur.cw[w] >> (8 * e)) & 15u], cp));
+      const float hi = round16<kF16>(__fmul_rn(c.q[(cur.cw[w] >> (8 * e + 4)) & 15u], cp));
       const float dlo = __uint_as_float(d4[i >> 2][i & 3]);
       const float dhi = __uint_as_float(d4[(i + 1) >> 2][(i + 1) & 3]);
-      o[e] = pack_bf16x2(__fadd_rn(lo, dlo), __fadd_rn(hi, dhi));
+      o[e] = pack16x2<kF16>(__fadd_rn(lo, dlo), __fadd_rn(hi, dhi));
     }
     if (row_ok && c.wok[w])
       *reinterpret_cast<u32x4_t*>(a.out + n * a.cols + c.kb + 64 * w) = o;
@@ -170,8 +179,10 @@ __device__ __forceinline__ void merge_pass(const MergeArgs& a, const MergeCtx& c
   __syncthreads();   // the delta buffer is rewritten by the next pass
 }
 
-template <int NP>
+template <int NP, bool kDQ, bool kF16>
 __global__ __launch_bounds__(256) void nf4_merge_kernel(MergeArgs a) {
+  // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int R = 16 * NP;
   __shared__ __attribute__((aligned(16))) uint16_t as[R * kASlice];
   __shared__ __attribute__((aligned(16))) float dl[256 * kDStride];
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(MergeArgs a) {
   const int64_t k0 = (int64_t)blockIdx.x * kMergeCols;
   const int64_t nb = (int64_t)blockIdx.y * kMergeRows;
   const int64_t ne = nb + kMergeRows < a.rows ? nb + kMergeRows : a.rows;
-  if (tid < 16) q[tid] = kNF4[tid];
+  if (tid < 16) q[tid] = a.qt ? kINT4[tid] : kNF4[tid];
   // the A slice; columns past the weight read a clamped column, and only
   // feed columns that are never stored
   for (int i = tid; i < R * 32; i += 256) {
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(MergeArgs a) {
     *reinterpret_cast<u32x4_t*>(as + p * kASlice + 8 * ch) =
         *reinterpret_cast<const u32x4_t*>(a.A + (int64_t)p * a.cols + k);
   }
-  c.mu = a.mu[0];
+  c.mu = kDQ ? a.mu[0] : 0.0f;
   // consumer role: row crow of the pass, chunks at columns kb + 64 w
   c.crow = tid >> 3;
   c.kb = k0 + 8 * (tid & 7);
@@ -215,32 +226,34 @@ __global__ __launch_bounds__(256) void nf4_merge_kernel(MergeArgs a) {
     c.acol[t] = 64 * c.wave + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   MergePass<NP> p0, p1;
-  merge_load(a, c, nb, p0);
+  merge_load<NP, kDQ>(a, c, nb, p0);
   __syncthreads();   // A slice and table visible
   if (ne - nb == kMergeRows) {
     // a whole row group: straight-line passes, so the waits before each
     // pass count exactly the loads and stores issued since its own loads
 #pragma unroll
     for (int i = 0; i < kMergeRows / kTileRows; i += 2) {
-      merge_pass(a, c, nb + i * kTileRows, p0, p1);
-      merge_pass(a, c, nb + (i + 1) * kTileRows, p1, p0);
+      merge_pass<NP, kDQ, kF16>(a, c, nb + i * kTileRows, p0, p1);
+      merge_pass<NP, kDQ, kF16>(a, c, nb + (i + 1) * kTileRows, p1, p0);
     }
   } else {
     for (int64_t n0 = nb; n0 < ne; n0 += 2 * kTileRows) {
-      merge_pass(a, c, n0, p0, p1);
+      merge_pass<NP, kDQ, kF16>(a, c, n0, p0, p1);
       if (n0 + kTileRows >= ne) break;
-      merge_pass(a, c, n0 + kTileRows, p1, p0);
+      merge_pass<NP, kDQ, kF16>(a, c, n0 + kTileRows, p1, p0);
     }
   }
+#endif
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+template <bool kDQ, bool kF16>
+static hipError_t merge_dispatch(const MergeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.cols + kMergeCols - 1) / kMergeCols),
                   (unsigned)((a.rows + kMergeRows - 1) / kMergeRows));
   switch (a.r >> 4) {
 #define QLORA_MERGE_CASE(NP)                                                                  \
   case NP:                                                                                    \
-    hipLaunchKernelGGL(nf4_merge_kernel<NP>, grid, dim3(256), 0, stream, a);                  \
+    hipLaunchKernelGGL((nf4_merge_kernel<NP, kDQ, kF16>), grid, dim3(256), 0, stream, a);     \
     break;
     QLORA_MERGE_CASE(1) QLORA_MERGE_CASE(2) QLORA_MERGE_CASE(3) QLORA_MERGE_CASE(4)
     QLORA_MERGE_CASE(5) QLORA_MERGE_CASE(6) QLORA_MERGE_CASE(7) QLORA_MERGE_CASE(8)
@@ -248,6 +261,13 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  if (a.dq && !a.f16) return merge_dispatch<true, false>(a, stream);
+  if (a.dq) return merge_dispatch<true, true>(a, stream);
+  if (!a.f16) return merge_dispatch<false, false>(a, stream);
+  return merge_dispatch<false, true>(a, stream);
 }
 
 }  // namespace qlora

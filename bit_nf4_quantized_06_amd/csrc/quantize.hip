@@ -1,5 +1,8 @@
 // Bulk kernels: blockwise NF4 quantisation, double quantisation of the block
-// constants, and dequantisation to bf16 (gfx950).
+// constants, and dequantisation to bf16 (gfx950).  Variants: the evenly
+// spaced INT4 codebook (Ultralytics glossary "QLoRA", code example), no double
+// quantisation (float32 constants stored as they are, ta-paperlens 二重量子化:
+// 4.5 bits per weight) and fp16 output (ta-paperlens 落とし穴).
 //
 // Method: ta-paperlens "QLoRA — 650億パラメータ…", sections 量子化を1段落で
 // (absmax per block of 64, nearest level, restore by lookup and multiply),
@@ -28,26 +31,37 @@ namespace qlora {
 // 0..3, odd lanes words 4..7.
 // ---------------------------------------------------------------------------
 
+// Decision threshold i of codebook kQT (0: NF4, 1: evenly spaced INT4).
+template <int kQT>
+__device__ __forceinline__ constexpr float thr(int i) {
+  return kQT ? kINT4Thr[i] : kNF4Thr[i];
+}
+
 // Nearest-level index by a 4-step binary search over the 15 decision
 // thresholds; the thresholds of each step are picked with selects from
 // constants (scalar registers), so no step waits on a memory read.
+template <int kQT>
 __device__ __forceinline__ uint32_t nf4_code(float r) {
-  const bool b8 = r > kNF4Thr[7];
-  const bool b4 = r > (b8 ? kNF4Thr[11] : kNF4Thr[3]);
-  const float t2lo = b4 ? kNF4Thr[5] : kNF4Thr[1];
-  const float t2hi = b4 ? kNF4Thr[13] : kNF4Thr[9];
+  const bool b8 = r > thr<kQT>(7);
+  const bool b4 = r > (b8 ? thr<kQT>(11) : thr<kQT>(3));
+  const float t2lo = b4 ? thr<kQT>(5) : thr<kQT>(1);
+  const float t2hi = b4 ? thr<kQT>(13) : thr<kQT>(9);
   const bool b2 = r > (b8 ? t2hi : t2lo);
   // threshold index 8 b8 + 4 b4 + 2 b2 (even indices 0 .. 14)
-  const float t00 = b2 ? kNF4Thr[2] : kNF4Thr[0];
-  const float t04 = b2 ? kNF4Thr[6] : kNF4Thr[4];
-  const float t08 = b2 ? kNF4Thr[10] : kNF4Thr[8];
-  const float t12 = b2 ? kNF4Thr[14] : kNF4Thr[12];
+  const float t00 = b2 ? thr<kQT>(2) : thr<kQT>(0);
+  const float t04 = b2 ? thr<kQT>(6) : thr<kQT>(4);
+  const float t08 = b2 ? thr<kQT>(10) : thr<kQT>(8);
+  const float t12 = b2 ? thr<kQT>(14) : thr<kQT>(12);
   const float tl = b4 ? t04 : t00;
   const float th = b4 ? t12 : t08;
   const bool b1 = r > (b8 ? th : tl);
   return (b8 ? 8u : 0u) | (b4 ? 4u : 0u) | (b2 ? 2u : 0u) | (b1 ? 1u : 0u);
 }
 
+// kDQ: also the group's float64 partial sum of the constants (the mean's
+// tree); cblk is then the workspace copy of the constants, otherwise the
+// stored float32 constants themselves.
+template <int kQT, bool kDQ>
 __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
     const float* __restrict__ W, int64_t n_b, uint32_t* __restrict__ codes,
     float* __restrict__ cblk, double* __restrict__ gpart) {
@@ -98,8 +112,16 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
         const float wm = ldexpf(v[e], -ex);
         const float q0 = wm * y;
         const float rem = fmaf(-q0, cm, wm);
-        const float r = fmaf(rem, y, q0);
-        hh[e >> 2] |= nf4_code(r) << (4 * (e & 3));
+        float r = fmaf(rem, y, q0);
+        if (kQT == 1 && fabsf(wm) < 0x1p-126f) {
+          // the scaling may have rounded a tiny w (c >= 1); the quotient is
+          // then below 2^-125, where the only decision is the evenly spaced
+          // codebook's threshold at 0: IEEE w / c is 0 exactly when
+          // |w| 2^150 <= c (an exact scaling; inf above 2^-22 is right too)
+          const bool nz = ldexpf(fabsf(v[e]), 150) > m;
+          r = copysignf(nz ? 0x1p-149f : 0.0f, v[e]);
+        }
+        hh[e >> 2] |= nf4_code<kQT>(r) << (4 * (e & 3));
       }
       h0 = hh[0];
       h1 = hh[1];
@@ -116,13 +138,15 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
   const float c = __shfl(c_keep, (lane & 7) * 8 + (lane >> 3));
   const int64_t bj = blk0 + lane;
   if (bj < n_b) cblk[bj] = c;
-  // pairwise float64 tree over the wave's 64 consecutive blocks (padding = 0)
-  double s = (bj < n_b) ? (double)c : 0.0;
+  if (kDQ) {
+    // pairwise float64 tree over the wave's 64 consecutive blocks (padding = 0)
+    double s = (bj < n_b) ? (double)c : 0.0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) s += __shfl_down(s, d);
-  if (lane == 0) wsum[wave] = s;
-  __syncthreads();
-  if (tid == 0) gpart[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    for (int d = 1; d < 64; d <<= 1) s += __shfl_down(s, d);
+    if (lane == 0) wsum[wave] = s;
+    __syncthreads();
+    if (tid == 0) gpart[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -216,17 +240,20 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // Dequantise to bf16: each thread handles 4 words of 8 codes, one wave-stride
 // apart so that every load (4 B per lane) and store (16 B per lane) of a wave
-// is contiguous.  The level is looked up in shared memory, multiplied by the
-// decoded block constant in float32 and rounded once to bf16.
+// is contiguous.  The level (codebook qt) is looked up in shared memory,
+// multiplied by the block constant (decoded, or the stored float32 one
+// without double quantisation) in float32 and rounded once to the 16-bit
+// compute type (bf16, or fp16 with kF16).
 // ---------------------------------------------------------------------------
+template <bool kDQ, bool kF16>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
-    const float* __restrict__ s2, const float* __restrict__ mu_p, int64_t n_words,
+    const float* __restrict__ s2, const float* __restrict__ mu_p, int64_t n_words, int qt,
     u32x4_t* __restrict__ out) {
   __shared__ float q[16];
-  if (threadIdx.x < 16) q[threadIdx.x] = kNF4[threadIdx.x];
+  if (threadIdx.x < 16) q[threadIdx.x] = qt ? kINT4[threadIdx.x] : kNF4[threadIdx.x];
   __syncthreads();
-  const float mu = mu_p[0];
+  const float mu = kDQ ? mu_p[0] : 0.0f;
   const int64_t base = (int64_t)blockIdx.x * (256 * 4) + threadIdx.x;
   uint32_t w[4];
   float cp[4];
@@ -238,7 +265,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     if (i < n_words) {
       w[j] = __builtin_nontemporal_load(codes + i);
       const int64_t blk = i >> 3;
-      cp[j] = block_constant(code8[blk], s2[blk >> 8], mu);
+      cp[j] = kDQ ? block_constant(code8[blk], s2[blk >> 8], mu) : s2[blk];
     }
   }
 #pragma unroll
@@ -250,7 +277,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
       for (int e = 0; e < 4; ++e) {
         const float a = __fmul_rn(q[(w[j] >> (8 * e)) & 15u], cp[j]);
         const float b = __fmul_rn(q[(w[j] >> (8 * e + 4)) & 15u], cp[j]);
-        o[e] = pack_bf16x2(a, b);
+        o[e] = pack16x2<kF16>(a, b);
       }
       __builtin_nontemporal_store(o, out + i);
     }
@@ -261,11 +288,26 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t* code8,
-                           float* s2, float* mu, float* cblk, double* gpart,
+                           float* s2, float* mu, float* cblk, double* gpart, int qt, bool dq,
                            hipStream_t stream) {
   const int64_t n_g = (n_b + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(nf4_quantize_blocks_kernel, dim3((unsigned)n_g), dim3(256), 0, stream, W,
-                     n_b, reinterpret_cast<uint32_t*>(codes), cblk, gpart);
+  uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
+  if (!dq) {
+    // the float32 constants are the stored state (s2 holds n_b of them)
+    if (qt)
+      hipLaunchKernelGGL((nf4_quantize_blocks_kernel<1, false>), dim3((unsigned)n_g), dim3(256),
+                         0, stream, W, n_b, cw, s2, nullptr);
+    else
+      hipLaunchKernelGGL((nf4_quantize_blocks_kernel<0, false>), dim3((unsigned)n_g), dim3(256),
+                         0, stream, W, n_b, cw, s2, nullptr);
+    return hipGetLastError();
+  }
+  if (qt)
+    hipLaunchKernelGGL((nf4_quantize_blocks_kernel<1, true>), dim3((unsigned)n_g), dim3(256), 0,
+                       stream, W, n_b, cw, cblk, gpart);
+  else
+    hipLaunchKernelGGL((nf4_quantize_blocks_kernel<0, true>), dim3((unsigned)n_g), dim3(256), 0,
+                       stream, W, n_b, cw, cblk, gpart);
   int64_t pow2 = 1;
   while (pow2 < n_g) pow2 <<= 1;
   const int64_t per = pow2 > 1024 ? pow2 / 1024 : 1;
@@ -276,12 +318,24 @@ hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t*
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* code8, const float* s2,
-                             const float* mu, int64_t n, uint16_t* out, hipStream_t stream) {
+                             const float* mu, int64_t n, uint16_t* out, int qt, bool dq, bool f16,
+                             hipStream_t stream) {
   const int64_t n_words = n / 8;
-  const int64_t grid = (n_words + 1023) / 1024;
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     reinterpret_cast<const uint32_t*>(codes), code8, s2, mu, n_words,
-                     reinterpret_cast<u32x4_t*>(out));
+  const dim3 grid((unsigned)((n_words + 1023) / 1024));
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
+  if (dq && !f16)
+    hipLaunchKernelGGL((nf4_dequant_kernel<true, false>), grid, dim3(256), 0, stream, cw, code8,
+                       s2, mu, n_words, qt, o);
+  else if (dq)
+    hipLaunchKernelGGL((nf4_dequant_kernel<true, true>), grid, dim3(256), 0, stream, cw, code8,
+                       s2, mu, n_words, qt, o);
+  else if (!f16)
+    hipLaunchKernelGGL((nf4_dequant_kernel<false, false>), grid, dim3(256), 0, stream, cw, code8,
+                       s2, mu, n_words, qt, o);
+  else
+    hipLaunchKernelGGL((nf4_dequant_kernel<false, true>), grid, dim3(256), 0, stream, cw, code8,
+                       s2, mu, n_words, qt, o);
   return hipGetLastError();
 }
 

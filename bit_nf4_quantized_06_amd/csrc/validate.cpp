@@ -101,16 +101,32 @@ qlora_status dropout_consts(const qlora_dropout* d, DropoutConsts* k) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Header fields only: version, block sizes and variant codes.
+static qlora_status check_format(const qlora_nf4_weight* w) {
+  if (w->format_version != QLORA_NF4_FORMAT_VERSION || w->blocksize != QLORA_NF4_BLOCKSIZE ||
+      (w->dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE && w->dq_blocksize != QLORA_NF4_DQ_OFF) ||
+      (w->quant_type != QLORA_QUANT_NF4 && w->quant_type != QLORA_QUANT_INT4) ||
+      (w->compute_dtype != QLORA_COMPUTE_BF16 && w->compute_dtype != QLORA_COMPUTE_FP16))
+    return QLORA_ERR_FORMAT;
+  return QLORA_OK;
+}
+
 qlora_status check_descriptor(const qlora_nf4_weight* w, WeightDims* d) {
   if (!w) return QLORA_ERR_NULL;
-  if (w->format_version != QLORA_NF4_FORMAT_VERSION || w->blocksize != QLORA_NF4_BLOCKSIZE ||
-      w->dq_blocksize != QLORA_NF4_DQ_BLOCKSIZE)
-    return QLORA_ERR_FORMAT;
-  const qlora_status s = check_weight_shape(w->rows, w->cols, d);
+  qlora_status s = check_format(w);
   if (s != QLORA_OK) return s;
-  if (!w->codes || !w->absmax_code || !w->absmax_scale || !w->absmax_offset) return QLORA_ERR_NULL;
-  if (!aligned16(w->codes) || !aligned16(w->absmax_code) || !aligned16(w->absmax_scale) ||
-      !aligned16(w->absmax_offset))
+  s = check_weight_shape(w->rows, w->cols, d);
+  if (s != QLORA_OK) return s;
+  const bool dq = w->dq_blocksize == QLORA_NF4_DQ_BLOCKSIZE;
+  if (d) {
+    d->qt = w->quant_type;
+    d->dq = dq;
+    d->f16 = w->compute_dtype == QLORA_COMPUTE_FP16;
+  }
+  if (!w->codes || !w->absmax_scale || (dq && (!w->absmax_code || !w->absmax_offset)))
+    return QLORA_ERR_NULL;
+  if (!aligned16(w->codes) || !aligned16(w->absmax_scale) ||
+      (dq && (!aligned16(w->absmax_code) || !aligned16(w->absmax_offset))))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
@@ -197,6 +213,7 @@ qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, 
                                WeightDims* d) {
   const qlora_status s = check_descriptor(w, d);
   if (s != QLORA_OK) return s;
+  if (d->qt != QLORA_QUANT_NF4) return QLORA_ERR_FORMAT;   // linear kernels: NF4 levels
   if (T < 1 || !linear_dims_ok(T, d->rows, d->cols)) return QLORA_ERR_SHAPE;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_SHAPE;
@@ -214,9 +231,43 @@ qlora_status qlora_nf4_weight_init(qlora_nf4_weight* w, int64_t rows, int64_t co
   w->format_version = QLORA_NF4_FORMAT_VERSION;
   w->blocksize = QLORA_NF4_BLOCKSIZE;
   w->dq_blocksize = QLORA_NF4_DQ_BLOCKSIZE;
-  w->reserved = 0;
+  w->quant_type = QLORA_QUANT_NF4;
+  w->compute_dtype = QLORA_COMPUTE_BF16;
   w->rows = rows;
   w->cols = cols;
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_weight_init_ex(qlora_nf4_weight* w, int64_t rows, int64_t cols,
+                                      int quant_type, int double_quant, int compute_dtype) {
+  if (!w) return QLORA_ERR_NULL;
+  if ((quant_type != QLORA_QUANT_NF4 && quant_type != QLORA_QUANT_INT4) ||
+      (double_quant != 0 && double_quant != 1) ||
+      (compute_dtype != QLORA_COMPUTE_BF16 && compute_dtype != QLORA_COMPUTE_FP16))
+    return QLORA_ERR_FORMAT;
+  const qlora_status s = qlora_nf4_weight_init(w, rows, cols);
+  if (s != QLORA_OK) return s;
+  w->dq_blocksize = double_quant ? QLORA_NF4_DQ_BLOCKSIZE : QLORA_NF4_DQ_OFF;
+  w->quant_type = (int16_t)quant_type;
+  w->compute_dtype = (int16_t)compute_dtype;
+  return QLORA_OK;
+}
+
+qlora_status qlora_nf4_weight_buffer_sizes(const qlora_nf4_weight* w, size_t* codes_bytes,
+                                           size_t* absmax_code_bytes,
+                                           size_t* absmax_scale_bytes,
+                                           size_t* absmax_offset_bytes) {
+  if (!w) return QLORA_ERR_NULL;
+  qlora_status s = qlora::check_format(w);
+  if (s != QLORA_OK) return s;
+  qlora::WeightDims d;
+  s = qlora::check_weight_shape(w->rows, w->cols, &d);
+  if (s != QLORA_OK) return s;
+  const bool dq = w->dq_blocksize == QLORA_NF4_DQ_BLOCKSIZE;
+  if (codes_bytes) *codes_bytes = (size_t)(d.n / 2);
+  if (absmax_code_bytes) *absmax_code_bytes = dq ? (size_t)d.n_b : 0;
+  if (absmax_scale_bytes) *absmax_scale_bytes = sizeof(float) * (size_t)(dq ? d.n_g : d.n_b);
+  if (absmax_offset_bytes) *absmax_offset_bytes = dq ? sizeof(float) : 0;
   return QLORA_OK;
 }
 

@@ -38,7 +38,15 @@ extern "C" {
 #define QLORA_NF4_FORMAT_VERSION 1
 #define QLORA_NF4_BLOCKSIZE 64       /* weights per absmax block               */
 #define QLORA_NF4_DQ_BLOCKSIZE 256   /* block constants per second-level scale */
+#define QLORA_NF4_DQ_OFF 0           /* dq_blocksize of a weight without double quantisation */
 #define QLORA_MAX_RANK 128
+
+/* quant_type: the 4-bit codebook */
+#define QLORA_QUANT_NF4 0            /* normal-quantile levels with an exact 0 */
+#define QLORA_QUANT_INT4 1           /* evenly spaced levels -1 + 2i/15        */
+/* compute_dtype: the 16-bit type of activations, adapters and dequantised weights */
+#define QLORA_COMPUTE_BF16 0
+#define QLORA_COMPUTE_FP16 1
 
 typedef enum {
   QLORA_OK = 0,
@@ -48,12 +56,15 @@ typedef enum {
   QLORA_ERR_WORKSPACE = 4,  /* workspace smaller than the matching *_workspace() */
   QLORA_ERR_DEVICE = 5,     /* the current device is not a gfx950 GPU           */
   QLORA_ERR_HIP = 6,        /* a HIP runtime call failed; see qlora_last_hip_error */
-  QLORA_ERR_FORMAT = 7      /* weight descriptor has a wrong version/blocksize  */
+  QLORA_ERR_FORMAT = 7      /* weight descriptor has a wrong version/blocksize,
+                               an unknown variant, or a variant the call does not take */
 } qlora_status;
 
 /*
  * Packed NF4 weight with double-quantised block constants (host struct that
- * holds device pointers; caller-owned).
+ * holds device pointers; caller-owned).  The layout below is the default
+ * format (quant_type NF4, double quantisation on, compute dtype bf16); the
+ * variants follow it.
  *
  * W is [rows = out_features, cols = in_features] row-major, rows % 16 == 0,
  * cols % 64 == 0.
@@ -71,12 +82,28 @@ typedef enum {
  * dequantised weight: bf16_RNE(RN32(q[code] * c'_b)).
  * Storage: n/2 + n_b + 4 n_g + 4 bytes = 4 + 8/64 + 32/16384 bits per weight
  * plus 32 bits per tensor (ta-paperlens 二重量子化: about 4.127 bits).
+ *
+ * Variants (the config knobs bnb_4bit_use_double_quant and
+ * bnb_4bit_compute_dtype of ta-paperlens コードで見る, and the comparison
+ * codebook of the Ultralytics code example):
+ *   dq_blocksize QLORA_NF4_DQ_OFF: no double quantisation; absmax_scale holds
+ *     the n_b float32 block constants c_b themselves and absmax_code,
+ *     absmax_offset are unused (may be NULL): 4 + 32/64 = 4.5 bits per weight
+ *     (ta-paperlens 二重量子化).
+ *   quant_type QLORA_QUANT_INT4: levels -1 + 2i/15 rounded to float32 (no
+ *     exact 0; a zero quotient takes level 7); quantise, dequantise and
+ *     merge only -- the linear entry points return QLORA_ERR_FORMAT.
+ *   compute_dtype QLORA_COMPUTE_FP16: every 16-bit tensor of the calls that
+ *     take this weight (dequantised or merged weight, X, A, B, Y, U, dY, dX)
+ *     is IEEE binary16; roundings are to nearest even (ta-paperlens 落とし穴:
+ *     FP16 where the GPU has no BF16; waylandz 26.6.4 uses float16).
  */
 typedef struct {
   int32_t format_version;   /* QLORA_NF4_FORMAT_VERSION */
   int32_t blocksize;        /* QLORA_NF4_BLOCKSIZE      */
-  int32_t dq_blocksize;     /* QLORA_NF4_DQ_BLOCKSIZE   */
-  int32_t reserved;         /* 0 */
+  int32_t dq_blocksize;     /* QLORA_NF4_DQ_BLOCKSIZE, or QLORA_NF4_DQ_OFF */
+  int16_t quant_type;       /* QLORA_QUANT_NF4 (0) or QLORA_QUANT_INT4 */
+  int16_t compute_dtype;    /* QLORA_COMPUTE_BF16 (0) or QLORA_COMPUTE_FP16 */
   int64_t rows;
   int64_t cols;
   uint8_t *codes;
@@ -85,11 +112,24 @@ typedef struct {
   float *absmax_offset;
 } qlora_nf4_weight;
 
-/* Fill a descriptor's header fields for a [rows, cols] weight (host call;
- * pointers are left untouched).  Returns QLORA_ERR_SHAPE unless rows >= 16,
- * rows % 16 == 0, cols >= 64, cols % 64 == 0 and rows * cols < 2^44;
- * QLORA_ERR_NULL if w is NULL. */
+/* Fill a descriptor's header fields for a [rows, cols] weight in the default
+ * format (host call; pointers are left untouched).  Returns QLORA_ERR_SHAPE
+ * unless rows >= 16, rows % 16 == 0, cols >= 64, cols % 64 == 0 and
+ * rows * cols < 2^44; QLORA_ERR_NULL if w is NULL. */
 qlora_status qlora_nf4_weight_init(qlora_nf4_weight *w, int64_t rows, int64_t cols);
+
+/* The same for a variant: quant_type QLORA_QUANT_*, double_quant 0 or 1,
+ * compute_dtype QLORA_COMPUTE_*.  QLORA_ERR_FORMAT for an unknown value. */
+qlora_status qlora_nf4_weight_init_ex(qlora_nf4_weight *w, int64_t rows, int64_t cols,
+                                      int quant_type, int double_quant, int compute_dtype);
+
+/* Byte sizes of the four device buffers of the weight a descriptor describes
+ * (any format; 0 for a buffer the format does not use).  Any output pointer
+ * may be NULL.  Errors as check of the descriptor's header fields. */
+qlora_status qlora_nf4_weight_buffer_sizes(const qlora_nf4_weight *w, size_t *codes_bytes,
+                                           size_t *absmax_code_bytes,
+                                           size_t *absmax_scale_bytes,
+                                           size_t *absmax_offset_bytes);
 
 /* Byte sizes of the four device buffers of a [rows, cols] weight (host call).
  * Any output pointer may be NULL.  Returns QLORA_ERR_SHAPE on a bad shape. */
@@ -98,7 +138,8 @@ qlora_status qlora_nf4_buffer_sizes(int64_t rows, int64_t cols, size_t *codes_by
                                     size_t *absmax_offset_bytes);
 
 /* Workspace bytes qlora_nf4_quantize needs: the float32 block constants and
- * one float64 partial sum per group (0 on a bad shape). */
+ * one float64 partial sum per group (0 on a bad shape).  A weight without
+ * double quantisation needs none (ws may then be NULL). */
 size_t qlora_nf4_quantize_workspace(int64_t rows, int64_t cols);
 
 /*
@@ -112,13 +153,17 @@ size_t qlora_nf4_quantize_workspace(int64_t rows, int64_t cols);
  * lower index; an all-zero block gets the zero level.  Then mu = mean of all
  * c (fixed pairwise float64 tree), d = RN32(c - mu), s2 = max |d| per group of
  * 256 blocks, code8 = E4M3 round-to-nearest-even of RN32(d / s2) * 256
- * (0x00 when s2 == 0).
+ * (0x00 when s2 == 0).  Without double quantisation c itself is stored.
+ * With quant_type INT4 the levels are the evenly spaced ones.
  */
 qlora_status qlora_nf4_quantize(const float *W, const qlora_nf4_weight *out, void *ws,
                                 size_t ws_bytes, void *stream);
 
 /*
- * Dequantise a packed weight to bf16 [rows, cols] (W_bf16 written).
+ * Dequantise a packed weight to bf16 [rows, cols] (W_bf16 written; fp16 for
+ * a weight whose compute_dtype is QLORA_COMPUTE_FP16): round16(RN32(q[code] *
+ * c)) with c the decoded or, without double quantisation, the stored
+ * constant.
  * (ta-paperlens 量子化を1段落で: restore by lookup and multiply; the bf16
  * values are bit-identical to those the fused linear kernels use.)
  */

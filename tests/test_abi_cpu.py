@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -34,6 +34,7 @@ def test_header_functions_exported_and_bound():
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(_lib.Nf4WeightDesc) == 4 * 4 + 2 * 8 + 4 * 8
     assert _lib.Nf4WeightDesc.codes.offset == 32
+    assert (_lib.Nf4WeightDesc.quant_type.offset, _lib.Nf4WeightDesc.compute_dtype.offset) == (12, 14)
     assert ctypes.sizeof(_lib.DropoutDesc) == 24
     assert (_lib.DropoutDesc.p.offset, _lib.DropoutDesc.seed.offset,
             _lib.DropoutDesc.offset.offset) == (0, 8, 16)
@@ -113,6 +114,60 @@ def test_merge_validation():
     bad = _desc()
     bad.format_version = 2
     assert lib.qlora_nf4_merge(ctypes.byref(bad), FAKE, FAKE, 16, 32.0, FAKE, None) == 7
+
+
+def _desc_ex(rows=1024, cols=1024, qt=0, dq=1, f16=0, code=FAKE, offset=FAKE):
+    lib = _lib.load()
+    d = _lib.Nf4WeightDesc()
+    assert lib.qlora_nf4_weight_init_ex(ctypes.byref(d), rows, cols, qt, dq, f16) == 0
+    d.codes = FAKE
+    d.absmax_code = code
+    d.absmax_scale = FAKE
+    d.absmax_offset = offset
+    return d
+
+
+def test_weight_variant_formats():
+    """Variants: no double quantisation (dq_blocksize 0, float32 constant per
+    block, no code / offset buffers), the INT4 codebook, fp16 compute.
+    Unknown codes are QLORA_ERR_FORMAT; the linear entry points take NF4
+    only; without double quantisation quantise needs no workspace and the
+    8-bit code and mean pointers may be NULL (the calls below then reach the
+    device check, 5 or 6, which no GPU here passes)."""
+    lib = _lib.load()
+    d = _lib.Nf4WeightDesc()
+    for bad in ((2, 1, 0), (-1, 1, 0), (0, 2, 0), (0, 1, 2), (0, 1, -1)):
+        assert lib.qlora_nf4_weight_init_ex(ctypes.byref(d), 1024, 1024, *bad) == 7, bad
+    assert lib.qlora_nf4_weight_init_ex(ctypes.byref(d), 1024, 1024, 1, 0, 1) == 0
+    assert (d.dq_blocksize, d.quant_type, d.compute_dtype) == (0, 1, 1)
+    sizes = [ctypes.c_size_t() for _ in range(4)]
+    assert lib.qlora_nf4_weight_buffer_sizes(ctypes.byref(d), *[ctypes.byref(x) for x in sizes]) == 0
+    n = 1024 * 1024
+    assert [x.value for x in sizes] == [n // 2, 0, 4 * (n // 64), 0]
+    dd = _desc_ex()
+    assert lib.qlora_nf4_weight_buffer_sizes(ctypes.byref(dd), *[ctypes.byref(x) for x in sizes]) == 0
+    assert [x.value for x in sizes] == [n // 2, n // 64, 4 * (n // 64 // 256), 4]
+    for field, val in (("dq_blocksize", 128), ("quant_type", 3), ("compute_dtype", 9)):
+        bad = _desc_ex()
+        setattr(bad, field, val)
+        assert lib.qlora_nf4_dequantize(ctypes.byref(bad), FAKE, None) == 7, field
+        assert lib.qlora_nf4_weight_buffer_sizes(ctypes.byref(bad), None, None, None, None) == 7
+    # double quantisation needs the code and mean buffers; without it they may be NULL
+    assert lib.qlora_nf4_dequantize(ctypes.byref(_desc_ex(code=None)), FAKE, None) == 1
+    assert lib.qlora_nf4_dequantize(ctypes.byref(_desc_ex(dq=0, code=None, offset=None)), FAKE,
+                                    None) in (5, 6)
+    assert lib.qlora_nf4_quantize(FAKE, ctypes.byref(_desc_ex(dq=0, code=None, offset=None)), None,
+                                  0, None) in (5, 6)
+    assert lib.qlora_nf4_quantize(FAKE, ctypes.byref(_desc_ex()), None, 0, None) == 1
+    # INT4: quantise / dequantise / merge, not the linear layer
+    i4 = ctypes.byref(_desc_ex(qt=1))
+    assert lib.qlora_nf4_dequantize(i4, FAKE, None) in (5, 6)
+    assert lib.qlora_nf4_merge(i4, FAKE, FAKE, 16, 32.0, FAKE, None) in (5, 6)
+    ws = lib.qlora_linear_workspace(512, 1024, 1024, 16, 0)
+    assert lib.qlora_linear_fwd(i4, FAKE, 512, FAKE, FAKE, 16, 32.0, FAKE, None, FAKE, ws,
+                                None) == 7
+    assert lib.qlora_linear_fwd(ctypes.byref(_desc_ex(dq=0, f16=1, code=None, offset=None)), FAKE,
+                                512, FAKE, FAKE, 16, 32.0, FAKE, None, FAKE, ws, None) in (5, 6)
 
 
 def test_adamw_validation():

@@ -173,3 +173,19 @@ def test_variant_states_validate():
         O.levels_for("fp4")
     with pytest.raises(ValueError):
         O.round16_bits(np.float32([1.0]), "fp32")
+
+
+def test_int4_zero_threshold_with_denormal_quotients():
+    """The INT4 threshold at 0 sees the quotient's sign and zero-ness: with
+    c = 1, w = +2^-149 gives r = 2^-149 > 0 (code 8) and -2^-149 gives code 7;
+    with c = 4, w = 2^-149 gives r = RN32(2^-151) = 0 (code 7)."""
+    q = O.int4_levels()
+    tiny = np.float32(2.0 ** -149)
+    blk = np.zeros(64, np.float32)
+    blk[0] = 1.0
+    blk[1], blk[2] = tiny, -tiny
+    codes = O.nf4_encode(blk, O.block_absmax(blk), levels=q)
+    assert (codes[1], codes[2]) == (8, 7)
+    blk[0] = 4.0
+    codes = O.nf4_encode(blk, O.block_absmax(blk), levels=q)
+    assert (codes[1], codes[2]) == (7, 7)
