@@ -561,9 +561,9 @@ def adamw_scalars(step: int, lr: float, beta1: float, beta2: float, eps: float,
 
 
 def adamw_step(param, exp_avg, exp_avg_sq, grad, step: int, lr: float, beta1: float,
-               beta2: float, eps: float, weight_decay: float):
+               beta2: float, eps: float, weight_decay: float, copy_dtype: str = "bf16"):
     """One AdamW step on float32 arrays; returns (param, exp_avg, exp_avg_sq,
-    param_bf16_bits).
+    the 16-bit copy's bit patterns: bf16, or fp16 for fp16 compute).
 
     [PL] ページ化オプティマイザ and page 2 26.6.4 (paged_adamw_32bit: Adam's two
     moments per trainable parameter, kept in 32 bit; only the adapters A, B
@@ -574,7 +574,7 @@ def adamw_step(param, exp_avg, exp_avg_sq, grad, step: int, lr: float, beta1: fl
     no fused multiply-add:
       p1 = p * decay;  m1 = b1 m + (1-b1) g;  v1 = b2 v + (1-b2) (g g);
       den = sqrt(v1) / sqrt(bc2) + eps;  p2 = p1 - step_size (m1 / den);
-    the bf16 copy for the next forward is bf16_RNE(p2).
+    the 16-bit copy for the next forward is p2 rounded to nearest even.
     """
     k = adamw_scalars(step, lr, beta1, beta2, eps, weight_decay)
     f32 = np.float32
@@ -589,7 +589,7 @@ def adamw_step(param, exp_avg, exp_avg_sq, grad, step: int, lr: float, beta1: fl
     den = ((np.sqrt(v1).astype(f32) / k["bc2_sqrt"]).astype(f32) + k["eps"]).astype(f32)
     upd = (k["step_size"] * (m1 / den).astype(f32)).astype(f32)
     p2 = (p1 - upd).astype(f32)
-    return p2, m1, v1, bf16_bits_rne(p2)
+    return p2, m1, v1, round16_bits(p2, copy_dtype)
 
 
 # --------------------------------------------------------------------------

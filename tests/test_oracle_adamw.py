@@ -68,3 +68,7 @@ def test_zero_gradient_only_decays_exactly():
     assert np.array_equal(p2, np.array([0.75, -1.5, 0.375, 2.25], np.float32))
     assert not m.any() and not v.any()
     assert np.array_equal(bits, np.array([0x3F40, 0xBFC0, 0x3EC0, 0x4010], np.uint16))
+    # the fp16 copy of the same parameters: 0.75, -1.5, 0.375, 2.25 in binary16
+    _, _, _, bits16 = O.adamw_step(p, np.zeros(4), np.zeros(4), np.zeros(4), 7, 0.5, 0.9, 0.99,
+                                   1e-8, 0.5, copy_dtype="fp16")
+    assert np.array_equal(bits16, np.array([0x3A00, 0xBE00, 0x3600, 0x4080], np.uint16))
