@@ -134,16 +134,19 @@ def profiled_traffic(kernel: str, workload: str, digest: str):
         return None
 
 
-def to_dev_bf16(bits, dev):
+def to_dev_bf16(bits, dev, dtype="bf16"):
+    """16-bit bit patterns to a device tensor of that type (bf16 or fp16)."""
     import numpy as np
     import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+    return t.view(torch.float16 if dtype == "fp16" else torch.bfloat16)
 
 
 class LinearSet:
     """Device-resident inputs, packed weights and outputs of a workload."""
 
-    def __init__(self, wl, dev, tokens=None, backward=True, dropout=None):
+    def __init__(self, wl, dev, tokens=None, backward=True, dropout=None, dtype="bf16",
+                 double_quant=True):
         import torch
 
         import bit_nf4_quantized_06_amd as q
@@ -154,20 +157,21 @@ class LinearSet:
         self.r, self.alpha = wl.rank, wl.alpha
         self.items = []
         for li, lin in enumerate(wl.linears):
-            inp = WL.linear_inputs(wl, li, tokens=self.T)
-            wq = q.qlora_nf4_quantize(torch.from_numpy(inp["w"]).to(dev))
-            it = {"lin": lin, "wq": wq, "X": to_dev_bf16(inp["x"], dev),
-                  "A": to_dev_bf16(inp["a"], dev), "B": to_dev_bf16(inp["b"], dev)}
+            inp = WL.linear_inputs(wl, li, tokens=self.T, dtype=dtype)
+            wq = q.qlora_nf4_quantize(torch.from_numpy(inp["w"]).to(dev),
+                                      double_quant=double_quant, compute_dtype=dtype)
+            it = {"lin": lin, "wq": wq, "X": to_dev_bf16(inp["x"], dev, dtype),
+                  "A": to_dev_bf16(inp["a"], dev, dtype), "B": to_dev_bf16(inp["b"], dev, dtype)}
             n, k, r, t = lin.out_features, lin.in_features, self.r, self.T
-            it["Y"] = torch.empty(t, n, dtype=torch.bfloat16, device=dev)
-            it["U"] = torch.empty(t, r, dtype=torch.bfloat16, device=dev)
+            it["Y"] = torch.empty(t, n, dtype=wq.dtype16, device=dev)
+            it["U"] = torch.empty(t, r, dtype=wq.dtype16, device=dev)
             wsz = q.qlora_linear_workspace if dropout is None else q.qlora_linear_workspace_dropout
             it["wsf"] = torch.empty(wsz(t, n, k, r, False), dtype=torch.uint8, device=dev)
             if dropout is not None:
                 it["keep"] = torch.empty((t + 3) // 4, k // 2, dtype=torch.uint8, device=dev)
             if backward and "dy" in inp:
-                it["dY"] = to_dev_bf16(inp["dy"], dev)
-                it["dX"] = torch.empty(t, k, dtype=torch.bfloat16, device=dev)
+                it["dY"] = to_dev_bf16(inp["dy"], dev, dtype)
+                it["dX"] = torch.empty(t, k, dtype=wq.dtype16, device=dev)
                 it["dA"] = torch.empty(r, k, dtype=torch.float32, device=dev)
                 it["dB"] = torch.empty(n, r, dtype=torch.float32, device=dev)
                 it["wsb"] = torch.empty(wsz(t, n, k, r, True), dtype=torch.uint8, device=dev)
@@ -396,6 +400,66 @@ def time_dropout(ev, dev, steps, warmup, reps, p):
     }
 
 
+def time_variants(ev, dev, steps, warmup, reps):
+    """The storage and compute variants: the headline step with fp16 compute
+    and with float32 block constants (no double quantisation), and quantize /
+    dequantize of the bulk weight in the other formats."""
+    import torch
+
+    import bit_nf4_quantized_06_amd as q
+    import workloads as WL
+    from bit_nf4_quantized_06_amd import _lib
+    lib = _lib.load()
+    res = {}
+    wl = WL.WORKLOADS[HEADLINE]
+    for name, dt, dq in (("fp16", "fp16", True), ("bf16_no_double_quant", "bf16", False)):
+        ls = LinearSet(wl, dev, dtype=dt, double_quant=dq)
+        tm = time_steps(ls, ev, steps, warmup, kernel_timing=False)
+        fl = ls.flops()
+        res[f"{HEADLINE}_{name}"] = {"ms_per_step": round(tm["ms_per_step"], 4),
+                                      "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2)}
+        del ls
+        torch.cuda.empty_cache()
+    lin = WL.WORKLOADS[BULK].linears[0]
+    rows, cols = lin.out_features, lin.in_features
+    w = torch.from_numpy(WL.linear_inputs(WL.WORKLOADS[BULK], 0)["w"]).to(dev)
+    n = rows * cols
+    ws = torch.empty(lib.qlora_nf4_quantize_workspace(rows, cols), dtype=torch.uint8, device=dev)
+    for name, qt, dq, dt in (("nf4_no_double_quant", "nf4", False, "bf16"),
+                             ("int4", "int4", True, "bf16"), ("nf4_fp16", "nf4", True, "fp16")):
+        wq = q.NF4Weight.empty(rows, cols, dev, qt, dq, dt)
+        deq = torch.empty(rows, cols, dtype=wq.dtype16, device=dev)
+        for _ in range(2):
+            q.qlora_nf4_quantize(w, out=wq, workspace=ws)
+            q.qlora_nf4_dequantize(wq, out=deq)
+        torch.cuda.synchronize()
+        qp, dp = [], []
+        for _ in range(reps):
+            a, b = (ev.new(), ev.new()), (ev.new(), ev.new())
+            lib.qlora_set_timing_events(2, a[0], a[1])
+            lib.qlora_set_timing_events(3, b[0], b[1])
+            q.qlora_nf4_quantize(w, out=wq, workspace=ws)
+            q.qlora_nf4_dequantize(wq, out=deq)
+            qp.append(a)
+            dp.append(b)
+        torch.cuda.synchronize()
+        for g in (2, 3):
+            lib.qlora_set_timing_events(g, None, None)
+        q_ms = sum(ev.ms(x, y) for x, y in qp) / reps
+        d_ms = sum(ev.ms(x, y) for x, y in dp) / reps
+        packed = packed_bytes(n) if dq else n // 2 + 4 * (n // 64)
+        qb, db = 4 * n + packed, packed + 2 * n
+        res[f"bulk_{name}"] = {
+            "quantize_ms": round(q_ms, 4), "quantize_GBps": round(qb / q_ms / 1e6, 1),
+            "quantize_hbm_frac": round(qb / q_ms / 1e6 / PEAK_HBM_GBPS, 4),
+            "dequant_ms": round(d_ms, 4), "dequant_GBps": round(db / d_ms / 1e6, 1),
+            "dequant_hbm_frac": round(db / d_ms / 1e6 / PEAK_HBM_GBPS, 4)}
+        del wq, deq
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration():
     """A plain device-to-device copy of a known size: its FETCH_SIZE and
     WRITE_SIZE counters give the scale between counter units and bytes."""
@@ -503,6 +567,8 @@ def main():
     dropout = time_dropout(ev, dev, max(5, args.steps // 2), args.warmup, args.bulk_reps,
                            DROPOUT_P)
     torch.cuda.empty_cache()
+    print("[bench] timing the storage and compute variants", file=sys.stderr, flush=True)
+    variants = time_variants(ev, dev, max(5, args.steps // 2), args.warmup, args.bulk_reps)
 
     extended = None
     if args.extended:
@@ -561,6 +627,7 @@ def main():
         "bulk": bulk,
         "adamw": adamw,
         "dropout": dropout,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     if extended is not None:

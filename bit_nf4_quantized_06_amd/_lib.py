@@ -66,6 +66,9 @@ SIGNATURES = {
     "qlora_adamw_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_double,
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_double, _P]),
+    "qlora_adamw_step16": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64,
+                                          ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                          ctypes.c_double, ctypes.c_double, _P]),
     "qlora_linear_workspace": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_int]),
     "qlora_linear_fwd": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P,
                                         _P, _SZ, _P]),

@@ -180,6 +180,29 @@ def qlora_adamw_step(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: tor
                                     float(eps), float(weight_decay), _stream(stream)))
 
 
+def qlora_adamw_step16(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                       grad: torch.Tensor, step: int, lr: float, param16: torch.Tensor,
+                       beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                       weight_decay: float = 0.0, stream=None) -> None:
+    """qlora_adamw_step16: the AdamW step with the 16-bit copy written in
+    param16's dtype (torch.bfloat16 or torch.float16, the compute dtype)."""
+    lib = _lib.load()
+    n = param.numel()
+    dev = param.device
+    for t, name in ((param, "param"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"),
+                    (grad, "grad")):
+        _need(t, name, torch.float32, tuple(param.shape), dev)
+    if param16.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"param16: expected bfloat16 or float16, got {param16.dtype}")
+    _need(param16, "param16", param16.dtype, tuple(param.shape), dev)
+    cd = _lib.COMPUTE_DTYPES["fp16" if param16.dtype == torch.float16 else "bf16"]
+    _lib.check("qlora_adamw_step16",
+               lib.qlora_adamw_step16(param.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(),
+                                      grad.data_ptr(), param16.data_ptr(), cd, int(n), int(step),
+                                      float(lr), float(beta1), float(beta2), float(eps),
+                                      float(weight_decay), _stream(stream)))
+
+
 def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 

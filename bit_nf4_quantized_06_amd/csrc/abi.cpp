@@ -284,7 +284,18 @@ qlora_status qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq,
                               const float* grad, uint16_t* param_bf16, int64_t n, int64_t step,
                               double lr, double beta1, double beta2, double eps,
                               double weight_decay, void* stream) {
+  return qlora_adamw_step16(param, exp_avg, exp_avg_sq, grad, param_bf16, QLORA_COMPUTE_BF16, n,
+                            step, lr, beta1, beta2, eps, weight_decay, stream);
+}
+
+qlora_status qlora_adamw_step16(float* param, float* exp_avg, float* exp_avg_sq,
+                                const float* grad, uint16_t* param16, int compute_dtype,
+                                int64_t n, int64_t step, double lr, double beta1, double beta2,
+                                double eps, double weight_decay, void* stream) {
   using namespace qlora;
+  uint16_t* param_bf16 = param16;
+  if (compute_dtype != QLORA_COMPUTE_BF16 && compute_dtype != QLORA_COMPUTE_FP16)
+    return QLORA_ERR_FORMAT;
   if (!param || !exp_avg || !exp_avg_sq || !grad) return QLORA_ERR_NULL;
   if (!aligned16(param) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
       (param_bf16 && !aligned16(param_bf16)))
@@ -301,6 +312,7 @@ qlora_status qlora_adamw_step(float* param, float* exp_avg, float* exp_avg_sq,
   a.v = exp_avg_sq;
   a.g = grad;
   a.p_bf16 = param_bf16;
+  a.f16 = compute_dtype == QLORA_COMPUTE_FP16;
   a.n = n;
   a.decay = k.decay;
   a.b1 = k.b1;

@@ -4,6 +4,7 @@
 //   p1 = p * decay;  m1 = b1 m + (1-b1) g;  v1 = b2 v + (1-b2) (g g);
 //   p2 = p1 - step_size * (m1 / (sqrt(v1) / sqrt(bc2) + eps))
 //
+// (the copy is fp16 for fp16 compute, ta-paperlens 落とし穴)
 // (ta-paperlens ページ化オプティマイザ and waylandz 26.6.4: Adam's two moments
 // per trainable parameter are kept in 32 bit, and only A and B have them;
 // Adam with decoupled weight decay, bias-corrected, in the form PyTorch's
@@ -72,7 +73,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwArgs a) {
     reinterpret_cast<f32x4_t*>(a.m)[i] = m;
     reinterpret_cast<f32x4_t*>(a.v)[i] = v;
     if (a.p_bf16)
-      reinterpret_cast<uint2*>(a.p_bf16)[i] = uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      reinterpret_cast<uint2*>(a.p_bf16)[i] =
+          a.f16 ? uint2{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])}
+                : uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
   }
   if (blockIdx.x == 0 && threadIdx.x < (a.n & 3)) {
     const int64_t j = 4 * n4 + threadIdx.x;
@@ -81,7 +84,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwArgs a) {
     a.p[j] = pe;
     a.m[j] = me;
     a.v[j] = ve;
-    if (a.p_bf16) a.p_bf16[j] = (uint16_t)(pack_bf16x2(pe, 0.0f) & 0xFFFFu);
+    if (a.p_bf16)
+      a.p_bf16[j] = (uint16_t)((a.f16 ? pack_f16x2(pe, 0.0f) : pack_bf16x2(pe, 0.0f)) & 0xFFFFu);
   }
 }
 

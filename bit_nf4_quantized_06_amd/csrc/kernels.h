@@ -90,7 +90,8 @@ struct AdamwArgs {
   float* m;
   float* v;
   const float* g;
-  uint16_t* p_bf16;         // may be NULL
+  uint16_t* p_bf16;         // 16-bit copy (bf16, or fp16 with f16), may be NULL
+  bool f16;
   int64_t n;
   float decay, b1, omb1, b2, omb2, step_size, bc2_sqrt, eps;
 };

@@ -15,7 +15,10 @@
  *     returns without synchronising.
  *   - The caller allocates and owns all memory, including workspaces.  The
  *     library never allocates, frees or keeps a pointer after returning.
- *   - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - 16-bit tensors are passed as uint16_t bit patterns, row-major.  They
+ *     are bf16 unless the weight they go with has compute_dtype
+ *     QLORA_COMPUTE_FP16, in which case every "bf16" below reads "fp16"
+ *     (IEEE binary16) and every rounding to it is to nearest even.
  *   - Arguments are validated on the host before anything is launched; on a
  *     non-OK status nothing has been enqueued.  Errors of already enqueued
  *     kernels surface at the caller's next synchronisation.
@@ -215,6 +218,15 @@ qlora_status qlora_adamw_step(float *param, float *exp_avg, float *exp_avg_sq,
                               const float *grad, uint16_t *param_bf16, int64_t n, int64_t step,
                               double lr, double beta1, double beta2, double eps,
                               double weight_decay, void *stream);
+
+/* The same step with the 16-bit copy in the compute dtype of the weights the
+ * adapters serve: compute_dtype QLORA_COMPUTE_BF16 (as qlora_adamw_step) or
+ * QLORA_COMPUTE_FP16 (param16 then receives binary16, nearest even;
+ * ta-paperlens 落とし穴).  QLORA_ERR_FORMAT for another compute_dtype. */
+qlora_status qlora_adamw_step16(float *param, float *exp_avg, float *exp_avg_sq,
+                                const float *grad, uint16_t *param16, int compute_dtype,
+                                int64_t n, int64_t step, double lr, double beta1, double beta2,
+                                double eps, double weight_decay, void *stream);
 
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
  * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args). */

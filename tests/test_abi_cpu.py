@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -182,6 +182,10 @@ def test_adamw_validation():
                                     a["b2"], a["eps"], a["wd"], None)
     assert call(p=None) == 1 and call(m=None) == 1 and call(v=None) == 1 and call(g=None) == 1
     assert call(p=MISALIGNED) == 3 and call(g=MISALIGNED) == 3 and call(pb=MISALIGNED) == 3
+    assert lib.qlora_adamw_step16(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1024, 1, 1e-3, 0.9, 0.999,
+                                  1e-8, 0.0, None) == 7          # unknown compute dtype
+    assert lib.qlora_adamw_step16(FAKE, FAKE, FAKE, FAKE, MISALIGNED, 1, 1024, 1, 1e-3, 0.9,
+                                  0.999, 1e-8, 0.0, None) == 3
     for bad in (dict(n=0), dict(step=0), dict(lr=-1e-3), dict(eps=0.0), dict(eps=-1.0),
                 dict(wd=-0.1), dict(b1=1.0), dict(b2=-0.1), dict(lr=float("nan")),
                 dict(b1=float("inf"))):

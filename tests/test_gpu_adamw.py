@@ -51,3 +51,27 @@ def test_adamw_7b_block_adapters():
     n = sum(wl.rank * (lin.in_features + lin.out_features) for lin in wl.linears)
     print(f"[adamw] 7B block adapters n={n}", flush=True)
     _run(n, steps=2, wd=0.01, with_bf16=True, seed=7)
+
+
+@pytest.mark.parametrize("n", [4099, 257])
+def test_adamw_fp16_copy_bit_exact(n):
+    """qlora_adamw_step16 with an fp16 copy (fp16 compute): parameters,
+    moments and the binary16 copy equal the oracle's bit for bit."""
+    import bit_nf4_quantized_06_amd as q
+    print(f"[adamw] fp16 copy n={n}", flush=True)
+    rng = np.random.default_rng(n + 1)
+    p = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    tp, tm, tv = (torch.from_numpy(x.copy()).to(dev()) for x in (p, m, v))
+    t16 = torch.empty(n, dtype=torch.float16, device=dev())
+    for step in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        q.qlora_adamw_step16(tp, tm, tv, torch.from_numpy(g).to(dev()), step, HP["lr"], t16,
+                             beta1=HP["beta1"], beta2=HP["beta2"], eps=HP["eps"],
+                             weight_decay=0.01)
+        p, m, v, bits = O.adamw_step(p, m, v, g, step, HP["lr"], HP["beta1"], HP["beta2"],
+                                     HP["eps"], 0.01, copy_dtype="fp16")
+        torch.cuda.synchronize()
+        assert np.array_equal(tp.cpu().numpy().view(np.uint32), p.view(np.uint32)), step
+        assert np.array_equal(bits_host(t16), bits), step
