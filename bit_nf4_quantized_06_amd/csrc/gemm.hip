@@ -556,20 +556,49 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   if (step + 3 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
   if (step + 4 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
 
-  // ---- epilogue: round to bf16 and store ------------------------------------
+  // ---- epilogue: round to 16 bit, stage the wave's 128 x 64 tile in LDS and
+  // write whole 128-byte rows with 16-byte stores (16 stores per lane instead
+  // of 128 two-byte ones; all workgroups reach this point together, so the
+  // 33.5 MB of a 4096 x 4096 output drain as one tail).  The stages are free
+  // once every DMA into them has landed, including the zero-filling ones
+  // issued past the last step.  Wave w owns half (w % 2) of stage w / 2;
+  // rows are 64 elements, their 8-column chunks XOR-swizzled by (row / 4) % 8
+  // so that the two rows one write instruction touches fall in different
+  // banks and each row still reads as 8 distinct 16-byte chunks.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    uint16_t* stg = (c.wave >> 1) == 0 ? sa0 : (c.wave >> 1) == 1 ? sa1
+                  : (c.wave >> 1) == 2 ? sa2 : sb0;
+    stg += (c.wave & 1) * 8192;
+    // the lane index re-derived behind an opaque copy, so that no address of
+    // this epilogue is computed early and held live across the main loop
+    int el = c.lane;
+    asm volatile("" : "+v"(el));
+    const int el32 = el & 31, elhi = el >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + col0 + 32 * j + l32;
-      if (col < out_len) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int64_t row = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * lhi + (e & 3);
-          if (row < g.T)
-            g.out[row * out_len + col] = (uint16_t)(pack16x2<kF16>(acc[i][j][e], 0.0f) & 0xFFFFu);
+          const int lr = 32 * i + 8 * (e >> 2) + 4 * elhi + (e & 3);
+          const int lc = 32 * j + el32;
+          stg[lr * 64 + ((((lc >> 3) ^ ((lr >> 2) & 7)) << 3) | (lc & 7))] =
+              (uint16_t)(pack16x2<kF16>(acc[i][j][e], 0.0f) & 0xFFFFu);
         }
-      }
+    // the wave reads back only what it wrote (LDS operations of one wave
+    // complete in order): no barrier
+    const int ch = el & 7;
+    const int64_t gcol = n0 + col0 + 8 * ch;   // out_len % 16 == 0: a chunk is all in or out
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 8 * it + (el >> 3);
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(stg + row * 64 + ((ch ^ ((row >> 2) & 7)) << 3));
+      const int64_t grow = m0 + 128 * wm + row;
+      if (grow < g.T && gcol < out_len)
+        *reinterpret_cast<u32x4_t*>(g.out + grow * out_len + gcol) = v;
     }
   }
 #endif
