@@ -15,6 +15,8 @@
 
 namespace qlora {
 
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
 // Quantise: one workgroup per group of 256 blocks (16384 weights, 64 KB of
 // float32).  A wave owns 64 consecutive blocks; per iteration 8 lanes share a
@@ -152,87 +154,135 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
 // ---------------------------------------------------------------------------
 // Mean of the block constants: perfect binary float64 tree over the group
 // partials (which are its level-8 nodes), zero-padded to a power of two.
-// One workgroup of 1024 threads; thread t first folds an aligned run of
-// `per` leaves (same tree), then the 1024 run sums are folded pairwise.
+// One workgroup of 16 waves.  A wave load takes 128 consecutive leaves
+// (16 bytes per lane, 1 KB contiguous); the lane adds its pair and five
+// shuffle levels fold the 64 pair sums, so lane 0 holds that 128-leaf
+// subtree.  Wave w owns an aligned run of R = max(S / 16, 1) such subtrees
+// (S = subtrees in the padded tree), folded 8 at a time and then like a
+// binary counter; the 16 run sums are folded last.  Every step adds the two
+// children of one node of the same tree.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void dq_mean_kernel(const double* __restrict__ gpart,
-                                                       int64_t n_g, int64_t n_b, int64_t per,
-                                                       float* __restrict__ mu_out) {
-  __shared__ double sh[16];
-  const int t = threadIdx.x;
-  // The run's leaves are read 16 at a time and folded as a perfect tree
-  // (zero padding beyond `per` only adds +0 to a subtree that is already
-  // complete, `per` being a power of two); runs longer than 16 combine the
-  // 16-leaf sums with a binary-counter cascade, which continues the same tree.
-  double stack[40];
-  int sp = 0;
-  for (int64_t i0 = 0; i0 < per; i0 += 16) {
-    double v[16];
+// R / 8 < 2^16 (n < 2^44 weights): at most 17 levels of pending subtrees.
+constexpr int kMeanLevels = 17;
+constexpr int kMeanChunk = 8;   // 128-leaf subtrees per load batch
+constexpr int kEncGroupsPerWave = 2;
+
+__device__ __forceinline__ double mean_tree_run(const double* __restrict__ gpart, int64_t n_g,
+                                                int64_t R, int wave, int lane) {
+  // pending[l]: sum of the last complete subtree of kMeanChunk * 2^l
+  // 128-leaf subtrees still waiting for its right sibling (lane 0's value
+  // is the one that counts; the levels are unrolled selects, so every index
+  // is a constant and the pending sums stay in registers)
+  double pending[kMeanLevels];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t idx = (int64_t)t * per + i0 + j;
-      v[j] = (i0 + j < per && idx < n_g) ? gpart[idx] : 0.0;
+  for (int l = 0; l < kMeanLevels; ++l) pending[l] = 0.0;
+  double run = 0.0;
+  const int64_t s0 = (int64_t)wave * R;   // first subtree of this wave's run
+  for (int64_t i0 = 0; i0 < R; i0 += kMeanChunk) {
+    double v[kMeanChunk];
+#pragma unroll
+    for (int j = 0; j < kMeanChunk; ++j) {
+      const int64_t idx = (s0 + i0 + j) * 128 + 2 * lane;
+      double lo = 0.0, hi = 0.0;
+      if (i0 + j < R) {
+        if (idx + 1 < n_g) {
+          const f64x2_t x = *reinterpret_cast<const f64x2_t*>(gpart + idx);
+          lo = x[0];
+          hi = x[1];
+        } else if (idx < n_g) {
+          lo = gpart[idx];
+        }
+      }
+      v[j] = lo + hi;
     }
 #pragma unroll
-    for (int w = 1; w < 16; w <<= 1)
+    for (int j = 0; j < kMeanChunk; ++j)
 #pragma unroll
-      for (int j = 0; j < 16; j += 2 * w) v[j] = v[j] + v[j + w];
+      for (int d = 1; d < 64; d <<= 1) v[j] += __shfl_down(v[j], d);
+#pragma unroll
+    for (int w = 1; w < kMeanChunk; w <<= 1)
+#pragma unroll
+      for (int j = 0; j < kMeanChunk; j += 2 * w) v[j] = v[j] + v[j + w];
     double acc = v[0];
-    for (int64_t k = i0 >> 4; k & 1; k >>= 1) acc = stack[--sp] + acc;
-    stack[sp++] = acc;
-  }
-  // the 1024 run sums: a tree over each wave's 64 (shuffles), then over the
-  // 16 wave sums -- the same perfect tree
-  double v = stack[0];
+    const int64_t k = i0 / kMeanChunk;   // chunk index inside the run
+    // the carry runs up through the set low bits of k, merging each pending
+    // left sibling, and parks the sum at the first clear bit
+    bool carry = true;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v += __shfl_down(v, d);
-  if ((t & 63) == 0) sh[t >> 6] = v;
+    for (int l = 0; l < kMeanLevels; ++l) {
+      const bool bit = (k >> l) & 1;
+      const double merged = pending[l] + acc;
+      pending[l] = (carry && !bit) ? acc : pending[l];
+      acc = (carry && bit) ? merged : acc;
+      carry = carry && bit;
+    }
+    run = acc;   // after the last chunk (all bits of k set): the run's sum
+  }
+  return run;
+}
+
+__global__ __launch_bounds__(1024) void dq_mean_kernel(const double* __restrict__ gpart,
+                                                       int64_t n_g, int64_t n_b, int64_t R,
+                                                       float* __restrict__ mu_out) {
+  __shared__ double sh[16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const double run = mean_tree_run(gpart, n_g, R, wave, lane);
+  if (lane == 0) sh[wave] = run;
   __syncthreads();
-  if (t < 64) {
-    double u = t < 16 ? sh[t] : 0.0;
+  if (threadIdx.x < 64) {
+    double u = lane < 16 ? sh[lane] : 0.0;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) u += __shfl_down(u, d);
-    if (t == 0) mu_out[0] = (float)(u / (double)n_b);
+    if (lane == 0) mu_out[0] = (float)(u / (double)n_b);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Double-quantisation codes: one workgroup (256 threads) per 4 groups; thread
-// t handles block t of each.  d = RN32(c - mu); s2 = max |d| over the group;
-// code8 = E4M3_RNE(RN32(d / s2) * 256).
+// Double-quantisation codes: one wave per group of 256 blocks, lane l holds
+// blocks 4l .. 4l + 3 of it (one 16-byte load, one 4-byte store of codes);
+// each wave takes two groups, both loaded before either is encoded.
+// d = RN32(c - mu); s2 = max |d| over the group; code8 = E4M3_RNE(RN32(d / s2)
+// * 256).  n_b is a multiple of 16, so a lane's 4 blocks are all in or out.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ cblk,
                                                         const float* __restrict__ mu_p,
-                                                        int64_t n_b, uint8_t* __restrict__ code8,
+                                                        int64_t n_b, int64_t n_g,
+                                                        uint32_t* __restrict__ code8,
                                                         float* __restrict__ s2_out) {
-  __shared__ float wmax[4][4];
-  const int t = threadIdx.x;
-  const int64_t g0 = (int64_t)blockIdx.x * 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const float mu = mu_p[0];
-  float d[4];
+  f32x4_t c[kEncGroupsPerWave];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t b = (g0 + k) * kGroup + t;
-    d[k] = b < n_b ? __fsub_rn(cblk[b], mu) : 0.0f;
+  for (int k = 0; k < kEncGroupsPerWave; ++k) {
+    const int64_t b0 = (wave * kEncGroupsPerWave + k) * kGroup + 4 * lane;
+    c[k] = b0 < n_b ? *reinterpret_cast<const f32x4_t*>(cblk + b0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float a = fabsf(d[k]);
+  for (int k = 0; k < kEncGroupsPerWave; ++k) {
+    const int64_t g = wave * kEncGroupsPerWave + k;
+    const int64_t b0 = g * kGroup + 4 * lane;
+    const bool valid = b0 < n_b;
+    float d[4];
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d[e] = valid ? __fsub_rn(c[k][e], mu) : 0.0f;
+      a = fmaxf(a, fabsf(d[e]));
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-    if ((t & 63) == 0) wmax[k][t >> 6] = a;
-  }
-  __syncthreads();
+    const float s2 = a;
+    if (lane == 0 && g < n_g) s2_out[g] = s2;
+    if (valid) {
+      uint32_t word = 0u;
+      if (s2 > 0.0f) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t g = g0 + k;
-    const int64_t b = g * kGroup + t;
-    const float s2 = fmaxf(fmaxf(wmax[k][0], wmax[k][1]), fmaxf(wmax[k][2], wmax[k][3]));
-    if (t == 0 && g * kGroup < n_b) s2_out[g] = s2;
-    if (b < n_b) {
-      uint32_t code = 0u;
-      if (s2 > 0.0f) code = e4m3_encode_rne(__fdiv_rn(d[k], s2) * 256.0f);
-      code8[b] = (uint8_t)code;
+        for (int e = 0; e < 4; ++e)
+          word |= e4m3_encode_rne(__fdiv_rn(d[e], s2) * 256.0f) << (8 * e);
+      }
+      code8[b0 >> 2] = word;
     }
   }
 }
@@ -310,10 +360,12 @@ hipError_t launch_quantize(const float* W, int64_t n_b, uint8_t* codes, uint8_t*
                        stream, W, n_b, cw, cblk, gpart);
   int64_t pow2 = 1;
   while (pow2 < n_g) pow2 <<= 1;
-  const int64_t per = pow2 > 1024 ? pow2 / 1024 : 1;
-  hipLaunchKernelGGL(dq_mean_kernel, dim3(1), dim3(1024), 0, stream, gpart, n_g, n_b, per, mu);
-  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((n_g + 3) / 4)), dim3(256), 0, stream, cblk,
-                     mu, n_b, code8, s2);
+  const int64_t subtrees = pow2 > 128 ? pow2 / 128 : 1;
+  const int64_t run = subtrees > 16 ? subtrees / 16 : 1;
+  hipLaunchKernelGGL(dq_mean_kernel, dim3(1), dim3(1024), 0, stream, gpart, n_g, n_b, run, mu);
+  const int64_t enc_waves = (n_g + kEncGroupsPerWave - 1) / kEncGroupsPerWave;
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((enc_waves + 3) / 4)), dim3(256), 0, stream,
+                     cblk, mu, n_b, n_g, reinterpret_cast<uint32_t*>(code8), s2);
   return hipGetLastError();
 }
 
