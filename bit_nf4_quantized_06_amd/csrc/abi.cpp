@@ -326,6 +326,28 @@ qlora_status qlora_adamw_step16(float* param, float* exp_avg, float* exp_avg_sq,
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
+namespace qlora {
+namespace {
+
+// T = 0, an empty token batch: nothing is read; the forward writes nothing,
+// the backward writes dA = 0 and dB = 0 (sums over no tokens).  Only the
+// adapter and gradient pointers are checked; activation pointers and the
+// workspace may be NULL.
+qlora_status empty_batch(const WeightDims& d, int32_t r, const uint16_t* A, const uint16_t* B,
+                         float* dA, float* dB, bool bwd, hipStream_t st) {
+  if (!A || !B || (bwd && (!dA || !dB))) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || (bwd && (!aligned16(dA) || !aligned16(dB))))
+    return QLORA_ERR_ALIGN;
+  const qlora_status s = check_device();
+  if (s != QLORA_OK || !bwd) return s;
+  hipError_t e = launch_zero_f32(dA, (int64_t)r * d.cols, st);
+  if (e == hipSuccess) e = launch_zero_f32(dB, d.rows * (int64_t)r, st);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+}  // namespace
+}  // namespace qlora
+
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
                               const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                               uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
@@ -334,6 +356,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
   if (s != QLORA_OK) return s;
+  if (T == 0)
+    return empty_batch(d, r, A, B, nullptr, nullptr, false, static_cast<hipStream_t>(stream));
   if (!X || !A || !B || !Y || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
       (U_save && !aligned16(U_save)))
@@ -384,6 +408,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
   if (s != QLORA_OK) return s;
+  if (T == 0) return empty_batch(d, r, A, B, dA, dB, true, static_cast<hipStream_t>(stream));
   if (!X || !dY || !A || !B || !dX || !dA || !dB || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
       !aligned16(dA) || !aligned16(dB) || !aligned16(ws) || (U_saved && !aligned16(U_saved)))
@@ -406,6 +431,7 @@ qlora_status qlora_dropout_mask(const qlora_dropout* dp, int64_t T, int64_t cols
   qlora_status s = dropout_consts(dp, &k);
   if (s != QLORA_OK) return s;
   if (!dropout_dims_ok(T, cols)) return QLORA_ERR_SHAPE;
+  if (T == 0) return QLORA_OK;   // an empty mask
   if (!keep || (X == nullptr) != (X_dropped == nullptr)) return QLORA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(keep) & 3u) != 0 || (X && !aligned16(X)) ||
       (X_dropped && !aligned16(X_dropped)))
@@ -429,6 +455,8 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   DropoutConsts k;
   s = dropout_consts(dp, &k);
   if (s != QLORA_OK) return s;
+  if (T == 0)
+    return empty_batch(d, r, A, B, nullptr, nullptr, false, static_cast<hipStream_t>(stream));
   if (!X || !A || !B || !Y || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
       (U_save && !aligned16(U_save)) || (keep_save && !aligned16(keep_save)))
@@ -460,6 +488,7 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   DropoutConsts k;
   s = dropout_consts(dp, &k);
   if (s != QLORA_OK) return s;
+  if (T == 0) return empty_batch(d, r, A, B, dA, dB, true, static_cast<hipStream_t>(stream));
   if (!X || !dY || !A || !B || !dX || !dA || !dB || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
       !aligned16(dA) || !aligned16(dB) || !aligned16(ws) || (U_saved && !aligned16(U_saved)) ||

@@ -179,4 +179,7 @@ hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int spl
 hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
                                    hipStream_t stream);
 
+// n float32 zeros at p (n % 4 == 0, p 16-byte aligned).
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+
 }  // namespace qlora

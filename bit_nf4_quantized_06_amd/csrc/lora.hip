@@ -624,4 +624,23 @@ hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float s
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// n float32 zeros (n % 4 == 0, 16-byte aligned): the adapter gradients of an
+// empty token batch, written by a kernel rather than a memset so that a
+// captured graph holds no memset node.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_f32_kernel(f32x4_t* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = (n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<f32x4_t*>(p), n4);
+  return hipGetLastError();
+}
+
 }  // namespace qlora

@@ -69,7 +69,7 @@ qlora_status check_weight_shape(int64_t rows, int64_t cols, WeightDims* d) {
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols) {
   const int64_t kMaxDim = int64_t(1) << 22;
   const int64_t kMaxElems16 = (int64_t(1) << 30) - 64;   // bf16 elements below 2 GiB
-  if (T < 1 || rows > kMaxDim || cols > kMaxDim) return false;
+  if (T < 0 || rows > kMaxDim || cols > kMaxDim) return false;   // T = 0: an empty batch
   if (rows * cols > 2 * kMaxElems16) return false;      // packed codes below 2 GiB
   if (T > kMaxElems16 / cols || T > kMaxElems16 / rows) return false;
   return true;
@@ -77,7 +77,7 @@ bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols) {
 
 bool dropout_dims_ok(int64_t T, int64_t cols) {
   const int64_t kMaxElems16 = (int64_t(1) << 30) - 64;
-  if (T < 1 || cols < 64 || (cols % 64) != 0 || cols > (int64_t(1) << 22)) return false;
+  if (T < 0 || cols < 64 || (cols % 64) != 0 || cols > (int64_t(1) << 22)) return false;
   return T <= kMaxElems16 / cols;
 }
 
@@ -214,7 +214,7 @@ qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, 
   const qlora_status s = check_descriptor(w, d);
   if (s != QLORA_OK) return s;
   if (d->qt != QLORA_QUANT_NF4) return QLORA_ERR_FORMAT;   // linear kernels: NF4 levels
-  if (T < 1 || !linear_dims_ok(T, d->rows, d->cols)) return QLORA_ERR_SHAPE;
+  if (!linear_dims_ok(T, d->rows, d->cols)) return QLORA_ERR_SHAPE;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_SHAPE;
   return QLORA_OK;
@@ -295,6 +295,7 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
   if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
   if (!qlora::linear_dims_ok(T, rows, cols)) return 0;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
+  if (T == 0) return 0;   // an empty batch uses no workspace
   return qlora::linear_ws_layout(T, d, r, is_bwd != 0).total;
 }
 
@@ -309,6 +310,7 @@ size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int
   if (qlora::check_weight_shape(rows, cols, &d) != QLORA_OK) return 0;
   if (!qlora::linear_dims_ok(T, rows, cols)) return 0;
   if (r < 16 || r > QLORA_MAX_RANK || (r % 16) != 0) return 0;
+  if (T == 0) return 0;   // an empty batch uses no workspace
   return qlora::linear_ws_layout(T, d, r, is_bwd != 0, true).total;
 }
 

@@ -229,7 +229,8 @@ qlora_status qlora_adamw_step16(float *param, float *exp_avg, float *exp_avg_sq,
                                 double eps, double weight_decay, void *stream);
 
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
- * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args). */
+ * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args;
+ * also 0 for T = 0, which needs no workspace). */
 size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd);
 
 /*
@@ -240,9 +241,10 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
  *   X      [T, cols] bf16        A [r, cols] bf16        B [rows, r] bf16
  *   Y      [T, rows] bf16 (written)
  *   U_save [T, r] bf16 (written; X A^T for the backward) or NULL
- * T >= 1, r % 16 == 0, 16 <= r <= 128; T * rows and T * cols below 2^30,
+ * T >= 0, r % 16 == 0, 16 <= r <= 128; T * rows and T * cols below 2^30,
  * rows * cols below 2^32, rows and cols at most 2^22 (QLORA_ERR_SHAPE
- * otherwise).  Accumulation is float32 on bf16 MFMA; the packed weight is
+ * otherwise).  T = 0 (an empty batch) writes nothing; X, Y, U_save and ws
+ * may then be NULL.  Accumulation is float32 on bf16 MFMA; the packed weight is
  * only read.  For T <= 64 (generation-sized batches, ta-paperlens 落とし穴)
  * the call takes the skinny path, which streams the packed weight once and
  * forms X A^T in the same pass; the workspace size reflects the path.
@@ -261,7 +263,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
  *   dA = s G^T X                            [r, cols] float32 (written)
  *   dB = s dY^T U                           [rows, r] float32 (written)
  * with s = alpha / r and U = X A^T: U_saved (the forward's U_save) when not
- * NULL, else recomputed.  Same shape rules as the forward.
+ * NULL, else recomputed.  Same shape rules as the forward; for T = 0 dA and
+ * dB are set to 0 (sums over no tokens) and X, dY, U_saved, dX and ws may
+ * be NULL.
  */
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
                               int64_t T, const uint16_t *A, const uint16_t *B, int32_t r,
@@ -292,7 +296,8 @@ typedef struct {
   uint64_t offset;   /* generator counter words 2 and 3                       */
 } qlora_dropout;
 
-/* Bytes of the packed keep mask of T tokens x cols features (0 on bad args). */
+/* Bytes of the packed keep mask of T tokens x cols features (0 on bad args,
+ * and for T = 0). */
 size_t qlora_dropout_mask_bytes(int64_t T, int64_t cols);
 
 /*
@@ -300,7 +305,7 @@ size_t qlora_dropout_mask_bytes(int64_t T, int64_t cols);
  * and, when X is given, the dropped input X_dropped [T, cols] bf16 (x where
  * kept, +0 elsewhere; the 1 / (1 - p) scale is not applied).  X and
  * X_dropped are both NULL or both set (16-byte aligned).  cols % 64 == 0,
- * T >= 1, T * cols below 2^30.  Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN,
+ * T >= 0, T * cols below 2^30; T = 0 does nothing (any pointers).  Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN,
  * QLORA_ERR_SHAPE (sizes, or p outside [0, 1)), QLORA_ERR_DEVICE,
  * QLORA_ERR_HIP.
  */
@@ -309,7 +314,7 @@ qlora_status qlora_dropout_mask(const qlora_dropout *d, int64_t T, int64_t cols,
                                 void *stream);
 
 /* Workspace bytes for qlora_linear_fwd_dropout (is_bwd = 0) or
- * qlora_linear_bwd_dropout (is_bwd = 1) (0 on bad args). */
+ * qlora_linear_bwd_dropout (is_bwd = 1) (0 on bad args, and for T = 0). */
 size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int32_t r,
                                       int is_bwd);
 

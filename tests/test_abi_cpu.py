@@ -202,7 +202,7 @@ def test_linear_validation():
     f = lib.qlora_linear_fwd
     assert f(d, FAKE, T, FAKE, FAKE, r, 32.0, FAKE, None, FAKE, wsf - 1, None) == 4
     assert f(d, None, T, FAKE, FAKE, r, 32.0, FAKE, None, FAKE, wsf, None) == 1
-    assert f(d, FAKE, 0, FAKE, FAKE, r, 32.0, FAKE, None, FAKE, wsf, None) == 2
+    assert f(d, FAKE, -1, FAKE, FAKE, r, 32.0, FAKE, None, FAKE, wsf, None) == 2
     for bad_r in (0, 8, 24, 144, -16):
         assert f(d, FAKE, T, FAKE, FAKE, bad_r, 32.0, FAKE, None, FAKE, wsf, None) == 2
     assert f(d, FAKE, T, FAKE, FAKE, r, float("nan"), FAKE, None, FAKE, wsf, None) == 2
@@ -235,6 +235,38 @@ def test_linear_size_limits():
                                 None) == 2
 
 
+def test_empty_batch_rules():
+    """T = 0 is an empty batch: no workspace; the activation pointers and the
+    workspace may be NULL; A and B (and dA, dB in the backward, which are
+    written with zeros) are still checked, and so are the weight and r; the
+    call then needs a device."""
+    lib = _lib.load()
+    d = ctypes.byref(_desc(1024, 1024))
+    r = 16
+    for is_bwd in (0, 1):
+        assert lib.qlora_linear_workspace(0, 1024, 1024, r, is_bwd) == 0
+        assert lib.qlora_linear_workspace_dropout(0, 1024, 1024, r, is_bwd) == 0
+        assert lib.qlora_linear_workspace(-1, 1024, 1024, r, is_bwd) == 0
+    f, b = lib.qlora_linear_fwd, lib.qlora_linear_bwd
+    assert f(d, None, 0, FAKE, FAKE, r, 32.0, None, None, None, 0, None) in (5, 6)
+    assert f(d, None, 0, None, FAKE, r, 32.0, None, None, None, 0, None) == 1
+    assert f(d, None, 0, FAKE, MISALIGNED, r, 32.0, None, None, None, 0, None) == 3
+    assert f(d, None, 0, FAKE, FAKE, 24, 32.0, None, None, None, 0, None) == 2
+    assert b(d, None, None, 0, FAKE, FAKE, r, 32.0, None, None, FAKE, FAKE, None, 0,
+             None) in (5, 6)
+    assert b(d, None, None, 0, FAKE, FAKE, r, 32.0, None, None, None, FAKE, None, 0, None) == 1
+    assert b(d, None, None, 0, FAKE, FAKE, r, 32.0, None, None, FAKE, MISALIGNED, None, 0,
+             None) == 3
+    fd, bd = lib.qlora_linear_fwd_dropout, lib.qlora_linear_bwd_dropout
+    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, 0,
+              None) in (5, 6)
+    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, None, None, None, None, None, 0, None) == 1
+    assert bd(d, None, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, FAKE, FAKE,
+              None, 0, None) in (5, 6)
+    assert bd(d, None, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, FAKE,
+              None, 0, None) == 1
+
+
 def test_skinny_forward_workspace():
     """Few tokens take the skinny forward, whose split partials need extra
     workspace; the backward layout does not depend on it."""
@@ -256,14 +288,18 @@ def test_dropout_mask_validation_and_size():
     lib = _lib.load()
     assert lib.qlora_dropout_mask_bytes(4096, 4096) == 1024 * 2048
     assert lib.qlora_dropout_mask_bytes(5, 64) == 2 * 32
-    assert lib.qlora_dropout_mask_bytes(0, 64) == 0
+    assert lib.qlora_dropout_mask_bytes(0, 64) == 0                # an empty mask
+    assert lib.qlora_dropout_mask_bytes(-1, 64) == 0
     assert lib.qlora_dropout_mask_bytes(8, 96) == 0
     assert lib.qlora_dropout_mask_bytes((1 << 30) // 64, 64) == 0
     m = lib.qlora_dropout_mask
     assert m(None, 8, 64, FAKE, FAKE, FAKE, None) == 1
     for p in (-0.01, 1.0, 1.5, float("nan"), float("inf")):
         assert m(_drop(p), 8, 64, FAKE, FAKE, FAKE, None) == 2, p
-    assert m(_drop(), 0, 64, FAKE, FAKE, FAKE, None) == 2
+    assert m(_drop(), -1, 64, FAKE, FAKE, FAKE, None) == 2
+    assert m(_drop(), 0, 64, None, None, None, None) == 0          # T = 0: nothing to do
+    assert m(_drop(), 0, 100, None, None, None, None) == 2         # cols still checked
+    assert m(_drop(1.0), 0, 64, None, None, None, None) == 2       # and p
     assert m(_drop(), 8, 100, FAKE, FAKE, FAKE, None) == 2
     assert m(_drop(), 8, 64, FAKE, FAKE, None, None) == 1          # no mask
     assert m(_drop(), 8, 64, FAKE, None, FAKE, None) == 1          # X without X_dropped

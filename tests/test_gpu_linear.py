@@ -120,3 +120,41 @@ def test_deterministic_frozen_weight_and_recompute_path():
     after = (wq.codes, wq.absmax_code, wq.absmax_scale, wq.absmax_offset)
     for a, b in zip(before, after):
         assert torch.equal(a, b)
+
+
+def test_empty_batch():
+    """T = 0: Y, U and dX are empty and dA, dB are exactly the oracle's sums
+    over no tokens (all +0.0), overwriting whatever the buffers held; the
+    same through the lora_dropout entry points."""
+    import bit_nf4_quantized_06_amd as q
+    N, K, r, alpha = 272, 320, 16, 32.0
+    print("[linear] empty batch T=0", flush=True)
+    inp = linear_case(4, N, K, r, alpha, seed=21)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    A, B = bf16_dev(inp["a"]), bf16_dev(inp["b"])
+    X = torch.empty(0, K, dtype=torch.bfloat16, device=A.device)
+    dY = torch.empty(0, N, dtype=torch.bfloat16, device=A.device)
+    x0 = np.zeros((0, K))
+    dy0 = np.zeros((0, N))
+    da_ref, db_ref = O.lora_grads(x0, dy0, WL.bf16_bits_value(inp["a"]),
+                                  WL.bf16_bits_value(inp["b"]), alpha, r)
+    for drop in (None, 0.1):
+        dA = torch.full((r, K), float("nan"), device=A.device)
+        dB = torch.full((N, r), float("nan"), device=A.device)
+        if drop is None:
+            Y, U = q.qlora_linear_fwd(wq, X, A, B, alpha)
+            dX, dA, dB = q.qlora_linear_bwd(wq, X, dY, A, B, alpha, U_saved=U, dA=dA, dB=dB)
+        else:
+            Y, U, keep = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, drop, 3, 4)
+            assert keep.numel() == 0
+            dX, dA, dB = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, drop, 3, 4,
+                                                    keep_saved=keep, U_saved=U, dA=dA, dB=dB)
+        torch.cuda.synchronize()
+        assert tuple(Y.shape) == (0, N) and tuple(U.shape) == (0, r)
+        assert tuple(dX.shape) == (0, K)
+        got_a, got_b = dA.cpu().numpy(), dB.cpu().numpy()
+        assert np.array_equal(got_a.view(np.uint32), da_ref.astype(np.float32).view(np.uint32))
+        assert np.array_equal(got_b.view(np.uint32), db_ref.astype(np.float32).view(np.uint32))
+    keep_only, none = q.qlora_dropout_mask(0, K, 0.1, 1, 2, device=A.device)
+    torch.cuda.synchronize()
+    assert keep_only.numel() == 0 and none is None
