@@ -468,6 +468,16 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   const int l32 = c.l32, lhi = c.lhi, wm = c.wm;
   const int64_t m0 = c.m0, n0 = c.n0;
 
+  // ---- first loads: the activation stages and codes of steps 0 and 1 go out
+  // before the LoRA seed, so their latency overlaps the seed's own loads
+  // (waiting for the seed's operands then drains them too, which leaves the
+  // prologue barrier's count satisfied)
+  CodeRegs ca, cb;   // codes of even / odd steps
+  issue_act(c, sa0, 0);
+  issue_codes<kBwd, kDQ>(c, 0, ca);
+  issue_act(c, sa1, 1);
+  issue_codes<kBwd, kDQ>(c, 1, cb);
+
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
   f32x16_t acc[4][2];
 #pragma unroll
@@ -536,12 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     }
   }
 
-  // ---- prologue ------------------------------------------------------------
-  CodeRegs ca, cb;   // codes of even / odd steps
-  issue_act(c, sa0, 0);
-  issue_codes<kBwd, kDQ>(c, 0, ca);
-  issue_act(c, sa1, 1);
-  issue_codes<kBwd, kDQ>(c, 1, cb);
+  // ---- prologue: step 0's weight tile ----------------------------------------
   {
     const Nf4Lut lut = lut_of<kBwd, kDQ, kF16>(c, ca);
 #pragma unroll
