@@ -182,6 +182,9 @@ class LinearSet:
             it["wsf"] = torch.empty(wsz(t, n, k, r, False), dtype=torch.uint8, device=dev)
             if dropout is not None:
                 it["keep"] = torch.empty((t + 3) // 4, k // 2, dtype=torch.uint8, device=dev)
+                # the dropped input, kept for the backward as autograd keeps a
+                # dropout's output
+                it["Xd"] = torch.empty(t, k, dtype=wq.dtype16, device=dev)
             if backward and "dy" in inp:
                 it["dY"] = to_dev_bf16(inp["dy"], dev, dtype)
                 it["dX"] = torch.empty(t, k, dtype=wq.dtype16, device=dev)
@@ -198,13 +201,14 @@ class LinearSet:
             for li, it in enumerate(self.items):
                 q.qlora_linear_fwd_dropout(it["wq"], it["X"], it["A"], it["B"], self.alpha,
                                            self.dropout, 1234, li, Y=it["Y"], U_save=it["U"],
-                                           keep_save=it["keep"], workspace=it["wsf"])
+                                           keep_save=it["keep"], workspace=it["wsf"],
+                                           X_dropped_save=it["Xd"])
                 if backward and "dY" in it:
                     q.qlora_linear_bwd_dropout(it["wq"], it["X"], it["dY"], it["A"], it["B"],
                                                self.alpha, self.dropout, 1234, li,
                                                keep_saved=it["keep"], U_saved=it["U"],
                                                dX=it["dX"], dA=it["dA"], dB=it["dB"],
-                                               workspace=it["wsb"])
+                                               workspace=it["wsb"], X_dropped_saved=it["Xd"])
             return
         for it in self.items:
             q.qlora_linear_fwd(it["wq"], it["X"], it["A"], it["B"], self.alpha, Y=it["Y"],
@@ -404,7 +408,8 @@ def time_dropout(ev, dev, steps, warmup, reps, p):
     del ls
     return {
         "workload": f"{HEADLINE} with lora_dropout {p:g} on the adapter input (Philox-4x32-10 "
-                    "keep mask drawn in the forward, kept for the backward)",
+                    "keep mask drawn in the forward; the mask and the dropped input kept for "
+                    "the backward)",
         "p": p, "ms_per_step": round(tm["ms_per_step"], 4),
         "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2),
         "mask_ms": round(mask_ms, 4), "mask_bytes": nbytes,

@@ -78,10 +78,10 @@ SIGNATURES = {
     "qlora_dropout_mask": (ctypes.c_int, [_DROP_P, _I64, _I64, _P, _P, _P, _P]),
     "qlora_linear_workspace_dropout": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_int]),
     "qlora_linear_fwd_dropout": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float,
-                                                _DROP_P, _P, _P, _P, _P, _SZ, _P]),
+                                                _DROP_P, _P, _P, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_dropout": (ctypes.c_int, [_DESC_P, _P, _P, _I64, _P, _P, _I32,
                                                 ctypes.c_float, _DROP_P, _P, _P, _P, _P, _P,
-                                                _P, _SZ, _P]),
+                                                _P, _P, _SZ, _P]),
     "qlora_set_timing_events": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_last_hip_error": (ctypes.c_int, []),

@@ -325,11 +325,13 @@ def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: 
                              Y: torch.Tensor | None = None, U_save: torch.Tensor | None = None,
                              save_u: bool = True, keep_save: torch.Tensor | None = None,
                              save_keep: bool = True, workspace: torch.Tensor | None = None,
-                             stream=None):
+                             X_dropped_save: torch.Tensor | None = None, stream=None):
     """Forward with lora_dropout on the adapter input (qlora_linear_fwd_dropout):
     Y = X dequant(W)^T + (alpha/r) (D(X) A^T) B^T, D(X) = keep X / (1 - p).
     Returns (Y, U, keep) with U = D(X) A^T in bf16 and the packed keep mask
-    (each None when not saved)."""
+    (each None when not saved).  X_dropped_save, when given ([T, cols] in
+    the compute dtype), receives the dropped input (x where kept, +0
+    elsewhere) for the backward's X_dropped_saved."""
     lib = _lib.load()
     T = X.shape[0]
     r = A.shape[0]
@@ -349,6 +351,8 @@ def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: 
         keep_save = torch.empty(quads, w.cols // 2, dtype=torch.uint8, device=dev)
     if keep_save is not None:
         _need(keep_save, "keep_save", torch.uint8, (quads, w.cols // 2), dev)
+    if X_dropped_save is not None:
+        _need(X_dropped_save, "X_dropped_save", w.dtype16, (T, w.cols), dev)
     ws_bytes = lib.qlora_linear_workspace_dropout(T, w.rows, w.cols, r, 0)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -358,26 +362,34 @@ def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: 
                lib.qlora_linear_fwd_dropout(ctypes.byref(desc), X.data_ptr(), T, A.data_ptr(),
                                             B.data_ptr(), r, float(alpha), ctypes.byref(d),
                                             Y.data_ptr(), _ptr(U_save), _ptr(keep_save),
-                                            workspace.data_ptr(), workspace.numel(),
+                                            _ptr(X_dropped_save), workspace.data_ptr(),
+                                            workspace.numel(),
                                             _stream(stream)))
     return Y, U_save, keep_save
 
 
-def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
-                             B: torch.Tensor, alpha: float, p: float, seed: int, offset: int,
-                             keep_saved: torch.Tensor | None = None,
+def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor | None, dY: torch.Tensor,
+                             A: torch.Tensor, B: torch.Tensor, alpha: float, p: float, seed: int,
+                             offset: int, keep_saved: torch.Tensor | None = None,
                              U_saved: torch.Tensor | None = None,
                              dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
                              dB: torch.Tensor | None = None,
-                             workspace: torch.Tensor | None = None, stream=None):
+                             workspace: torch.Tensor | None = None,
+                             X_dropped_saved: torch.Tensor | None = None, stream=None):
     """Backward with lora_dropout (qlora_linear_bwd_dropout): dX (bf16), dA and
-    dB (float32); no dW.  keep_saved / U_saved from the forward, or None to
-    redraw / recompute them."""
+    dB (float32); no dW.  keep_saved / U_saved / X_dropped_saved from the
+    forward, or None to redraw / recompute them; with X_dropped_saved, X is
+    not read and may be None."""
     lib = _lib.load()
-    T = X.shape[0]
+    if X is None and X_dropped_saved is None:
+        raise ValueError("X: needed unless X_dropped_saved is given")
+    T = (X if X is not None else X_dropped_saved).shape[0]
     r = A.shape[0]
     dev = w.device
-    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    if X is not None:
+        _need(X, "X", w.dtype16, (T, w.cols), dev)
+    if X_dropped_saved is not None:
+        _need(X_dropped_saved, "X_dropped_saved", w.dtype16, (T, w.cols), dev)
     _need(dY, "dY", w.dtype16, (T, w.rows), dev)
     _need(A, "A", w.dtype16, (r, w.cols), dev)
     _need(B, "B", w.dtype16, (w.rows, r), dev)
@@ -400,9 +412,10 @@ def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A:
     desc = w.descriptor()
     d = _dropout_desc(p, seed, offset)
     _lib.check("qlora_linear_bwd_dropout",
-               lib.qlora_linear_bwd_dropout(ctypes.byref(desc), X.data_ptr(), dY.data_ptr(), T,
+               lib.qlora_linear_bwd_dropout(ctypes.byref(desc), _ptr(X), dY.data_ptr(), T,
                                             A.data_ptr(), B.data_ptr(), r, float(alpha),
-                                            ctypes.byref(d), _ptr(keep_saved), _ptr(U_saved),
+                                            ctypes.byref(d), _ptr(keep_saved),
+                                            _ptr(X_dropped_saved), _ptr(U_saved),
                                             dX.data_ptr(), dA.data_ptr(), dB.data_ptr(),
                                             workspace.data_ptr(), workspace.numel(),
                                             _stream(stream)))

@@ -446,8 +446,9 @@ qlora_status qlora_dropout_mask(const qlora_dropout* dp, int64_t T, int64_t cols
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
                                       const uint16_t* A, const uint16_t* B, int32_t r,
                                       float alpha, const qlora_dropout* dp, uint16_t* Y,
-                                      uint16_t* U_save, uint8_t* keep_save, void* ws,
-                                      size_t ws_bytes, void* stream) {
+                                      uint16_t* U_save, uint8_t* keep_save,
+                                      uint16_t* X_dropped_save, void* ws, size_t ws_bytes,
+                                      void* stream) {
   using namespace qlora;
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
@@ -459,14 +460,15 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t*
     return empty_batch(d, r, A, B, nullptr, nullptr, false, static_cast<hipStream_t>(stream));
   if (!X || !A || !B || !Y || !ws) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
-      (U_save && !aligned16(U_save)) || (keep_save && !aligned16(keep_save)))
+      (U_save && !aligned16(U_save)) || (keep_save && !aligned16(keep_save)) ||
+      (X_dropped_save && !aligned16(X_dropped_save)))
     return QLORA_ERR_ALIGN;
   const LinearWs L = linear_ws_layout(T, d, r, false, true);
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint16_t* Xd = ws_ptr<uint16_t>(ws, L.xd_off);
+  uint16_t* Xd = X_dropped_save ? X_dropped_save : ws_ptr<uint16_t>(ws, L.xd_off);
   uint8_t* keep = keep_save ? keep_save : ws_ptr<uint8_t>(ws, L.keep_off);
   hipError_t e = enqueue_dropout(k, T, d.cols, X, Xd, keep, true, st);
   if (e == hipSuccess)
@@ -479,8 +481,9 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
                                       const uint16_t* dY, int64_t T, const uint16_t* A,
                                       const uint16_t* B, int32_t r, float alpha,
                                       const qlora_dropout* dp, const uint8_t* keep_saved,
-                                      const uint16_t* U_saved, uint16_t* dX, float* dA,
-                                      float* dB, void* ws, size_t ws_bytes, void* stream) {
+                                      const uint16_t* X_dropped_saved, const uint16_t* U_saved,
+                                      uint16_t* dX, float* dA, float* dB, void* ws,
+                                      size_t ws_bytes, void* stream) {
   using namespace qlora;
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
@@ -489,22 +492,33 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   s = dropout_consts(dp, &k);
   if (s != QLORA_OK) return s;
   if (T == 0) return empty_batch(d, r, A, B, dA, dB, true, static_cast<hipStream_t>(stream));
-  if (!X || !dY || !A || !B || !dX || !dA || !dB || !ws) return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dX) ||
-      !aligned16(dA) || !aligned16(dB) || !aligned16(ws) || (U_saved && !aligned16(U_saved)) ||
-      (keep_saved && !aligned16(keep_saved)))
+  // X is not read when the forward's dropped input is given
+  if ((!X && !X_dropped_saved) || !dY || !A || !B || !dX || !dA || !dB || !ws)
+    return QLORA_ERR_NULL;
+  if ((X && !aligned16(X)) || !aligned16(dY) || !aligned16(A) || !aligned16(B) ||
+      !aligned16(dX) || !aligned16(dA) || !aligned16(dB) || !aligned16(ws) ||
+      (U_saved && !aligned16(U_saved)) || (keep_saved && !aligned16(keep_saved)) ||
+      (X_dropped_saved && !aligned16(X_dropped_saved)))
     return QLORA_ERR_ALIGN;
   const LinearWs L = linear_ws_layout(T, d, r, true, true);
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint16_t* Xd = ws_ptr<uint16_t>(ws, L.xd_off);
   // with a saved mask the kernel only reads it (the pointer is not written)
   uint8_t* keep = keep_saved ? const_cast<uint8_t*>(keep_saved) : ws_ptr<uint8_t>(ws, L.keep_off);
-  hipError_t e = enqueue_dropout(k, T, d.cols, X, Xd, keep, keep_saved == nullptr, st);
+  const uint16_t* Xa = X_dropped_saved;
+  hipError_t e = hipSuccess;
+  if (X_dropped_saved) {
+    // the dropped input is given: only a missing mask is redrawn (bits only)
+    if (!keep_saved) e = enqueue_dropout(k, T, d.cols, nullptr, nullptr, keep, true, st);
+  } else {
+    uint16_t* Xd = ws_ptr<uint16_t>(ws, L.xd_off);
+    e = enqueue_dropout(k, T, d.cols, X, Xd, keep, keep_saved == nullptr, st);
+    Xa = Xd;
+  }
   if (e == hipSuccess)
-    e = enqueue_bwd(w, d, Xd, dY, T, A, B, r, alpha / (float)r, k.inv_keep, keep, U_saved, dX,
+    e = enqueue_bwd(w, d, Xa, dY, T, A, B, r, alpha / (float)r, k.inv_keep, keep, U_saved, dX,
                     dA, dB, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }

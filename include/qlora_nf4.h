@@ -324,6 +324,11 @@ size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int
  *   U_save     [T, r] bf16, D(X) A^T (what dB needs), written, or NULL.
  *   keep_save  the packed keep mask, written (16-byte aligned), or NULL (then it lives in the
  *              workspace only); pass it to the backward to skip the redraw.
+ *   X_dropped_save  [T, cols] 16-bit, written with the dropped input (x where
+ *              kept, +0 elsewhere; 1 / (1 - p) not applied; 16-byte aligned), or
+ *              NULL.  Passing it to the backward spares the backward the pass
+ *              that re-forms it from X and the mask (T * cols * 2 bytes kept per
+ *              layer, as autograd keeps a dropout's output).
  * Every token count takes the general path (the skinny path of
  * qlora_linear_fwd serves inference, which has no dropout).  p = 0 gives
  * the same bits as qlora_linear_fwd's general path.  Other arguments,
@@ -333,8 +338,9 @@ size_t qlora_linear_workspace_dropout(int64_t T, int64_t rows, int64_t cols, int
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
                                       const uint16_t *A, const uint16_t *B, int32_t r,
                                       float alpha, const qlora_dropout *d, uint16_t *Y,
-                                      uint16_t *U_save, uint8_t *keep_save, void *ws,
-                                      size_t ws_bytes, void *stream);
+                                      uint16_t *U_save, uint8_t *keep_save,
+                                      uint16_t *X_dropped_save, void *ws, size_t ws_bytes,
+                                      void *stream);
 
 /*
  * Backward with lora_dropout (no dW):
@@ -343,15 +349,18 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const uint16_t 
  *   dA = s G^T D(X)
  *   dB = s dY^T U,   U = D(X) A^T: U_saved if not NULL, else recomputed.
  * keep_saved: the forward's keep_save (read), or NULL to redraw the mask
- * from d (the same seed and offset as the forward).  Other arguments as
+ * from d (the same seed and offset as the forward).  X_dropped_saved: the
+ * forward's X_dropped_save (read), or NULL to form D(X) again from X and
+ * the mask; when given, X is not read and may be NULL.  Other arguments as
  * qlora_linear_bwd.
  */
 qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X,
                                       const uint16_t *dY, int64_t T, const uint16_t *A,
                                       const uint16_t *B, int32_t r, float alpha,
                                       const qlora_dropout *d, const uint8_t *keep_saved,
-                                      const uint16_t *U_saved, uint16_t *dX, float *dA,
-                                      float *dB, void *ws, size_t ws_bytes, void *stream);
+                                      const uint16_t *X_dropped_saved, const uint16_t *U_saved,
+                                      uint16_t *dX, float *dA, float *dB, void *ws,
+                                      size_t ws_bytes, void *stream);
 
 /*
  * Measurement aid.  On the calling host thread, until changed, every later

@@ -258,13 +258,14 @@ def test_empty_batch_rules():
     assert b(d, None, None, 0, FAKE, FAKE, r, 32.0, None, None, FAKE, MISALIGNED, None, 0,
              None) == 3
     fd, bd = lib.qlora_linear_fwd_dropout, lib.qlora_linear_bwd_dropout
-    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, 0,
+    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, None, 0,
               None) in (5, 6)
-    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, None, None, None, None, None, 0, None) == 1
-    assert bd(d, None, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, FAKE, FAKE,
-              None, 0, None) in (5, 6)
+    assert fd(d, None, 0, FAKE, FAKE, r, 32.0, None, None, None, None, None, None, 0,
+              None) == 1
     assert bd(d, None, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, FAKE,
-              None, 0, None) == 1
+              FAKE, None, 0, None) in (5, 6)
+    assert bd(d, None, None, 0, FAKE, FAKE, r, 32.0, _drop(), None, None, None, None, None,
+              FAKE, None, 0, None) == 1
 
 
 def test_skinny_forward_workspace():
@@ -322,9 +323,9 @@ def test_linear_dropout_validation_and_workspace():
         lib.qlora_linear_workspace(16, 8192, 8192, 64, 0)
     f = lib.qlora_linear_fwd_dropout
     args = lambda **k: dict(dict(X=FAKE, T=T, r=r, alpha=32.0, drop=_drop(), Y=FAKE, U=None,
-                                 keep=None, ws=FAKE, wsb=wsf), **k)
+                                 keep=None, xd=None, ws=FAKE, wsb=wsf), **k)
     call = lambda a: f(d, a["X"], a["T"], FAKE, FAKE, a["r"], a["alpha"], a["drop"], a["Y"],
-                       a["U"], a["keep"], a["ws"], a["wsb"], None)
+                       a["U"], a["keep"], a["xd"], a["ws"], a["wsb"], None)
     assert call(args(wsb=wsf - 1)) == 4
     assert call(args(drop=None)) == 1
     assert call(args(drop=_drop(1.0))) == 2
@@ -332,17 +333,20 @@ def test_linear_dropout_validation_and_workspace():
     assert call(args(X=None)) == 1
     assert call(args(r=24)) == 2
     assert call(args(keep=MISALIGNED)) == 3
+    assert call(args(xd=MISALIGNED)) == 3
+    assert call(args(xd=FAKE)) in (5, 6)                 # X_dropped_save accepted
     b = lib.qlora_linear_bwd_dropout
-    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), None, None, FAKE, FAKE, FAKE, FAKE,
-             wsb - 1, None) == 4
-    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, None, None, None, FAKE, FAKE, FAKE, FAKE,
-             wsb, None) == 1
-    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(-0.5), None, None, FAKE, FAKE, FAKE,
-             FAKE, wsb, None) == 2
-    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), MISALIGNED, None, FAKE, FAKE, FAKE,
-             FAKE, wsb, None) == 3
-    assert b(d, FAKE, FAKE, T, FAKE, FAKE, r, 32.0, _drop(), None, None, FAKE, None, FAKE, FAKE,
-             wsb, None) == 1
+    # (X, keep_saved, X_dropped_saved, U_saved, dA)
+    bcall = lambda X=FAKE, keep=None, xd=None, U=None, dA=FAKE, drop=_drop(), wsz=wsb: b(
+        d, X, FAKE, T, FAKE, FAKE, r, 32.0, drop, keep, xd, U, FAKE, dA, FAKE, FAKE, wsz, None)
+    assert bcall(wsz=wsb - 1) == 4
+    assert bcall(drop=None) == 1
+    assert bcall(drop=_drop(-0.5)) == 2
+    assert bcall(keep=MISALIGNED) == 3
+    assert bcall(dA=None) == 1
+    assert bcall(X=None) == 1                            # neither X nor X_dropped_saved
+    assert bcall(X=None, xd=FAKE) in (5, 6)              # X not needed with X_dropped_saved
+    assert bcall(X=None, xd=MISALIGNED) == 3
 
 
 def test_timing_hook_validation():

@@ -185,3 +185,32 @@ def test_attn_4096_with_dropout_full_size():
     got = {"y": _val(Y)[:, sel_n], "u": _val(U), "dx": _val(dX)[:, sel_k],
            "da": dA.cpu().numpy().astype(np.float64), "db": dB.cpu().numpy().astype(np.float64)}
     _check("attn_4096 p=0.05", got, ref)
+
+
+def test_saved_dropped_input_gives_the_same_bits():
+    """The forward's X_dropped_save is the oracle's dropped input bit for bit;
+    a backward given it (X not passed, with the saved mask or redrawing the
+    mask bits) gives exactly the bits of the backward that forms D(X) again
+    from X and the mask."""
+    q = _api()
+    T, N, K, r, alpha, p = 260, 272, 1088, 32, 32.0, 0.2
+    print("[dropout] saved dropped input", flush=True)
+    inp = linear_case(T, N, K, r, alpha, seed=15)
+    wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
+    X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
+    Xd = torch.empty_like(X)
+    Y, U, keep = q.qlora_linear_fwd_dropout(wq, X, A, B, alpha, p, 21, 22, X_dropped_save=Xd)
+    ref = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, 21, 22, keep_saved=keep,
+                                     U_saved=U)
+    g1 = q.qlora_linear_bwd_dropout(wq, None, dY, A, B, alpha, p, 21, 22, keep_saved=keep,
+                                    U_saved=U, X_dropped_saved=Xd)
+    g2 = q.qlora_linear_bwd_dropout(wq, None, dY, A, B, alpha, p, 21, 22, U_saved=U,
+                                    X_dropped_saved=Xd)
+    g3 = q.qlora_linear_bwd_dropout(wq, X, dY, A, B, alpha, p, 21, 22, X_dropped_saved=Xd)
+    torch.cuda.synchronize()
+    mask = O.dropout_keep_mask(T, K, p, 21, 22)
+    assert np.array_equal(bits_host(Xd), np.where(mask, inp["x"], np.uint16(0)))
+    for name, g in (("keep saved", g1), ("mask redrawn", g2), ("U recomputed", g3)):
+        for a, b in zip(ref, g):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), name
