@@ -33,31 +33,59 @@ typedef double f64x2_t __attribute__((ext_vector_type(2)));
 // 0..3, odd lanes words 4..7.
 // ---------------------------------------------------------------------------
 
-// Decision threshold i of codebook kQT (0: NF4, 1: evenly spaced INT4).
-template <int kQT>
-__device__ __forceinline__ constexpr float thr(int i) {
-  return kQT ? kINT4Thr[i] : kNF4Thr[i];
-}
+// Nearest-level code by bins.  [-1, 1] is cut into 32 bins of width 1/16,
+// bin b covering [b/16 - 1, (b+1)/16 - 1).  Each holds at most one decision
+// threshold of either codebook (neighbouring NF4 thresholds are at least
+// 0.08 apart, INT4's 2/15), so the code of a quotient r in bin b is the
+// number of thresholds below the bin's lower edge plus (r > the bin's
+// threshold; +inf for a bin without one), ties going to the lower level as
+// the comparison is strict.  b = floor(fma(r, 16, 16)) (|r| <= 1, so 0 <=
+// b <= 32, clamped to 31): 16 r is exact and the one rounding can only lift
+// r into the next bin, and only within 2^-24 of that bin's lower edge, where
+// the next bin's count plus its comparison give the same code as long as no
+// threshold lies in between -- NF4's thresholds lie at least 1.6e-3 from an
+// edge, and INT4's threshold at exactly 0 is itself an edge, compared
+// against r.  (Checked on the host against the plain threshold count for
+// both codebooks on 2.0e6 quotients each: random, every float32 within 200
+// ulps of each threshold and edge, +-1, +-0, +-2^-149.)  The table, one
+// 8-byte entry per bin, lives in LDS: the 32 entries cover the 64 banks once,
+// so lanes reading different bins never conflict.  This replaces a 4-step
+// binary search of compares and selects: 600 -> 349 vector instructions in
+// the NF4 kernel body, 15-22% less time.
+struct CodeBin {
+  float thr;
+  uint32_t base;
+};
 
-// Nearest-level index by a 4-step binary search over the 15 decision
-// thresholds; the thresholds of each step are picked with selects from
-// constants (scalar registers), so no step waits on a memory read.
 template <int kQT>
-__device__ __forceinline__ uint32_t nf4_code(float r) {
-  const bool b8 = r > thr<kQT>(7);
-  const bool b4 = r > (b8 ? thr<kQT>(11) : thr<kQT>(3));
-  const float t2lo = b4 ? thr<kQT>(5) : thr<kQT>(1);
-  const float t2hi = b4 ? thr<kQT>(13) : thr<kQT>(9);
-  const bool b2 = r > (b8 ? t2hi : t2lo);
-  // threshold index 8 b8 + 4 b4 + 2 b2 (even indices 0 .. 14)
-  const float t00 = b2 ? thr<kQT>(2) : thr<kQT>(0);
-  const float t04 = b2 ? thr<kQT>(6) : thr<kQT>(4);
-  const float t08 = b2 ? thr<kQT>(10) : thr<kQT>(8);
-  const float t12 = b2 ? thr<kQT>(14) : thr<kQT>(12);
-  const float tl = b4 ? t04 : t00;
-  const float th = b4 ? t12 : t08;
-  const bool b1 = r > (b8 ? th : tl);
-  return (b8 ? 8u : 0u) | (b4 ? 4u : 0u) | (b2 ? 2u : 0u) | (b1 ? 1u : 0u);
+struct CodeBins {
+  CodeBin b[32];
+  constexpr CodeBins() : b{} {
+    for (int i = 0; i < 32; ++i) {
+      const float lo = (float)i / 16.0f - 1.0f;
+      const float hi = (float)(i + 1) / 16.0f - 1.0f;
+      uint32_t base = 0u;
+      float t = __builtin_huge_valf();
+      for (int k = 0; k < 15; ++k) {
+        const float x = kQT ? kINT4Thr[k] : kNF4Thr[k];   // 0: NF4, 1: evenly spaced INT4
+        if (x < lo)
+          ++base;
+        else if (x < hi)
+          t = x;
+      }
+      b[i] = CodeBin{t, base};
+    }
+  }
+};
+
+template <int kQT>
+__device__ constexpr CodeBins<kQT> kCodeBins{};
+
+__device__ __forceinline__ uint32_t code_of(float r, const uint2* bins) {
+  uint32_t bi = __float2uint_rz(fmaf(r, 16.0f, 16.0f));
+  bi = bi < 31u ? bi : 31u;
+  const uint2 e = bins[bi];
+  return e.y + (r > __uint_as_float(e.x) ? 1u : 0u);
 }
 
 // kDQ: also the group's float64 partial sum of the constants (the mean's
@@ -68,9 +96,13 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
     const float* __restrict__ W, int64_t n_b, uint32_t* __restrict__ codes,
     float* __restrict__ cblk, double* __restrict__ gpart) {
   __shared__ double wsum[4];
+  __shared__ uint2 bins[32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  if (tid < 32)
+    bins[tid] = make_uint2(__float_as_uint(kCodeBins<kQT>.b[tid].thr), kCodeBins<kQT>.b[tid].base);
+  __syncthreads();
 
   const int64_t blk0 = (int64_t)blockIdx.x * kGroup + wave * 64;
   const int sub = lane & 7;
@@ -123,7 +155,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
           const bool nz = ldexpf(fabsf(v[e]), 150) > m;
           r = copysignf(nz ? 0x1p-149f : 0.0f, v[e]);
         }
-        hh[e >> 2] |= nf4_code<kQT>(r) << (4 * (e & 3));
+        hh[e >> 2] |= code_of(r, bins) << (4 * (e & 3));
       }
       h0 = hh[0];
       h1 = hh[1];
