@@ -335,10 +335,13 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[f][i], fb[f][j], acc[i][j]);
     store_w(c, bs_next, lut, cur, s);
+    // 8 VALU ops per MFMA in the slice that also issues the step's memory
+    // loads, 5 in the others (a sweep of 3..7 found 5..7 alike, about 2 us
+    // per step ahead of 4, and 3 behind)
     if (s == 0)
       slice_schedule<8, kReads, kVmemPerStep>();
     else
-      slice_schedule<4, kReads, 0>();
+      slice_schedule<5, kReads, 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
   // slice 3: 6 MFMAs with the last word, barrier, next step's first
