@@ -194,6 +194,11 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
   load(st, st < st1, cur);
   for (; st < st1; st += 4) {
     load(st + 4, st + 4 < st1, nxt);
+    // priority 1 while this block is dequantised and multiplied, 0 while
+    // the wave waits for the next one's loads: a wave whose data has
+    // arrived issues ahead of one still waiting (-2.5% on the 65B decode
+    // block, same bits)
+    __builtin_amdgcn_s_setprio(1);
     u32x4_t a[TG][4];
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg)
@@ -219,6 +224,7 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     cur = nxt;
   }
 }
