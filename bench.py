@@ -1,12 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the NF4 + LoRA linear layer on one MI355X.
 
-A step is one forward (Y, U) plus one backward (dX, dA, dB) of the
-attention-projection workload: W 4096x4096 (NF4 blocks of 64, double
-quantisation in groups of 256, 0.1% outliers x20), T = 4096 tokens, r = 16,
-alpha = 32.  The weight is quantised once before timing (a load-time cost);
-every step dequantises it on the fly inside the fused GEMMs.  The bulk path
-(quantise and dequantise an 8192 x 22016 weight) is timed in the same run.
+Headline (`value`): a step is the forward (Y, U) and the backward (dX, dA,
+dB) of all seven linears of a 7B-style decoder block (q/k/v/o 4096x4096,
+gate/up 11008x4096, down 4096x11008; NF4 blocks of 64, double quantisation in
+groups of 256), T = 8192 tokens, r = 64, alpha = 16.  The weights are
+quantised once before timing (a load-time cost); every step dequantises them
+on the fly inside the fused GEMMs.  The same line carries the other
+workloads: the 4096x4096 attention projection at 4096 tokens, the 65B-style
+block at 2048 tokens (fwd+bwd) and at 16 tokens (forward, skinny path, GB/s),
+the bulk quantize / dequantize of an 8192x22016 weight, and the rows built
+after those (merge, AdamW, lora_dropout, storage/compute variants).
 
 Prints one JSON line.  Timing uses HIP events on the stream the library
 launches on: whole steps for `value`, and per-kernel events (the library's
@@ -29,7 +33,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 
-HEADLINE = "attn_4096"
+HEADLINE = "block_7b"            # the training workload with the most flops per step
+SMALL_TRAIN = "attn_4096"        # one 4096 x 4096 linear, 4096 tokens
+TRAIN_65B = "block_65b_train"
+DECODE_65B = "block_65b_decode"
 BULK = "bulk_8192x22016"
 MERGE = "merge_8192x22016"
 DROPOUT_P = 0.05              # lora_dropout of the adapter configs on the pages
@@ -38,20 +45,22 @@ DROPOUT_P = 0.05              # lora_dropout of the adapter configs on the pages
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the clock settles over the first ~10 ms of steady work: with 5 warm-up
-    # steps the first timed pass ran about 8% slower than the next ones
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    # the clock ramps over the first ~10-30 ms of load; a step count alone
+    # does not cover that for short steps, so warm-up also lasts at least this
+    ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--bulk-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
-                    help="tokens of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens of the 7B block the CPU oracle is timed on")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle step until this much time has passed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
-    ap.add_argument("--extended", action="store_true",
-                    help="also time the 7B-block, 65B-block and decode workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated subset of: block_7b, attn_4096, block_65b_train, "
+                         "block_65b_decode, bulk, adamw, dropout, variants (profiling runs)")
     return ap.parse_args()
 
 
@@ -159,7 +168,7 @@ class LinearSet:
     """Device-resident inputs, packed weights and outputs of a workload."""
 
     def __init__(self, wl, dev, tokens=None, backward=True, dropout=None, dtype="bf16",
-                 double_quant=True):
+                 double_quant=True, weights=None):
         import torch
 
         import bit_nf4_quantized_06_amd as q
@@ -168,11 +177,16 @@ class LinearSet:
         self.dropout = dropout          # lora_dropout probability, or None
         self.T = wl.tokens if tokens is None else tokens
         self.r, self.alpha = wl.rank, wl.alpha
+        self.backward = backward and wl.backward
         self.items = []
         for li, lin in enumerate(wl.linears):
-            inp = WL.linear_inputs(wl, li, tokens=self.T, dtype=dtype)
-            wq = q.qlora_nf4_quantize(torch.from_numpy(inp["w"]).to(dev),
-                                      double_quant=double_quant, compute_dtype=dtype)
+            inp = WL.linear_inputs(wl, li, tokens=self.T, dtype=dtype,
+                                   with_weight=weights is None)
+            if weights is None:
+                wq = q.qlora_nf4_quantize(torch.from_numpy(inp["w"]).to(dev),
+                                          double_quant=double_quant, compute_dtype=dtype)
+            else:
+                wq = weights[li]      # the same packed weight (same draws), another token count
             it = {"lin": lin, "wq": wq, "X": to_dev_bf16(inp["x"], dev, dtype),
                   "A": to_dev_bf16(inp["a"], dev, dtype), "B": to_dev_bf16(inp["b"], dev, dtype)}
             n, k, r, t = lin.out_features, lin.in_features, self.r, self.T
@@ -185,7 +199,7 @@ class LinearSet:
                 # the dropped input, kept for the backward as autograd keeps a
                 # dropout's output
                 it["Xd"] = torch.empty(t, k, dtype=wq.dtype16, device=dev)
-            if backward and "dy" in inp:
+            if self.backward and "dy" in inp:
                 it["dY"] = to_dev_bf16(inp["dy"], dev, dtype)
                 it["dX"] = torch.empty(t, k, dtype=wq.dtype16, device=dev)
                 it["dA"] = torch.empty(r, k, dtype=torch.float32, device=dev)
@@ -195,76 +209,220 @@ class LinearSet:
             del inp
         torch.cuda.synchronize()
 
-    def step(self, backward=True):
+    def step(self, hook=None):
+        """One step: the forward of every linear, then (training workloads)
+        the backward of every linear.  hook(li, "fwd" | "bwd"), if given, runs
+        before each call (the kernel-timing pass sets its events there)."""
         import bit_nf4_quantized_06_amd as q
-        if self.dropout is not None:
-            for li, it in enumerate(self.items):
+        for li, it in enumerate(self.items):
+            if hook:
+                hook(li, "fwd")
+            if self.dropout is not None:
                 q.qlora_linear_fwd_dropout(it["wq"], it["X"], it["A"], it["B"], self.alpha,
                                            self.dropout, 1234, li, Y=it["Y"], U_save=it["U"],
                                            keep_save=it["keep"], workspace=it["wsf"],
                                            X_dropped_save=it["Xd"])
-                if backward and "dY" in it:
-                    q.qlora_linear_bwd_dropout(it["wq"], it["X"], it["dY"], it["A"], it["B"],
-                                               self.alpha, self.dropout, 1234, li,
-                                               keep_saved=it["keep"], U_saved=it["U"],
-                                               dX=it["dX"], dA=it["dA"], dB=it["dB"],
-                                               workspace=it["wsb"], X_dropped_saved=it["Xd"])
+            else:
+                q.qlora_linear_fwd(it["wq"], it["X"], it["A"], it["B"], self.alpha, Y=it["Y"],
+                                   U_save=it["U"], workspace=it["wsf"])
+        if not self.backward:
             return
-        for it in self.items:
-            q.qlora_linear_fwd(it["wq"], it["X"], it["A"], it["B"], self.alpha, Y=it["Y"],
-                               U_save=it["U"], workspace=it["wsf"])
-            if backward and "dY" in it:
+        for li in reversed(range(len(self.items))):
+            it = self.items[li]
+            if "dY" not in it:
+                continue
+            if hook:
+                hook(li, "bwd")
+            if self.dropout is not None:
+                q.qlora_linear_bwd_dropout(it["wq"], it["X"], it["dY"], it["A"], it["B"],
+                                           self.alpha, self.dropout, 1234, li,
+                                           keep_saved=it["keep"], U_saved=it["U"],
+                                           dX=it["dX"], dA=it["dA"], dB=it["dB"],
+                                           workspace=it["wsb"], X_dropped_saved=it["Xd"])
+            else:
                 q.qlora_linear_bwd(it["wq"], it["X"], it["dY"], it["A"], it["B"], self.alpha,
                                    U_saved=it["U"], dX=it["dX"], dA=it["dA"], dB=it["dB"],
                                    workspace=it["wsb"])
 
-    def flops(self, backward=True):
+    def flops(self):
         tot = 0
         for it in self.items:
             n, k = it["lin"].out_features, it["lin"].in_features
-            if backward:
+            if self.backward:
                 tot += flops_fwd_bwd(self.T, n, k, self.r)
             else:
                 tot += 2 * self.T * n * k + 2 * self.T * self.r * (n + k)
         return tot
 
+    def gemm_flops(self):
+        """Algorithmic flops of the fused forward GEMMs and of the dX GEMMs
+        (the LoRA seed included) over one step."""
+        fwd = dx = 0
+        for it in self.items:
+            n, k, t, r = it["lin"].out_features, it["lin"].in_features, self.T, self.r
+            fwd += 2 * t * n * (k + r)
+            if self.backward:
+                dx += 2 * t * k * (n + r)
+        return fwd, dx
 
-def time_steps(ls, ev, steps, warmup, backward=True, kernel_timing=True):
-    """Whole-step and per-GEMM times (ms) over `steps` timed steps."""
+    def hbm_bytes_fwd(self):
+        """Algorithmic bytes of a forward-only step: packed weights, A, B, X
+        and Y once each."""
+        return sum(packed_bytes(it["lin"].out_features * it["lin"].in_features)
+                   + 2 * (it["A"].numel() + it["B"].numel() + it["X"].numel() + it["Y"].numel())
+                   for it in self.items)
+
+
+def warm_up(ls, steps, seconds):
+    """At least `steps` steps and at least `seconds` of steady work: the clock
+    of the part ramps over the first ~10-30 ms of load and settles
+    (power-limited) after that, so a step count alone is not enough for a
+    short step.  Returns (steps run, seconds)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        ls.step()
+        n += 1
+    torch.cuda.synchronize()
+    chunk = max(1, steps)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(chunk):
+            ls.step()
+        n += chunk
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def time_steps(ls, ev, steps, warmup, warmup_s, kernel_timing=True):
+    """Whole-step time (ms) over `steps` timed steps with no event between
+    their kernels, then (kernel_timing) the same number of steps again with
+    a pair of HIP events around every fused GEMM (or skinny forward) on the
+    library's stream; returns per-kernel totals and launch counts."""
     import torch
 
     from bit_nf4_quantized_06_amd import _lib
     lib = _lib.load()
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(warmup):
-        ls.step(backward)
-    torch.cuda.synchronize()
-    per_step = []
-    fwd_pairs, dx_pairs = [], []
+    wsteps, wsec = warm_up(ls, warmup, warmup_s)
     start, stop = ev.new(fence=True), ev.new(fence=True)
     t_wall = time.perf_counter()
     ev.record(start, stream)
     for _ in range(steps):
-        if kernel_timing:
-            fp = (ev.new(), ev.new())
-            dp = (ev.new(), ev.new())
-            lib.qlora_set_timing_events(0, fp[0], fp[1])
-            lib.qlora_set_timing_events(1, dp[0], dp[1])
-            fwd_pairs.append(fp)
-            dx_pairs.append(dp)
-        ls.step(backward)
+        ls.step()
     ev.record(stop, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    total = ev.ms(start, stop)
+    res = {"ms_per_step": total / steps, "wall_s": wall, "warmup_steps_run": wsteps,
+           "warmup_s": wsec}
+    if not kernel_timing:
+        return res
+    pairs = {"fwd": [], "dx": []}
+
+    def hook(li, phase):
+        if phase == "fwd":
+            p = (ev.new(), ev.new())
+            lib.qlora_set_timing_events(0, p[0], p[1])
+            lib.qlora_set_timing_events(1, None, None)
+            pairs["fwd"].append(p)
+        else:
+            p = (ev.new(), ev.new())
+            lib.qlora_set_timing_events(0, None, None)
+            lib.qlora_set_timing_events(1, p[0], p[1])
+            pairs["dx"].append(p)
+
+    start2, stop2 = ev.new(fence=True), ev.new(fence=True)
+    ev.record(start2, stream)
+    for _ in range(steps):
+        ls.step(hook)
+    ev.record(stop2, stream)
+    torch.cuda.synchronize()
     lib.qlora_set_timing_events(0, None, None)
     lib.qlora_set_timing_events(1, None, None)
-    total = ev.ms(start, stop)
-    res = {"ms_per_step": total / steps, "wall_s": wall}
-    if kernel_timing and len(ls.items) == 1:
-        res["fwd_gemm_ms"] = sum(ev.ms(a, b) for a, b in fwd_pairs) / steps
-        if backward:
-            res["dx_gemm_ms"] = sum(ev.ms(a, b) for a, b in dx_pairs) / steps
+    res["ms_per_step_with_kernel_events"] = ev.ms(start2, stop2) / steps
+    for k, v in pairs.items():
+        if v:
+            res[k] = {"total_ms": sum(ev.ms(a, b) for a, b in v) / steps,
+                      "launches": len(v) // steps}
     return res
+
+
+def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
+    """fwd+bwd TFLOP/s of a training workload and the roofline of its
+    dominant fused GEMM (achieved = its algorithmic flops over its event-timed
+    duration, summed over the step's launches of it)."""
+    import torch
+
+    import workloads as WL
+    wl = WL.WORKLOADS[name]
+    ls = LinearSet(wl, dev)
+    tm = time_steps(ls, ev, steps, warmup, warmup_s)
+    fl = ls.flops()
+    fwd_fl, dx_fl = ls.gemm_flops()
+    kern = {"qlora_gemm_fwd": (tm["fwd"], fwd_fl), "qlora_gemm_dx": (tm["dx"], dx_fl)}
+    dom = max(kern, key=lambda k: kern[k][0]["total_ms"])
+    kt, kfl = kern[dom]
+    achieved = kfl / (kt["total_ms"] / 1e3) / 1e12
+    digest = source_digest("gemm.hip", "device_common.h")
+    shapes = sorted({(it["lin"].out_features, it["lin"].in_features) for it in ls.items})
+    out = {
+        "ms_per_step": round(tm["ms_per_step"], 4),
+        "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2),
+        "mfma_frac": round(fl / (tm["ms_per_step"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": fl,
+        "tokens": ls.T, "rank": ls.r, "alpha": ls.alpha, "linears": len(ls.items),
+        "shapes": [f"{n}x{k}" for n, k in shapes],
+        "warmup_steps_run": tm["warmup_steps_run"], "warmup_s": round(tm["warmup_s"], 3),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic(dom, name, digest),
+                     "flops_per_launch": kfl // max(1, kt["launches"]),
+                     "avg_launch_ms": round(kt["total_ms"] / max(1, kt["launches"]), 4),
+                     "launches_per_step": kt["launches"], "source_digest": digest},
+        "kernels_ms_per_step": {k: round(v[0]["total_ms"], 4) for k, v in kern.items()},
+        "ms_per_step_with_kernel_events": round(tm["ms_per_step_with_kernel_events"], 4),
+    }
+    weights = [it["wq"] for it in ls.items] if keep_weights else None
+    del ls
+    torch.cuda.empty_cache()
+    return (out, weights) if keep_weights else out
+
+
+def decode_config(name, ev, dev, steps, warmup, warmup_s, weights=None):
+    """Forward-only skinny workload: GB/s of the algorithmic bytes (packed
+    weights, A, B, X, Y) against 8 TB/s, and the skinny forward's own rate."""
+    import torch
+
+    import workloads as WL
+    wl = WL.WORKLOADS[name]
+    ls = LinearSet(wl, dev, backward=False, weights=weights)
+    tm = time_steps(ls, ev, steps, warmup, warmup_s)
+    by = ls.hbm_bytes_fwd()
+    fl = ls.flops()
+    kt = tm["fwd"]
+    gbps = by / (tm["ms_per_step"] / 1e3) / 1e9
+    kgbps = by / (kt["total_ms"] / 1e3) / 1e9
+    digest = source_digest("gemv.hip", "device_common.h")
+    out = {
+        "ms_per_step": round(tm["ms_per_step"], 4),
+        "GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 3),
+        "bytes_per_step": by, "tokens": ls.T, "linears": len(ls.items),
+        "warmup_steps_run": tm["warmup_steps_run"], "warmup_s": round(tm["warmup_s"], 3),
+        "roofline": {"kernel": "qlora_gemv", "bound": "hbm", "achieved": round(kgbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(kgbps / PEAK_HBM_GBPS, 4),
+                     "traffic": profiled_traffic("qlora_gemv", name, digest),
+                     "bytes_per_launch": by // max(1, kt["launches"]),
+                     "avg_launch_ms": round(kt["total_ms"] / max(1, kt["launches"]), 4),
+                     "launches_per_step": kt["launches"], "source_digest": digest},
+        "ms_per_step_with_kernel_events": round(tm["ms_per_step_with_kernel_events"], 4),
+    }
+    del ls
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_bulk(ev, dev, reps):
@@ -374,7 +532,7 @@ def time_adamw(ev, dev, reps):
     }
 
 
-def time_dropout(ev, dev, steps, warmup, reps, p):
+def time_dropout(ev, dev, steps, warmup, warmup_s, reps, p):
     """The headline workload with lora_dropout p (mask drawn in the forward,
     kept for the backward), and the mask kernel alone on its X (draws the
     mask, writes the dropped input)."""
@@ -384,9 +542,9 @@ def time_dropout(ev, dev, steps, warmup, reps, p):
     import workloads as WL
     from bit_nf4_quantized_06_amd import _lib
     lib = _lib.load()
-    wl = WL.WORKLOADS[HEADLINE]
+    wl = WL.WORKLOADS[SMALL_TRAIN]
     ls = LinearSet(wl, dev, dropout=p)
-    tm = time_steps(ls, ev, steps, warmup, kernel_timing=False)
+    tm = time_steps(ls, ev, steps, warmup, warmup_s, kernel_timing=False)
     fl = ls.flops()
     it = ls.items[0]
     T, K = ls.T, it["lin"].in_features
@@ -407,7 +565,7 @@ def time_dropout(ev, dev, steps, warmup, reps, p):
     nbytes = 4 * T * K + ((T + 3) // 4) * (K // 2)
     del ls
     return {
-        "workload": f"{HEADLINE} with lora_dropout {p:g} on the adapter input (Philox-4x32-10 "
+        "workload": f"{SMALL_TRAIN} with lora_dropout {p:g} on the adapter input (Philox-4x32-10 "
                     "keep mask drawn in the forward; the mask and the dropped input kept for "
                     "the backward)",
         "p": p, "ms_per_step": round(tm["ms_per_step"], 4),
@@ -418,7 +576,7 @@ def time_dropout(ev, dev, steps, warmup, reps, p):
     }
 
 
-def time_variants(ev, dev, steps, warmup, reps):
+def time_variants(ev, dev, steps, warmup, warmup_s, reps):
     """The storage and compute variants: the headline step with fp16 compute
     and with float32 block constants (no double quantisation), and quantize /
     dequantize of the bulk weight in the other formats."""
@@ -429,12 +587,12 @@ def time_variants(ev, dev, steps, warmup, reps):
     from bit_nf4_quantized_06_amd import _lib
     lib = _lib.load()
     res = {}
-    wl = WL.WORKLOADS[HEADLINE]
+    wl = WL.WORKLOADS[SMALL_TRAIN]
     for name, dt, dq in (("fp16", "fp16", True), ("bf16_no_double_quant", "bf16", False)):
         ls = LinearSet(wl, dev, dtype=dt, double_quant=dq)
-        tm = time_steps(ls, ev, steps, warmup, kernel_timing=False)
+        tm = time_steps(ls, ev, steps, warmup, warmup_s, kernel_timing=False)
         fl = ls.flops()
-        res[f"{HEADLINE}_{name}"] = {"ms_per_step": round(tm["ms_per_step"], 4),
+        res[f"{SMALL_TRAIN}_{name}"] = {"ms_per_step": round(tm["ms_per_step"], 4),
                                       "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2)}
         del ls
         torch.cuda.empty_cache()
@@ -492,8 +650,10 @@ def copy_calibration():
 
 
 def cpu_baseline(tokens, min_seconds):
-    """The oracle (dequantise the packed weight + float64 forward + backward)
-    on `tokens` tokens of the headline workload, timed on the host cores."""
+    """The oracle on a bounded sample of the headline workload, timed on the
+    host cores: every linear of the 7B block, its packed weight dequantised
+    by the oracle (as every step does) and the float64 forward + backward
+    (NumPy / BLAS) on the first `tokens` of its 8192 tokens."""
     import numpy as np
 
     import workloads as WL
@@ -504,34 +664,37 @@ def cpu_baseline(tokens, min_seconds):
     except Exception:  # pragma: no cover
         threads = None
     wl = WL.WORKLOADS[HEADLINE]
-    lin = wl.linears[0]
-    inp = WL.linear_inputs(wl, 0, tokens=tokens)
-    st = O.quantize(inp["w"])
-    x = WL.bf16_bits_value(inp["x"]).astype(np.float64)
-    a = WL.bf16_bits_value(inp["a"]).astype(np.float64)
-    b = WL.bf16_bits_value(inp["b"]).astype(np.float64)
-    dy = WL.bf16_bits_value(inp["dy"]).astype(np.float64)
+    lin_data = []
+    for li in range(len(wl.linears)):
+        inp = WL.linear_inputs(wl, li, tokens=tokens)
+        st = O.quantize(inp["w"])
+        del inp["w"]
+        vals = {k: WL.bf16_bits_value(inp[k]).astype(np.float64) for k in ("x", "a", "b", "dy")}
+        lin_data.append((st, vals))
     reps = 0
     t0 = time.perf_counter()
     while True:
-        w_hat = O.dequantize(st)
-        O.linear_forward(x, w_hat, a, b, wl.alpha, wl.rank)
-        O.linear_backward(x, dy, w_hat, a, b, wl.alpha, wl.rank)
+        for st, v in lin_data:
+            w_hat = O.dequantize(st)
+            O.linear_forward(v["x"], w_hat, v["a"], v["b"], wl.alpha, wl.rank)
+            O.linear_backward(v["x"], v["dy"], w_hat, v["a"], v["b"], wl.alpha, wl.rank)
+            del w_hat
         reps += 1
-        if time.perf_counter() - t0 >= min_seconds or reps >= 50:
+        if time.perf_counter() - t0 >= min_seconds or reps >= 20:
             break
     dt = (time.perf_counter() - t0) / reps
-    fl = flops_fwd_bwd(tokens, lin.out_features, lin.in_features, wl.rank)
+    fl = sum(flops_fwd_bwd(tokens, lin.out_features, lin.in_features, wl.rank)
+             for lin in wl.linears)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count()
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads or cores,
             "kind": "oracle",
-            "sample": f"{HEADLINE} at T={tokens} of {wl.tokens} tokens: oracle dequantise of the "
-                      f"full {lin.out_features}x{lin.in_features} weight + float64 forward + "
-                      f"backward (NumPy/BLAS), {dt:.2f} s per step, mean of {reps}; "
-                      f"{cores} host cores visible",
+            "sample": f"{HEADLINE}: all {len(wl.linears)} linears, oracle dequantise of each "
+                      f"full packed weight + float64 forward + backward (NumPy/BLAS) on "
+                      f"{tokens} of the {wl.tokens} tokens; {dt:.2f} s per step, mean of {reps}; "
+                      f"{cores} host cores visible, {threads} BLAS threads",
             "seconds_per_step": round(dt, 3)}
 
 
@@ -554,111 +717,91 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     ev = HipEvents()
+    only = set(args.only.split(",")) if args.only else None
 
-    wl = WL.WORKLOADS[HEADLINE]
-    lin = wl.linears[0]
-    print(f"[bench] preparing {HEADLINE}", file=sys.stderr, flush=True)
-    ls = LinearSet(wl, dev)
-    print("[bench] timing fwd+bwd", file=sys.stderr, flush=True)
-    # the timed steps: the hot path alone, no events between its kernels
-    tm = time_steps(ls, ev, args.steps, args.warmup, kernel_timing=False)
-    # kernel durations: the same number of steps again, with a pair of HIP
-    # events around each GEMM on the library's stream (each event record
-    # costs several microseconds of idle GPU, so these steps are slower)
-    tk = time_steps(ls, ev, args.steps, 0)
-    fl = ls.flops()
-    value = fl / (tm["ms_per_step"] / 1e3) / 1e12
-    T, N, K, r = wl.tokens, lin.out_features, lin.in_features, wl.rank
-    kern = {
-        "qlora_gemm_fwd": (tk["fwd_gemm_ms"], 2 * T * N * (K + r)),
-        "qlora_gemm_dx": (tk["dx_gemm_ms"], 2 * T * K * (N + r)),
-    }
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_ms, dom_flops = kern[dom]
-    achieved = dom_flops / (dom_ms / 1e3) / 1e12
-    digest = source_digest("gemm.hip", "device_common.h")
-    traffic = profiled_traffic(dom, HEADLINE, digest)
-    del ls
-    torch.cuda.empty_cache()
+    def want(k):
+        return only is None or k in only
 
-    print("[bench] timing bulk quantize/dequantize", file=sys.stderr, flush=True)
-    bulk = time_bulk(ev, dev, args.bulk_reps)
-    print("[bench] timing the adapter AdamW step", file=sys.stderr, flush=True)
-    adamw = time_adamw(ev, dev, args.bulk_reps)
-    torch.cuda.empty_cache()
-    print("[bench] timing fwd+bwd with lora_dropout", file=sys.stderr, flush=True)
-    dropout = time_dropout(ev, dev, max(5, args.steps // 2), args.warmup, args.bulk_reps,
-                           DROPOUT_P)
-    torch.cuda.empty_cache()
-    print("[bench] timing the storage and compute variants", file=sys.stderr, flush=True)
-    variants = time_variants(ev, dev, max(5, args.steps // 2), args.warmup, args.bulk_reps)
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    extended = None
-    if args.extended:
-        extended = {}
-        for name, bwd in (("block_7b", True), ("block_65b_train", True),
-                          ("block_65b_decode", False)):
-            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            w2 = WL.WORKLOADS[name]
-            ls2 = LinearSet(w2, dev, backward=bwd)
-            t2 = time_steps(ls2, ev, max(3, args.steps // 10), 2, backward=bwd,
-                            kernel_timing=False)
-            f2 = ls2.flops(bwd)
-            extended[name] = {"ms_per_step": round(t2["ms_per_step"], 4),
-                              "TFLOPs": round(f2 / (t2["ms_per_step"] / 1e3) / 1e12, 2),
-                              "fwd_bwd" if bwd else "fwd_only": True}
-            if not bwd:
-                by = sum(packed_bytes(it["lin"].out_features * it["lin"].in_features)
-                         + 2 * (it["A"].numel() + it["B"].numel() + it["X"].numel()
-                                + it["Y"].numel()) for it in ls2.items)
-                extended[name]["GBps"] = round(by / (t2["ms_per_step"] / 1e3) / 1e9, 1)
-                extended[name]["hbm_frac"] = round(extended[name]["GBps"] / PEAK_HBM_GBPS, 4)
-            del ls2
-            torch.cuda.empty_cache()
+    head = None
+    configs = {}
+    if want(HEADLINE):
+        log(f"timing {HEADLINE} fwd+bwd (headline)")
+        head = training_config(HEADLINE, ev, dev, args.steps, args.warmup, args.warmup_seconds)
+    if want(SMALL_TRAIN):
+        log(f"timing {SMALL_TRAIN} fwd+bwd")
+        configs[SMALL_TRAIN] = training_config(SMALL_TRAIN, ev, dev, args.steps, args.warmup,
+                                               args.warmup_seconds)
+    w65 = None
+    if want(TRAIN_65B):
+        log(f"timing {TRAIN_65B} fwd+bwd")
+        configs[TRAIN_65B], w65 = training_config(TRAIN_65B, ev, dev, args.steps, args.warmup,
+                                                  args.warmup_seconds,
+                                                  keep_weights=want(DECODE_65B))
+    if want(DECODE_65B):
+        # the decode block is the same 65B-style block (same weight draws) at 16 tokens
+        log(f"timing {DECODE_65B} forward (skinny path)")
+        configs[DECODE_65B] = decode_config(DECODE_65B, ev, dev, args.steps, args.warmup,
+                                            args.warmup_seconds, weights=w65)
+    del w65
+    torch.cuda.empty_cache()
+    if want("bulk"):
+        log("timing bulk quantize/dequantize/merge")
+        configs[BULK] = time_bulk(ev, dev, args.bulk_reps)
+    nxt = {}
+    if want("adamw"):
+        log("timing the adapter AdamW step")
+        nxt["adamw"] = time_adamw(ev, dev, args.bulk_reps)
+        torch.cuda.empty_cache()
+    if want("dropout"):
+        log("timing fwd+bwd with lora_dropout")
+        nxt["dropout"] = time_dropout(ev, dev, args.steps, args.warmup, args.warmup_seconds,
+                                      args.bulk_reps, DROPOUT_P)
+        torch.cuda.empty_cache()
+    if want("variants"):
+        log("timing the storage and compute variants")
+        nxt["variants"] = time_variants(ev, dev, args.steps, args.warmup, args.warmup_seconds,
+                                        args.bulk_reps)
     ev.close()
 
     cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing CPU oracle", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline and head is not None:
+        log("timing CPU oracle")
         cpu = cpu_baseline(args.cpu_tokens, args.cpu_seconds)
 
+    wl = WL.WORKLOADS[HEADLINE]
     line = {
         "metric": "QLoRA linear fwd+bwd TFLOP/s (NF4 dequant-fused); NF4 dequant GB/s",
-        "value": round(value, 2),
+        "value": head["TFLOPs"] if head else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(tm["ms_per_step"], 4),
+        "warmup_steps_run": head["warmup_steps_run"] if head else None,
+        "warmup_s": head["warmup_s"] if head else None,
+        "ms_per_step": head["ms_per_step"] if head else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded W ~ N(0, 0.02^2) with 0.1% of entries x20, bf16 X, dY ~ N(0,1),"
-                " A ~ N(0, 1/r), B ~ N(0, 0.01^2)",
-        "config": {"workload": f"{HEADLINE}: one QLoRA linear, W {N}x{K} NF4/64 + double quant/256, "
-                               f"T={T} tokens (8x512), r={r}, alpha={wl.alpha:g}; step = forward "
-                               "(Y, U) + backward (dX, dA, dB), no dW",
-                   "tokens": T, "out_features": N, "in_features": K, "rank": r,
-                   "alpha": wl.alpha, "flops_per_step": fl},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
-                     "source_digest": digest},
-        "kernels_ms": {k: round(v[0], 4) for k, v in kern.items()},
-        "kernel_timing": {"steps": args.steps,
-                          "ms_per_step_with_kernel_events": round(tk["ms_per_step"], 4),
-                          "how": "a second pass of the same steps with HIP events around "
-                                 "each GEMM on the library's stream"},
-        "bulk": bulk,
-        "adamw": adamw,
-        "dropout": dropout,
-        "variants": variants,
+        "data": "synthetic: seeded W ~ N(0, 0.02^2) (0.1% of entries x20 where the workload asks), "
+                "bf16 X, dY ~ N(0,1), A ~ N(0, 1/r), B ~ N(0, 0.01^2); no dataset",
+        "config": {"workload": f"{HEADLINE}: one 7B-style decoder block, all 7 QLoRA linears "
+                               "(q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008), NF4/64 "
+                               f"+ double quant/256, T={wl.tokens} tokens (16x512), r={wl.rank}, "
+                               f"alpha={wl.alpha:g}; step = forward (Y, U) of every linear + "
+                               "backward (dX, dA, dB) of every linear, no dW",
+                   "tokens": wl.tokens, "rank": wl.rank, "alpha": wl.alpha,
+                   "flops_per_step": head["flops_per_step"] if head else None},
+        "roofline": head["roofline"] if head else None,
+        "kernels_ms_per_step": head["kernels_ms_per_step"] if head else None,
+        "ms_per_step_with_kernel_events": head["ms_per_step_with_kernel_events"] if head else None,
+        "configs": configs,
+        "next": nxt,
         "cpu_baseline": cpu,
     }
-    if extended is not None:
-        line["extended"] = extended
     print(json.dumps(line))
 
 

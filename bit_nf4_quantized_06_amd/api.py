@@ -7,6 +7,8 @@ kernels.  bf16 tensors are passed as their bit patterns.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 from dataclasses import dataclass
 
 import torch
@@ -22,6 +24,36 @@ def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _as_torch_stream(stream):
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle)
+
+
+def _stream_scoped(fn):
+    """Run `fn` with the caller's `stream` as torch's current stream.
+
+    Every output and workspace the binding allocates for a call is then taken
+    from the caching allocator's pool of the stream the kernels run on: a
+    workspace released when the call returns can only be handed to a later
+    allocation on that same stream, whose work is ordered after these kernels.
+    (Allocated on another stream, the block could be reused by that stream
+    while the kernels still read and write it.)"""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        ba = sig.bind(*args, **kw)
+        stream = ba.arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kw)
+        ba.arguments["stream"] = None
+        with torch.cuda.stream(_as_torch_stream(stream)):
+            return fn(*ba.args, **ba.kwargs)
+    return wrapper
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> None:
@@ -104,6 +136,7 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
+@_stream_scoped
 def qlora_nf4_quantize(W: torch.Tensor, out: NF4Weight | None = None,
                        workspace: torch.Tensor | None = None, stream=None,
                        quant_type: str = "nf4", double_quant: bool = True,
@@ -126,6 +159,7 @@ def qlora_nf4_quantize(W: torch.Tensor, out: NF4Weight | None = None,
     return out
 
 
+@_stream_scoped
 def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """[rows, cols] dequantised weight in the weight's compute dtype
     (qlora_nf4_dequantize)."""
@@ -139,6 +173,7 @@ def qlora_nf4_dequantize(w: NF4Weight, out: torch.Tensor | None = None, stream=N
     return out
 
 
+@_stream_scoped
 def qlora_nf4_merge(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, alpha: float,
                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """[rows, cols] weight with the adapter folded in (qlora_nf4_merge):
@@ -207,6 +242,7 @@ def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 
 
+@_stream_scoped
 def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                      alpha: float, Y: torch.Tensor | None = None,
                      U_save: torch.Tensor | None = None, save_u: bool = True,
@@ -241,6 +277,7 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     return Y, U_save
 
 
+@_stream_scoped
 def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
                      B: torch.Tensor, alpha: float, U_saved: torch.Tensor | None = None,
                      dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
@@ -290,6 +327,7 @@ def qlora_dropout_mask_bytes(T: int, cols: int) -> int:
     return int(_lib.load().qlora_dropout_mask_bytes(T, cols))
 
 
+@_stream_scoped
 def qlora_dropout_mask(T: int, cols: int, p: float, seed: int, offset: int,
                        X: torch.Tensor | None = None, X_dropped: torch.Tensor | None = None,
                        keep: torch.Tensor | None = None, device=None, stream=None):
@@ -320,6 +358,7 @@ def qlora_linear_workspace_dropout(T: int, rows: int, cols: int, r: int, is_bwd:
     return int(_lib.load().qlora_linear_workspace_dropout(T, rows, cols, r, int(bool(is_bwd))))
 
 
+@_stream_scoped
 def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                              alpha: float, p: float, seed: int, offset: int,
                              Y: torch.Tensor | None = None, U_save: torch.Tensor | None = None,
@@ -368,6 +407,7 @@ def qlora_linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: 
     return Y, U_save, keep_save
 
 
+@_stream_scoped
 def qlora_linear_bwd_dropout(w: NF4Weight, X: torch.Tensor | None, dY: torch.Tensor,
                              A: torch.Tensor, B: torch.Tensor, alpha: float, p: float, seed: int,
                              offset: int, keep_saved: torch.Tensor | None = None,

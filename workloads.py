@@ -132,15 +132,16 @@ def bf16_normal(shape, std: float, *, seed: int, workload: int, linear: int,
 
 
 def linear_inputs(wl: Workload, li: int, *, seed: int = 0, tokens: int | None = None,
-                  dtype: str = "bf16"):
+                  dtype: str = "bf16", with_weight: bool = True):
     """All inputs of linear `li` of workload `wl` (numpy; the 16-bit tensors as
-    uint16 bit patterns of `dtype`, "bf16" or "fp16")."""
+    uint16 bit patterns of `dtype`, "bf16" or "fp16").  with_weight=False
+    skips the float32 weight (every other draw is unchanged)."""
     lin = wl.linears[li]
     t = wl.tokens if tokens is None else tokens
     n, k, r = lin.out_features, lin.in_features, wl.rank
-    out = {
-        "w": weight(n, k, seed=seed, workload=wl.index, linear=li, outliers=wl.outliers),
-    }
+    out = {}
+    if with_weight:
+        out["w"] = weight(n, k, seed=seed, workload=wl.index, linear=li, outliers=wl.outliers)
     if r > 0:
         out["a"] = bf16_normal((r, k), float(np.sqrt(1.0 / r)), seed=seed, workload=wl.index,
                                linear=li, kind=KIND_A, dtype=dtype)
