@@ -738,8 +738,9 @@ def main():
     if want(TRAIN_65B):
         log(f"timing {TRAIN_65B} fwd+bwd")
         configs[TRAIN_65B], w65 = training_config(TRAIN_65B, ev, dev, args.steps, args.warmup,
-                                                  args.warmup_seconds,
-                                                  keep_weights=want(DECODE_65B))
+                                                  args.warmup_seconds, keep_weights=True)
+        if not want(DECODE_65B):
+            w65 = None
     if want(DECODE_65B):
         # the decode block is the same 65B-style block (same weight draws) at 16 tokens
         log(f"timing {DECODE_65B} forward (skinny path)")

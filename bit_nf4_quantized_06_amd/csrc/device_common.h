@@ -225,4 +225,52 @@ __device__ __forceinline__ f32x16v_t mfma32x32(const u32x4_t& a, const u32x4_t& 
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Last-arriving workgroup of a split reduction.  The workgroups that write
+// partial sums of one output tile each arrive at a 64-bit word in the
+// caller's workspace after their partial stores; the one that completes the
+// count reduces the partials in a fixed order and writes the result, so the
+// reduction needs no dependent kernel launch and stays deterministic.
+//
+// word = (epoch << 32) | arrivals.  Every call of an entry point carries its
+// own non-zero epoch (a process-wide counter on the host), so a word left by
+// any earlier call, or never written, is recognised as stale by its tag and
+// restarted at 1: the workspace needs no zeroing.  The last arriver resets
+// the word to (epoch, 0), so a captured graph, which replays one epoch, also
+// counts from 0 on every replay.
+//
+// Ordering across the XCDs: every thread releases its partial stores at
+// device scope before the workgroup barrier (the L2 of the writer's XCD is
+// written back), the arrival is a device-scope acquire-release atomic, and
+// the last workgroup acquires at device scope before reading the partials
+// (its own XCD's L2 is invalidated).  Nothing waits for another workgroup,
+// so no schedule of the workgroups can stall.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool arrive_last(unsigned long long* word, uint32_t epoch, uint32_t n,
+                                            uint32_t* sh_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long nxt;
+    do {
+      nxt = ((uint32_t)(cur >> 32) == epoch) ? cur + 1ull
+                                              : (((unsigned long long)epoch << 32) | 1ull);
+    } while (!__hip_atomic_compare_exchange_weak(word, &cur, nxt, __ATOMIC_ACQ_REL,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    *sh_flag = ((uint32_t)nxt == n) ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool last = *sh_flag != 0u;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// The last arriver, once done with the partials: restart the count.
+__device__ __forceinline__ void arrival_reset(unsigned long long* word, uint32_t epoch) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(word, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace qlora
