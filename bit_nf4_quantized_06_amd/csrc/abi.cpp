@@ -58,24 +58,12 @@ hipError_t timed(int which, hipStream_t st, F&& launch) {
   return e;
 }
 
-std::atomic<uint32_t> g_epoch{0};
-
 template <typename T>
 T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
 }  // namespace
-
-namespace qlora {
-
-uint32_t next_epoch() {
-  uint32_t e = g_epoch.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  if (e == 0u) e = g_epoch.fetch_add(1u, std::memory_order_relaxed) + 1u;   // never 0
-  return e;
-}
-
-}  // namespace qlora
 
 namespace {
 
@@ -88,27 +76,17 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
                                const uint16_t* Xa, int64_t T, const uint16_t* A,
                                const uint16_t* B, int32_t r, float scale, float inv,
                                uint16_t* Y, uint16_t* U_save, void* ws, const LinearWs& L,
-                               uint32_t epoch, hipStream_t st) {
+                               hipStream_t st) {
   uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * U)
-  ProjArgs pa;
-  pa.L = Xa;
-  pa.R = A;
-  pa.r_by_rows = false;
-  pa.T = T;
-  pa.red = d.cols;
-  pa.r = r;
-  pa.splits = L.s_proj_x;
-  pa.P = ws_ptr<float>(ws, L.proj_off);
-  pa.out_rm = U_save;
-  pa.out_sc = Us;
-  pa.scale = scale * inv;
-  pa.scale_rm = inv;
-  pa.f16 = d.f16;
-  pa.counters = ws_ptr<unsigned long long>(ws, L.cnt_proj_off);
-  pa.epoch = epoch;
-  TransposeJobs none;
-  none.n = 0;
-  hipError_t e = launch_lora_proj(pa, none, st);
+  float* P = ws_ptr<float>(ws, L.proj_off);
+  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
+  if (e == hipSuccess) {
+    TransposeJobs none;
+    none.n = 0;
+    e = launch_lora_proj_reduce(
+        ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0, d.f16}, none,
+        st);
+  }
   if (e == hipSuccess) {
     GemmArgs g;
     g.act = X;
@@ -131,15 +109,15 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
   return e;
 }
 
-// Backward: G = dY B (Gn = bf16(inv G), Gs = bf16(s inv G)) with the A^T
-// transpose in the same launch, U if not saved, dX = dY dequant(W) + keep *
-// (Gs A) in the fused GEMM, then dA = s Gn^T Xa and dB = s dY^T U.  Without
-// dropout Xa = X, inv = 1 and keep = NULL.
+// Backward: G = dY B (Gn = bf16(inv G), Gs = bf16(s inv G)), the A^T
+// transpose, U if not saved, dX = dY dequant(W) + keep * (Gs A) in the fused
+// GEMM, then dA = s Gn^T Xa and dB = s dY^T U.  Without dropout Xa = X,
+// inv = 1 and keep = NULL.
 hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uint16_t* Xa,
                        const uint16_t* dY, int64_t T, const uint16_t* A, const uint16_t* B,
                        int32_t r, float scale, float inv, const uint8_t* keep,
                        const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
-                       const LinearWs& L, uint32_t epoch, hipStream_t st) {
+                       const LinearWs& L, hipStream_t st) {
   uint16_t* At = ws_ptr<uint16_t>(ws, L.at_off);    // [cols, r]
   uint16_t* Gs = ws_ptr<uint16_t>(ws, L.g_off);     // [T, r] bf16(s inv dY B)
   uint16_t* Gn = ws_ptr<uint16_t>(ws, L.gn_off);    // [T, r] bf16(inv dY B)
@@ -149,42 +127,24 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
   // G = dY B (B read in place as [rows, r]); its reduction writes the dX
   // seed's left operand and dA's, and the same launch transposes A for the
   // dX seed
-  ProjArgs pg;
-  pg.L = dY;
-  pg.R = B;
-  pg.r_by_rows = true;
-  pg.T = T;
-  pg.red = d.rows;
-  pg.r = r;
-  pg.splits = L.s_proj_dy;
-  pg.P = P;
-  pg.out_rm = Gn;
-  pg.out_sc = Gs;
-  pg.scale = scale * inv;
-  pg.scale_rm = inv;
-  pg.f16 = d.f16;
-  pg.counters = ws_ptr<unsigned long long>(ws, L.cnt_projb_off);
-  pg.epoch = epoch;
-  TransposeJobs tj;
-  tj.n = 1;
-  tj.job[0] = TransposeJob{A, r, d.cols, At, r};
-  hipError_t e = launch_lora_proj(pg, tj, st);
+  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
+  if (e == hipSuccess) {
+    TransposeJobs tj;
+    tj.n = 1;
+    tj.job[0] = TransposeJob{A, r, d.cols, At, r};
+    e = launch_lora_proj_reduce(
+        ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0, d.f16}, tj, st);
+  }
   // U for dB when the forward's U was not kept: recompute inv Xa A^T
   const uint16_t* U = U_saved;
   if (e == hipSuccess && !U_saved) {
-    ProjArgs pu = pg;
-    pu.L = Xa;
-    pu.R = A;
-    pu.r_by_rows = false;
-    pu.red = d.cols;
-    pu.splits = L.s_proj_x;
-    pu.out_rm = Un;
-    pu.out_sc = nullptr;
-    pu.scale = 0.0f;
-    pu.counters = ws_ptr<unsigned long long>(ws, L.cnt_un_off);
-    TransposeJobs none;
-    none.n = 0;
-    e = launch_lora_proj(pu, none, st);
+    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
+    if (e == hipSuccess) {
+      TransposeJobs none;
+      none.n = 0;
+      e = launch_lora_proj_reduce(
+          ProjReduce{P, T, r, L.s_proj_x, Un, nullptr, 0.0f, inv, nullptr, 0, d.f16}, none, st);
+    }
     U = Un;
   }
   if (e == hipSuccess) {
@@ -206,15 +166,15 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
     g.f16 = d.f16;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
-  // dA = s Gn^T Xa and dB = s dY^T U in one launch, each column tile
-  // reduced by its last-arriving split
+  // dA = s Gn^T Xa and dB = s dY^T U: partials of both in one launch, then
+  // one fixed-order reduction
   if (e == hipSuccess) {
     GradJobs gj;
     gj.n = 2;
     gj.job[0] = GradJob{Gn, Xa, d.cols, ws_ptr<float>(ws, L.grad_off), dA, 0};
     gj.job[1] = GradJob{U, dY, d.rows, ws_ptr<float>(ws, L.grad_b_off), dB, 1};
-    e = launch_lora_grad(gj, T, r, L.s_grad, scale, d.f16,
-                         ws_ptr<unsigned long long>(ws, L.cnt_grad_off), epoch, st);
+    e = launch_lora_grad_partial(gj, T, r, L.s_grad, d.f16, st);
+    if (e == hipSuccess) e = launch_lora_grad_reduce(gj, r, L.s_grad, scale, st);
   }
   return e;
 }
@@ -435,8 +395,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
         timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_gemv(ga, st); });
     return e == hipSuccess ? QLORA_OK : hip_fail(e);
   }
-  const hipError_t e = enqueue_fwd_general(w, d, X, X, T, A, B, r, scale, 1.0f, Y, U_save, ws, L,
-                                           next_epoch(), st);
+  const hipError_t e =
+      enqueue_fwd_general(w, d, X, X, T, A, B, r, scale, 1.0f, Y, U_save, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -459,7 +419,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, cons
   if (s != QLORA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = enqueue_bwd(w, d, X, dY, T, A, B, r, alpha / (float)r, 1.0f, nullptr,
-                                   U_saved, dX, dA, dB, ws, L, next_epoch(), st);
+                                   U_saved, dX, dA, dB, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -513,7 +473,7 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   hipError_t e = enqueue_dropout(k, T, d.cols, X, Xd, keep, true, st);
   if (e == hipSuccess)
     e = enqueue_fwd_general(w, d, X, Xd, T, A, B, r, alpha / (float)r, k.inv_keep, Y, U_save,
-                            ws, L, next_epoch(), st);
+                            ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -559,7 +519,7 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   }
   if (e == hipSuccess)
     e = enqueue_bwd(w, d, Xa, dY, T, A, B, r, alpha / (float)r, k.inv_keep, keep, U_saved, dX,
-                    dA, dB, ws, L, next_epoch(), st);
+                    dA, dB, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

@@ -43,9 +43,6 @@ struct LinearWs {
   int s_gemv;       // split count of the skinny forward (0: fused GEMM path)
   size_t proj_off, u_off, gemv_off, gemv_u_off, at_off, g_off, gn_off, un_off, grad_off, grad_b_off;
   size_t xd_off, keep_off;   // lora_dropout: dropped input [T, cols] bf16 and the packed mask
-  // arrival words of the split reductions: forward projection, backward
-  // projection, recomputed U, adapter gradients ([2][column tiles])
-  size_t cnt_proj_off, cnt_projb_off, cnt_un_off, cnt_grad_off;
   size_t total;
 };
 // With dropout the forward always takes the general path and the layout
@@ -54,10 +51,6 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd,
                           bool dropout = false);
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
-
-// Non-zero tag of one enqueued call (process-wide counter): the split
-// reductions' arrival words recognise stale contents by it.
-uint32_t next_epoch();
 
 // lora_dropout: shape rule of a [T, cols] input (cols % 64 == 0, T * cols
 // bf16 below 2 GiB), bytes of its packed keep mask, and the kernel constants

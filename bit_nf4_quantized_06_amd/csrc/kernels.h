@@ -117,11 +117,13 @@ struct MergeArgs {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 // --- LoRA side products (lora.hip) ----------------------------------------
-// Each split reduction is finished by its last-arriving workgroup (see
-// arrive_last in device_common.h): `counters` points to 64-bit arrival words
-// in the caller's workspace (one per output tile, any initial contents) and
-// `epoch` is the call's non-zero tag.
-//
+// Split-reduction partials P[s][t][p] = sum_{k in chunk s} L[t][k] R(p, k),
+// L [T, red] bf16, P float32 [S][T][r]; R is [r, red] (R(p, k) = R[p][k]) or,
+// with r_by_rows, [red, r] (R(p, k) = R[k][p]), read in place.
+int lora_proj_splits(int64_t T, int64_t red, int32_t r);
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
+                                    bool f16, hipStream_t stream);
 // bf16 transposes: out[c][r'] = in[r'][c] for an [R, C] input; out has row
 // stride ld_out and is zero for R <= r' < ld_out.
 struct TransposeJob {
@@ -133,40 +135,32 @@ struct TransposeJob {
 struct TransposeJobs {
   TransposeJob job[3];
   int tiles[3];   // filled by the launcher
-  int total;      // filled by the launcher
   int n;
 };
-// Rank-r projection v[t][p] = sum_k L[t][k] R(p, k), L [T, red] bf16, R is
-// [r, red] (R(p, k) = R[p][k]) or, with r_by_rows, [red, r] (R(p, k) =
-// R[k][p]), read in place.  Split over `splits` chunks of the reduction
-// (float32 partials P [S][T][r]), summed in the fixed order s = 0, 1, ...
-// Outputs (each may be NULL): out_rm[t][p] = round16(scale_rm v),
-// out_sc[t][p] = round16(scale v).  The same launch runs the transposes of
-// `tj` (tj.n may be 0).
-struct ProjArgs {
-  const uint16_t* L;
-  const uint16_t* R;
-  bool r_by_rows;
-  int64_t T, red;
+// v = sum_s P[s] (fixed order s = 0, 1, ...).  Each output may be NULL:
+// out_rm[t][p] = bf16(scale_rm * v), out_sc[t][p] = bf16(scale * v),
+// out_tr[p][t] = bf16(scale_rm * v) with row stride ld_tr and zeros for
+// T <= t < ld_tr.  The same launch runs the transposes of `tj` (tj.n may
+// be 0).
+struct ProjReduce {
+  const float* P;
+  int64_t T;
   int32_t r;
   int32_t splits;
-  float* P;
   uint16_t* out_rm;
   uint16_t* out_sc;
   float scale;
   float scale_rm;          // 1 except under lora_dropout (1 / (1 - p))
+  uint16_t* out_tr;
+  int64_t ld_tr;
   bool f16;                // outputs fp16 (else bf16)
-  unsigned long long* counters;   // [ceil(T / 128)]
-  uint32_t epoch;
 };
-int lora_proj_splits(int64_t T, int64_t red, int32_t r);
-hipError_t launch_lora_proj(const ProjArgs& a, TransposeJobs tj, hipStream_t stream);
+hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream);
 
-// Adapter gradients, up to two problems per launch: out = scale * sum_t S[t][p]
-// L[t][q] with S [T, r] and L [T, Q] bf16 (token-major), stored [r, Q]
-// (transposed == 0) or [Q, r] (transposed != 0); split over tokens with
-// float32 partials P [S] in the output's layout.  counters:
-// [n][ceil(max Q / 128)].
+// Adapter-gradient partials and their reduction, up to two problems per
+// launch: P[s] = sum_{t in chunk s} S[t][p] L[t][q] with S [T, r] and L [T, Q]
+// bf16 (token-major), stored [r, Q] (transposed == 0) or [Q, r]
+// (transposed != 0); then out = scale * sum_s P[s] in the same layout.
 struct GradJob {
   const uint16_t* S;
   const uint16_t* L;
@@ -180,9 +174,10 @@ struct GradJobs {
   int n;
 };
 int lora_grad_splits(int64_t T, int64_t Q);
-hipError_t launch_lora_grad(GradJobs jobs, int64_t T, int32_t r, int splits, float scale,
-                            bool f16, unsigned long long* counters, uint32_t epoch,
-                            hipStream_t stream);
+hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits, bool f16,
+                                    hipStream_t stream);
+hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
+                                   hipStream_t stream);
 
 // n float32 zeros at p (n % 4 == 0, p 16-byte aligned).
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);

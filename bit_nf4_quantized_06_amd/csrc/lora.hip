@@ -148,87 +148,12 @@ __device__ __forceinline__ void proj_iter(const ProjCtx<NJ, kRT>& c, int it, uin
 #endif
 }
 
-// bf16 transpose of one 32 x 32 tile of the jobs in `jobs` (tile index b
-// over all jobs): out[c][r'] = in[r'][c], zeros for R <= r' < ld_out.
-__device__ void transpose_tile(const TransposeJobs& jobs, int b) {
-  __shared__ uint16_t tile[32][33];
-  int jdx = 0;
-  while (jdx < jobs.n - 1 && b >= jobs.tiles[jdx]) {
-    b -= jobs.tiles[jdx];
-    ++jdx;
-  }
-  const TransposeJob& jb = jobs.job[jdx];
-  const int64_t tiles_c = (jb.C + 31) / 32;
-  const int64_t c0 = (int64_t)(b % tiles_c) * 32;
-  const int64_t r0 = (int64_t)(b / tiles_c) * 32;
-  const int tx = threadIdx.x & 31;
-  const int ty = threadIdx.x >> 5;   // 0..7
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t rr = r0 + ty + 8 * k;
-    const int64_t cc = c0 + tx;
-    tile[ty + 8 * k][tx] = (rr < jb.R && cc < jb.C) ? jb.in[rr * jb.C + cc] : (uint16_t)0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t cc = c0 + ty + 8 * k;
-    const int64_t rr = r0 + tx;
-    if (cc < jb.C && rr < jb.ld_out) jb.out[cc * jb.ld_out + rr] = tile[tx][ty + 8 * k];
-  }
-}
-
-// Reduction of one 128-token tile by its last-arriving workgroup: v = P[0] +
-// P[1] + ... (fixed split order, four consecutive outputs per thread), then
-// out_rm = round16(scale_rm v) and out_sc = round16(scale v).
-template <int NJ, bool kF16>
-__device__ __forceinline__ void proj_reduce_tile(const ProjArgs& a, int64_t t0) {
-  constexpr int R = 16 * NJ;
-  const int64_t rows = (a.T - t0) < 128 ? (a.T - t0) : 128;
-  const int64_t nel = rows * R;
-  const int64_t stride = a.T * R / 4;   // one split, in float4
-  for (int64_t i = (int64_t)threadIdx.x * 4; i < nel; i += 256 * 4) {
-    const int64_t idx = t0 * R + i;
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.P + idx);
-    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int sp = 0;
-    for (; sp + 8 <= a.splits; sp += 8) {
-      f32x4_t x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = __builtin_nontemporal_load(src + (int64_t)(sp + j) * stride);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v += x[j];
-    }
-    for (; sp < a.splits; ++sp) v += __builtin_nontemporal_load(src + (int64_t)sp * stride);
-    if (a.out_rm)
-      *reinterpret_cast<uint2*>(a.out_rm + idx) =
-          uint2{pack16x2<kF16>(v[0] * a.scale_rm, v[1] * a.scale_rm),
-                pack16x2<kF16>(v[2] * a.scale_rm, v[3] * a.scale_rm)};
-    if (a.out_sc)
-      *reinterpret_cast<uint2*>(a.out_sc + idx) =
-          uint2{pack16x2<kF16>(v[0] * a.scale, v[1] * a.scale),
-                pack16x2<kF16>(v[2] * a.scale, v[3] * a.scale)};
-  }
-}
-
-// Grid: (token tiles of 128, splits + transpose rows).  Rows y < splits are
-// the projection's workgroups; the rows past them run the bf16 transposes of
-// `tj` (32 x 32 tiles), small layout changes the next kernels need.
 template <int NJ, bool kRT, bool kF16>
-__global__ __launch_bounds__(256) void lora_proj_kernel(ProjArgs a, TransposeJobs tj,
-                                                        int64_t chunk) {
+__global__ __launch_bounds__(256) void lora_proj_partial_kernel(
+    const uint16_t* __restrict__ L, const uint16_t* __restrict__ R, int64_t T, int64_t red,
+    int64_t chunk, float* __restrict__ P) {
   // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
 #if defined(__HIP_DEVICE_COMPILE__)
-  if ((int)blockIdx.y >= a.splits) {
-    const int tb = ((int)blockIdx.y - a.splits) * (int)gridDim.x + (int)blockIdx.x;
-    if (tb < tj.total) transpose_tile(tj, tb);
-    return;
-  }
-  const uint16_t* __restrict__ L = a.L;
-  const uint16_t* __restrict__ R = a.R;
-  const int64_t T = a.T, red = a.red;
-  float* __restrict__ P = a.P;
-  __shared__ uint32_t last_flag;
   constexpr int kStage = 16 * NJ * 128;   // bf16 elements
   __shared__ __attribute__((aligned(1024))) uint16_t s0[kStage];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[kStage];
@@ -305,11 +230,6 @@ __global__ __launch_bounds__(256) void lora_proj_kernel(ProjArgs a, TransposeJob
         const int64_t t = m0 + 16 * g + 4 * (c.lane >> 4) + e;
         if (t < T) out[t * (16 * NJ) + 16 * j + (c.lane & 15)] = acc[g][j][e];
       }
-  // the split that completes this token tile reduces it
-  if (arrive_last(a.counters + blockIdx.x, a.epoch, (uint32_t)a.splits, &last_flag)) {
-    proj_reduce_tile<NJ, kF16>(a, (int64_t)blockIdx.x * 128);
-    arrival_reset(a.counters + blockIdx.x, a.epoch);
-  }
 #endif
 }
 
@@ -319,26 +239,20 @@ static int64_t proj_chunk(int64_t red, int splits) {
 }
 
 template <bool kF16>
-static hipError_t proj_dispatch(const ProjArgs& a, TransposeJobs tj, hipStream_t stream) {
-  const int64_t chunk = proj_chunk(a.red, a.splits);
-  const unsigned tiles = (unsigned)((a.T + 127) / 128);
-  tj.total = 0;
-  for (int i = 0; i < tj.n; ++i) {
-    const TransposeJob& j = tj.job[i];
-    tj.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
-    tj.total += tj.tiles[i];
-  }
-  const unsigned trows = (unsigned)((tj.total + tiles - 1) / tiles);
-  const dim3 grid(tiles, (unsigned)a.splits + trows);
-  switch ((a.r >> 4) * 2 + (a.r_by_rows ? 1 : 0)) {
-#define QLORA_PROJ_CASE(NJ)                                                                 \
-  case 2 * NJ:                                                                              \
-    hipLaunchKernelGGL((lora_proj_kernel<NJ, false, kF16>), grid, dim3(256), 0, stream, a,  \
-                       tj, chunk);                                                          \
-    break;                                                                                  \
-  case 2 * NJ + 1:                                                                          \
-    hipLaunchKernelGGL((lora_proj_kernel<NJ, true, kF16>), grid, dim3(256), 0, stream, a,   \
-                       tj, chunk);                                                          \
+static hipError_t proj_partial_dispatch(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                        int64_t T, int64_t red, int32_t r, int splits, float* P,
+                                        hipStream_t stream) {
+  const int64_t chunk = proj_chunk(red, splits);
+  const dim3 grid((unsigned)((T + 127) / 128), (unsigned)splits);
+  switch ((r >> 4) * 2 + (r_by_rows ? 1 : 0)) {
+#define QLORA_PROJ_CASE(NJ)                                                                   \
+  case 2 * NJ:                                                                                \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, false, kF16>), grid, dim3(256), 0, stream, \
+                       L, R, T, red, chunk, P);                                               \
+    break;                                                                                    \
+  case 2 * NJ + 1:                                                                            \
+    hipLaunchKernelGGL((lora_proj_partial_kernel<NJ, true, kF16>), grid, dim3(256), 0, stream, \
+                       L, R, T, red, chunk, P);                                               \
     break;
     QLORA_PROJ_CASE(1) QLORA_PROJ_CASE(2) QLORA_PROJ_CASE(3) QLORA_PROJ_CASE(4)
     QLORA_PROJ_CASE(5) QLORA_PROJ_CASE(6) QLORA_PROJ_CASE(7) QLORA_PROJ_CASE(8)
@@ -348,9 +262,110 @@ static hipError_t proj_dispatch(const ProjArgs& a, TransposeJobs tj, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_lora_proj(const ProjArgs& a, TransposeJobs tj, hipStream_t stream) {
-  if (a.splits < 1 || a.T < 1) return hipErrorInvalidValue;
-  return a.f16 ? proj_dispatch<true>(a, tj, stream) : proj_dispatch<false>(a, tj, stream);
+hipError_t launch_lora_proj_partial(const uint16_t* L, const uint16_t* R, bool r_by_rows,
+                                    int64_t T, int64_t red, int32_t r, int splits, float* P,
+                                    bool f16, hipStream_t stream) {
+  return f16 ? proj_partial_dispatch<true>(L, R, r_by_rows, T, red, r, splits, P, stream)
+             : proj_partial_dispatch<false>(L, R, r_by_rows, T, red, r, splits, P, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order sum of the split partials, v = P[0] + P[1] + ... + P[S-1], for
+// four consecutive outputs (t, p .. p + 3) per thread (16-byte loads, 8
+// splits in flight).  Writes any of: out_rm[t][p] = bf16(v), out_sc[t][p] =
+// bf16(scale * v) (the pre-scaled operand the fused GEMM seeds its
+// accumulators with), out_tr[p][t] = bf16(v) with row stride ld_tr and zeros
+// for T <= t < ld_tr.  Workgroups past the reduction run the bf16 transposes
+// of `tj` (32 x 32 tiles through LDS), so small layout changes the next
+// kernels need ride along in the same launch.
+// ---------------------------------------------------------------------------
+__device__ void transpose_tile(const TransposeJobs& jobs, int b) {
+  __shared__ uint16_t tile[32][33];
+  int jdx = 0;
+  while (jdx < jobs.n - 1 && b >= jobs.tiles[jdx]) {
+    b -= jobs.tiles[jdx];
+    ++jdx;
+  }
+  const TransposeJob& jb = jobs.job[jdx];
+  const int64_t tiles_c = (jb.C + 31) / 32;
+  const int64_t c0 = (int64_t)(b % tiles_c) * 32;
+  const int64_t r0 = (int64_t)(b / tiles_c) * 32;
+  const int tx = threadIdx.x & 31;
+  const int ty = threadIdx.x >> 5;   // 0..7
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t rr = r0 + ty + 8 * k;
+    const int64_t cc = c0 + tx;
+    tile[ty + 8 * k][tx] = (rr < jb.R && cc < jb.C) ? jb.in[rr * jb.C + cc] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t cc = c0 + ty + 8 * k;
+    const int64_t rr = r0 + tx;
+    if (cc < jb.C && rr < jb.ld_out) jb.out[cc * jb.ld_out + rr] = tile[tx][ty + 8 * k];
+  }
+}
+
+__global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, TransposeJobs tj,
+                                                               unsigned reduce_blocks) {
+  if (blockIdx.x >= reduce_blocks) {
+    transpose_tile(tj, (int)(blockIdx.x - reduce_blocks));
+    return;
+  }
+  const int64_t rows_total = a.out_tr ? a.ld_tr : a.T;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= rows_total * a.r) return;
+  const int64_t t = i / a.r;
+  const int p = (int)(i - t * a.r);
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (t < a.T) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.P + i);
+    const int64_t stride = a.T * a.r / 4;
+    int s = 0;
+    for (; s + 8 <= a.splits; s += 8) {
+      f32x4_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += x[j];
+    }
+    for (; s < a.splits; ++s) v += src[(int64_t)s * stride];
+  }
+  uint16_t b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    b[e] = (uint16_t)((a.f16 ? pack_f16x2(v[e] * a.scale_rm, 0.0f)
+                             : pack_bf16x2(v[e] * a.scale_rm, 0.0f)) & 0xFFFFu);
+  if (t < a.T) {
+    if (a.out_rm)
+      *reinterpret_cast<uint2*>(a.out_rm + i) =
+          uint2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+    if (a.out_sc)
+      *reinterpret_cast<uint2*>(a.out_sc + i) =
+          a.f16 ? uint2{pack_f16x2(v[0] * a.scale, v[1] * a.scale),
+                        pack_f16x2(v[2] * a.scale, v[3] * a.scale)}
+                : uint2{pack_bf16x2(v[0] * a.scale, v[1] * a.scale),
+                        pack_bf16x2(v[2] * a.scale, v[3] * a.scale)};
+  }
+  if (a.out_tr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a.out_tr[(int64_t)(p + e) * a.ld_tr + t] = b[e];
+  }
+}
+
+hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream) {
+  const int64_t rows_total = a.out_tr ? a.ld_tr : a.T;
+  const unsigned nred = (unsigned)((rows_total * a.r / 4 + 255) / 256);
+  int ttiles = 0;
+  for (int i = 0; i < tj.n; ++i) {
+    const TransposeJob& j = tj.job[i];
+    tj.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
+    ttiles += tj.tiles[i];
+  }
+  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3(nred + (unsigned)ttiles), dim3(256), 0, stream,
+                     a, tj, nred);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -461,49 +476,11 @@ __device__ __forceinline__ void grad_iter(const GradCtx<NP>& c, int it, uint16_t
 #endif
 }
 
-// Reduction of one 128-column tile of job `jb` by its last-arriving split:
-// out = scale * (P[0] + P[1] + ...) in the fixed split order, in the
-// partials' own layout ([r, Q], or [Q, r] for a transposed job).
-template <int NP>
-__device__ __forceinline__ void grad_reduce_tile(const GradJob& jb, int64_t q0, int splits,
-                                                 float scale) {
-  constexpr int R = 16 * NP;
-  const int64_t qn = (jb.Q - q0) < 128 ? (jb.Q - q0) : 128;   // a multiple of 16
-  const int64_t stride = R * jb.Q / 4;                          // one split, in float4
-  const int64_t n4 = qn * R / 4;
-  for (int64_t k = threadIdx.x; k < n4; k += 256) {
-    // transposed: element 4k of the tile's contiguous [qn, r] block;
-    // otherwise row p = 4k / qn, columns q0 + (4k % qn) .. + 3
-    int64_t idx;
-    if (jb.transposed) {
-      idx = q0 * R + 4 * k;
-    } else {
-      const int64_t p = (4 * k) / qn;
-      idx = p * jb.Q + q0 + (4 * k - p * qn);
-    }
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(jb.P + idx);
-    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-      f32x4_t x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = __builtin_nontemporal_load(src + (int64_t)(sp + j) * stride);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v += x[j];
-    }
-    for (; sp < splits; ++sp) v += __builtin_nontemporal_load(src + (int64_t)sp * stride);
-    *reinterpret_cast<f32x4_t*>(jb.out + idx) = v * scale;
-  }
-}
-
 template <int NP, bool kF16>
-__global__ __launch_bounds__(256) void lora_grad_kernel(GradJobs jobs, int64_t T, int64_t chunk,
-                                                        float scale,
-                                                        unsigned long long* counters,
-                                                        uint32_t epoch) {
+__global__ __launch_bounds__(256) void lora_grad_partial_kernel(GradJobs jobs, int64_t T,
+                                                               int64_t chunk) {
   // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ uint32_t last_flag;
   __shared__ __attribute__((aligned(1024))) uint16_t l0[64 * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t l1[64 * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t l2[64 * 128];
@@ -577,12 +554,6 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradJobs jobs, int64_t T
       }
     }
   }
-  // the split that completes this column tile reduces it
-  unsigned long long* word = counters + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
-  if (arrive_last(word, epoch, gridDim.y, &last_flag)) {
-    grad_reduce_tile<NP>(jb, q0, (int)gridDim.y, scale);
-    arrival_reset(word, epoch);
-  }
 #endif
 }
 
@@ -591,9 +562,8 @@ static int64_t grad_chunk(int64_t T, int splits) {
   return (c + 63) / 64 * 64;
 }
 
-hipError_t launch_lora_grad(GradJobs jobs, int64_t T, int32_t r, int splits, float scale,
-                            bool f16, unsigned long long* counters, uint32_t epoch,
-                            hipStream_t stream) {
+hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int splits,
+                                    bool f16, hipStream_t stream) {
   const int64_t chunk = grad_chunk(T, splits);
   int64_t qmax = 0;
   for (int i = 0; i < jobs.n; ++i) qmax = jobs.job[i].Q > qmax ? jobs.job[i].Q : qmax;
@@ -602,17 +572,55 @@ hipError_t launch_lora_grad(GradJobs jobs, int64_t T, int32_t r, int splits, flo
 #define QLORA_GRAD_CASE(NP)                                                                  \
   case NP:                                                                                   \
     if (f16)                                                                                 \
-      hipLaunchKernelGGL((lora_grad_kernel<NP, true>), grid, dim3(256), 0, stream, jobs, T,  \
-                         chunk, scale, counters, epoch);                                     \
+      hipLaunchKernelGGL((lora_grad_partial_kernel<NP, true>), grid, dim3(256), 0, stream,   \
+                         jobs, T, chunk);                                                    \
     else                                                                                     \
-      hipLaunchKernelGGL((lora_grad_kernel<NP, false>), grid, dim3(256), 0, stream, jobs, T, \
-                         chunk, scale, counters, epoch);                                     \
+      hipLaunchKernelGGL((lora_grad_partial_kernel<NP, false>), grid, dim3(256), 0, stream,  \
+                         jobs, T, chunk);                                                    \
     break;
     QLORA_GRAD_CASE(1) QLORA_GRAD_CASE(2) QLORA_GRAD_CASE(3) QLORA_GRAD_CASE(4)
     QLORA_GRAD_CASE(5) QLORA_GRAD_CASE(6) QLORA_GRAD_CASE(7) QLORA_GRAD_CASE(8)
 #undef QLORA_GRAD_CASE
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// out[i] = scale * (P[0][i] + P[1][i] + ...) (fixed order) for each job; the
+// partials already have the output's layout ([r, Q], or [Q, r] for a
+// transposed job).  Four outputs per thread, 8 splits in flight; all jobs in
+// one launch.
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradJobs jobs, int r, int splits,
+                                                               float scale) {
+  int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  int jdx = 0;
+  while (jdx < jobs.n && i >= (int64_t)r * jobs.job[jdx].Q) {
+    i -= (int64_t)r * jobs.job[jdx].Q;
+    ++jdx;
+  }
+  if (jdx >= jobs.n) return;
+  const GradJob& jb = jobs.job[jdx];
+  const int64_t stride = (int64_t)r * jb.Q / 4;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(jb.P + i);
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    f32x4_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += x[j];
+  }
+  for (; s < splits; ++s) v += src[(int64_t)s * stride];
+  *reinterpret_cast<f32x4_t*>(jb.out + i) = v * scale;
+}
+
+hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
+                                   hipStream_t stream) {
+  int64_t n = 0;
+  for (int i = 0; i < jobs.n; ++i) n += (int64_t)r * jobs.job[i].Q;
+  hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                     stream, jobs, r, splits, scale);
   return hipGetLastError();
 }
 

@@ -176,21 +176,6 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, b
     L.keep_off = off;
     off += align_up(dropout_mask_bytes(T, d.cols), kWsAlign);
   }
-  // 64-bit arrival words of the split reductions (any initial contents): one
-  // per 128-token tile of each projection, one per 128-column tile of each
-  // adapter gradient
-  const size_t ttiles = (size_t)((T + 127) / 128);
-  const size_t qtiles = (size_t)(((d.cols > d.rows ? d.cols : d.rows) + 127) / 128);
-  L.cnt_proj_off = off;
-  off += align_up(8 * ttiles, kWsAlign);
-  if (bwd) {
-    L.cnt_projb_off = off;
-    off += align_up(8 * ttiles, kWsAlign);
-    L.cnt_un_off = off;
-    off += align_up(8 * ttiles, kWsAlign);
-    L.cnt_grad_off = off;
-    off += align_up(8 * 2 * qtiles, kWsAlign);
-  }
   L.total = off;
   return L;
 }
