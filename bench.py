@@ -348,6 +348,41 @@ def time_steps(ls, ev, steps, warmup, warmup_s, kernel_timing=True):
     return res
 
 
+def time_graph(ls, ev, steps):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed `steps` times: the per-call host work (argument checks, kernel
+    launches) leaves the timed region, as in a serving loop.  Returns ms per
+    step, or None if capture fails."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            ls.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ls.step()
+        torch.cuda.synchronize()
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
+        return None
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(max(3, steps // 4)):
+        g.replay()
+    torch.cuda.synchronize()
+    start, stop = ev.new(fence=True), ev.new(fence=True)
+    ev.record(start, stream)
+    for _ in range(steps):
+        g.replay()
+    ev.record(stop, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(start, stop) / steps
+    del g
+    return ms
+
+
 def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
     """fwd+bwd TFLOP/s of a training workload and the roofline of its
     dominant fused GEMM (achieved = its algorithmic flops over its event-timed
@@ -384,6 +419,10 @@ def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
         "kernels_ms_per_step": {k: round(v[0]["total_ms"], 4) for k, v in kern.items()},
         "ms_per_step_with_kernel_events": round(tm["ms_per_step_with_kernel_events"], 4),
     }
+    gms = time_graph(ls, ev, steps)
+    if gms is not None:
+        out["graph_replay"] = {"ms_per_step": round(gms, 4),
+                               "TFLOPs": round(fl / (gms / 1e3) / 1e12, 2)}
     weights = [it["wq"] for it in ls.items] if keep_weights else None
     del ls
     torch.cuda.empty_cache()
@@ -420,6 +459,11 @@ def decode_config(name, ev, dev, steps, warmup, warmup_s, weights=None):
                      "launches_per_step": kt["launches"], "source_digest": digest},
         "ms_per_step_with_kernel_events": round(tm["ms_per_step_with_kernel_events"], 4),
     }
+    gms = time_graph(ls, ev, steps)
+    if gms is not None:
+        gg = by / (gms / 1e3) / 1e9
+        out["graph_replay"] = {"ms_per_step": round(gms, 4), "GBps": round(gg, 1),
+                               "hbm_frac": round(gg / PEAK_HBM_GBPS, 4)}
     del ls
     torch.cuda.empty_cache()
     return out

@@ -43,13 +43,15 @@ def _stream_scoped(fn):
     (Allocated on another stream, the block could be reused by that stream
     while the kernels still read and write it.)"""
     sig = inspect.signature(fn)
+    pos = list(sig.parameters).index("stream")
 
     @functools.wraps(fn)
     def wrapper(*args, **kw):
-        ba = sig.bind(*args, **kw)
-        stream = ba.arguments.get("stream")
+        # fast path (no signature binding): no stream given
+        stream = args[pos] if len(args) > pos else kw.get("stream")
         if stream is None:
             return fn(*args, **kw)
+        ba = sig.bind(*args, **kw)
         ba.arguments["stream"] = None
         with torch.cuda.stream(_as_torch_stream(stream)):
             return fn(*ba.args, **ba.kwargs)
@@ -57,6 +59,8 @@ def _stream_scoped(fn):
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> None:
+    if t.dtype == dtype and t.shape == shape and t.device == device and t.is_contiguous():
+        return
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -121,13 +125,19 @@ class NF4Weight:
         return torch.float16 if self.compute_dtype == "fp16" else torch.bfloat16
 
     def descriptor(self) -> _lib.Nf4WeightDesc:
+        """The C descriptor of this weight, built once and rebuilt only when a
+        field changes (a call's host work stays small next to its kernels)."""
+        key = (self.rows, self.cols, self.quant_type, self.double_quant, self.compute_dtype,
+               self.codes.data_ptr(), self.absmax_code.data_ptr(),
+               self.absmax_scale.data_ptr(), self.absmax_offset.data_ptr())
+        cached = self.__dict__.get("_desc")
+        if cached is not None and cached[0] == key:
+            return cached[1]
         d = _lib.Nf4WeightDesc()
         NF4Weight._init(d, self.rows, self.cols, self.quant_type, self.double_quant,
                         self.compute_dtype)
-        d.codes = self.codes.data_ptr()
-        d.absmax_code = self.absmax_code.data_ptr()
-        d.absmax_scale = self.absmax_scale.data_ptr()
-        d.absmax_offset = self.absmax_offset.data_ptr()
+        d.codes, d.absmax_code, d.absmax_scale, d.absmax_offset = key[5:]
+        self.__dict__["_desc"] = (key, d)
         return d
 
 
@@ -238,6 +248,7 @@ def qlora_adamw_step16(param: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: t
                                       float(weight_decay), _stream(stream)))
 
 
+@functools.lru_cache(maxsize=256)
 def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -> int:
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 
@@ -266,8 +277,8 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
         U_save = torch.empty(T, r, dtype=w.dtype16, device=dev)
     if U_save is not None:
         _need(U_save, "U_save", w.dtype16, (T, r), dev)
-    ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 0)
     if workspace is None:
+        ws_bytes = qlora_linear_workspace(T, w.rows, w.cols, r, False)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     desc = w.descriptor()
     _lib.check("qlora_linear_fwd",
@@ -303,8 +314,8 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     _need(dX, "dX", w.dtype16, (T, w.cols), dev)
     _need(dA, "dA", torch.float32, (r, w.cols), dev)
     _need(dB, "dB", torch.float32, (w.rows, r), dev)
-    ws_bytes = lib.qlora_linear_workspace(T, w.rows, w.cols, r, 1)
     if workspace is None:
+        ws_bytes = qlora_linear_workspace(T, w.rows, w.cols, r, True)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     desc = w.descriptor()
     _lib.check("qlora_linear_bwd",
