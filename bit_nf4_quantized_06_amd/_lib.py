@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf
 QLORA_OK = 0
 STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
                 4: "QLORA_ERR_WORKSPACE", 5: "QLORA_ERR_DEVICE", 6: "QLORA_ERR_HIP",
-                7: "QLORA_ERR_FORMAT"}
+                7: "QLORA_ERR_FORMAT", 8: "QLORA_ERR_SCRATCH"}
 FORMAT_VERSION = 1
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
@@ -72,6 +72,9 @@ SIGNATURES = {
     "qlora_linear_workspace": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_int]),
     "qlora_linear_fwd": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P,
                                         _P, _SZ, _P]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float,
+                                                _P, _P, _P]),
+    "qlora_linear_fwd_noalloc_max_scratch": (_SZ, []),
     "qlora_linear_bwd": (ctypes.c_int, [_DESC_P, _P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P,
                                         _P, _P, _P, _P, _SZ, _P]),
     "qlora_dropout_mask_bytes": (_SZ, [_I64, _I64]),

@@ -288,6 +288,30 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     return Y, U_save
 
 
+def qlora_linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             alpha: float, Y: torch.Tensor, U_save: torch.Tensor | None = None,
+                             stream=None):
+    """qlora_linear_fwd_noalloc: the forward with the library's fixed device
+    array as workspace (for callers that cannot allocate, e.g. under graph
+    capture).  Y (and U_save, if wanted) must be given; nothing is allocated."""
+    lib = _lib.load()
+    T = X.shape[0]
+    r = A.shape[0]
+    dev = w.device
+    _need(X, "X", w.dtype16, (T, w.cols), dev)
+    _need(A, "A", w.dtype16, (r, w.cols), dev)
+    _need(B, "B", w.dtype16, (w.rows, r), dev)
+    _need(Y, "Y", w.dtype16, (T, w.rows), dev)
+    if U_save is not None:
+        _need(U_save, "U_save", w.dtype16, (T, r), dev)
+    desc = w.descriptor()
+    _lib.check("qlora_linear_fwd_noalloc",
+               lib.qlora_linear_fwd_noalloc(ctypes.byref(desc), X.data_ptr(), T, A.data_ptr(),
+                                            B.data_ptr(), r, float(alpha), Y.data_ptr(),
+                                            _ptr(U_save), _stream(stream)))
+    return Y, U_save
+
+
 @_stream_scoped
 def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
                      B: torch.Tensor, alpha: float, U_saved: torch.Tensor | None = None,

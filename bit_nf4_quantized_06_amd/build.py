@@ -22,7 +22,7 @@ LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 HIP_SOURCES = ["quantize.hip", "lora.hip", "gemm.hip", "gemv.hip", "merge.hip", "adamw.hip",
-               "dropout.hip"]
+               "dropout.hip", "noalloc.hip"]
 HOST_SOURCES = ["abi.cpp", "validate.cpp"]
 ARCH = "gfx950"
 

@@ -23,7 +23,7 @@ qlora_status hip_fail(hipError_t e) {
   return QLORA_ERR_HIP;
 }
 
-qlora_status check_device() {
+qlora_status check_device_impl() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -64,6 +64,14 @@ T* ws_ptr(void* ws, size_t off) {
 }
 
 }  // namespace
+
+namespace qlora {
+
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+
+qlora_status check_device() { return check_device_impl(); }
+
+}  // namespace qlora
 
 namespace {
 

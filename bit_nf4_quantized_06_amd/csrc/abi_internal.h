@@ -52,6 +52,12 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd,
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
 
+// Records the hipError_t that qlora_last_hip_error reports for this thread.
+void set_last_hip_error(int e);
+
+// QLORA_OK if the current device is a gfx950 GPU (cached per device).
+qlora_status check_device();
+
 // lora_dropout: shape rule of a [T, cols] input (cols % 64 == 0, T * cols
 // bf16 below 2 GiB), bytes of its packed keep mask, and the kernel constants
 // of a qlora_dropout (QLORA_ERR_NULL / QLORA_ERR_SHAPE for a NULL pointer or

@@ -324,6 +324,9 @@ const char* qlora_status_string(qlora_status s) {
     case QLORA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
     case QLORA_ERR_HIP: return "a HIP runtime call failed";
     case QLORA_ERR_FORMAT: return "weight descriptor has a wrong format version or block size";
+    case QLORA_ERR_SCRATCH:
+      return "the call needs more workspace than qlora_linear_fwd_noalloc's fixed device array "
+             "(qlora_linear_fwd_noalloc_max_scratch bytes); use qlora_linear_fwd with a workspace";
   }
   return "unknown status";
 }

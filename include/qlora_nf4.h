@@ -59,8 +59,10 @@ typedef enum {
   QLORA_ERR_WORKSPACE = 4,  /* workspace smaller than the matching *_workspace() */
   QLORA_ERR_DEVICE = 5,     /* the current device is not a gfx950 GPU           */
   QLORA_ERR_HIP = 6,        /* a HIP runtime call failed; see qlora_last_hip_error */
-  QLORA_ERR_FORMAT = 7      /* weight descriptor has a wrong version/blocksize,
+  QLORA_ERR_FORMAT = 7,     /* weight descriptor has a wrong version/blocksize,
                                an unknown variant, or a variant the call does not take */
+  QLORA_ERR_SCRATCH = 8     /* qlora_linear_fwd_noalloc: the call needs more workspace
+                               than its fixed device array holds */
 } qlora_status;
 
 /*
@@ -253,6 +255,25 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
                               const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
                               uint16_t *Y, uint16_t *U_save, void *ws, size_t ws_bytes,
                               void *stream);
+
+/*
+ * qlora_linear_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (the same kernels, bit for bit) and errors as
+ * qlora_linear_fwd, without a workspace argument: the workspace is a fixed
+ * array of qlora_linear_fwd_noalloc_max_scratch() bytes (32 MiB) that the
+ * library holds in device memory on every GPU it runs on, until the process
+ * ends.  The call allocates and frees nothing.  QLORA_ERR_SCRATCH (before any
+ * device work) when qlora_linear_workspace(T, rows, cols, r, 0) exceeds that
+ * size.  All calls on one GPU share its array: calls that overlap on one GPU
+ * (on two streams at once) race; calls ordered on one stream do not.  The
+ * first call on a device resolves the array's address (hipGetSymbolAddress),
+ * which a caller under graph capture should do once before capturing.
+ */
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
+                                      const uint16_t *A, const uint16_t *B, int32_t r,
+                                      float alpha, uint16_t *Y, uint16_t *U_save, void *stream);
+size_t qlora_linear_fwd_noalloc_max_scratch(void);
 
 /*
  * Backward of the same layer for an upstream gradient dY; there is no

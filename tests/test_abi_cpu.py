@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -362,3 +362,21 @@ def test_status_strings():
     for s in range(0, 8):
         assert lib.qlora_status_string(s)
     assert lib.qlora_status_string(99) == b"unknown status"
+
+
+def test_noalloc_forward_rejects_oversize_on_the_host():
+    """qlora_linear_fwd_noalloc takes its workspace from a fixed device array
+    (qlora_linear_fwd_noalloc_max_scratch bytes); a call that would need more
+    is rejected with QLORA_ERR_SCRATCH before any device work, and the usual
+    argument errors come first."""
+    lib = _lib.load()
+    cap = lib.qlora_linear_fwd_noalloc_max_scratch()
+    assert cap == 32 << 20
+    f = lib.qlora_linear_fwd_noalloc
+    # 131072 tokens of a 4096 x 4096 weight at r = 128 need more than the array
+    assert lib.qlora_linear_workspace(131072, 4096, 4096, 128, 0) > cap
+    d = _desc(4096, 4096)
+    assert f(ctypes.byref(d), FAKE, 131072, FAKE, FAKE, 128, 32.0, FAKE, None, None) == 8
+    assert b"qlora_linear_fwd_noalloc" in lib.qlora_status_string(8)
+    assert f(None, FAKE, 16, FAKE, FAKE, 16, 32.0, FAKE, None, None) == 1     # NULL weight
+    assert f(ctypes.byref(d), FAKE, 16, FAKE, FAKE, 24, 32.0, FAKE, None, None) == 2   # bad r
