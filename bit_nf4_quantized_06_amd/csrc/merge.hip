@@ -5,28 +5,45 @@
 // w_hat the bf16 dequantised weight, B [rows, r] and A [r, cols] bf16, the
 // product accumulated in float32, scaled and added in float32, rounded once
 // to bf16.  (Variants: fp16 in place of bf16 throughout, float32 block
-// constants without double quantisation, the evenly spaced INT4 codebook.)  (waylandz LLM book 26.2: at inference the adapter is folded into
-// the weight once, W + (alpha/r) B A; ta-paperlens 落とし穴 and the
-// Ultralytics QLoRA page, Kompromisse: the merge is done on the base
-// dequantised to 16 bit, and the result may be quantised again.)
+// constants without double quantisation, the evenly spaced INT4 codebook.)
+// (waylandz LLM book 26.2: at inference the adapter is folded into the
+// weight once, W + (alpha/r) B A; ta-paperlens 落とし穴 and the Ultralytics
+// QLoRA page, Kompromisse: the merge is done on the base dequantised to 16
+// bit, and the result may be quantised again.)
 //
 // Bound by HBM: per weight it reads half a byte of codes and writes two bytes
 // of bf16; the rank-r product (r multiply-adds per weight) runs on MFMA.
 //
-// Workgroup = 4 waves over 256 columns and a group of 256 rows, walked 32
-// rows at a time.  The 256-column slice of A stays in LDS for the whole
-// group (row stride padded by 16 bytes); each wave forms (B A) for the 32
-// rows x its 64 columns with MFMA 32x32x16, B fragments straight from
-// memory (8 consecutive r of one row), A fragments through ds_read_b64_tr_b16
-// (8 consecutive r of one column).  s * (B A) goes to LDS in float32, laid
-// out per consumer thread (36 floats, 16-byte aligned, 9 distinct 16-byte
-// bank groups per 16 threads); then each thread decodes four 8-weight
-// chunks of one row, 64 columns apart, adds its 32 values and writes four
-// 16-byte pieces: 8 neighbouring threads fill whole 128-byte lines with each
-// store (16-byte pieces at a 64-byte stride, as a thread-contiguous layout
-// gives, measured 25% slower, twice as slow with non-temporal stores).  The codes, block
-// constant inputs and B fragments of the next pass are loaded while the
-// current one runs.
+// Workgroup = 8 waves over a tile of 256 columns x 256 rows; wave w owns
+// the 32-row block w.  Every load of the workgroup goes out at its start --
+// the tile's 256-column slice of A (for LDS, row stride 576 bytes, so the
+// transposed fragment reads below hit 64 distinct banks per 32 lanes), then
+// each wave's B fragments, codes and block-constant inputs -- so the A
+// slice's wait before the one workgroup barrier leaves the row loads in
+// flight.  The codes arrive as whole 128-byte lines (8 lanes a row) and are
+// redistributed through the wave's LDS tile.  All of a row block's loads
+// complete before its first store, so no wait on a load ever waits on a
+// store.
+//
+// A wave walks its 8 column sub-tiles of 32.  A sub-tile is one MFMA
+// 32x32x16 chain over r with the A fragment first (8 consecutive r of one
+// column, ds_read_b64_tr_b16) and the B fragment second (8 consecutive r of
+// one row), so the float32 product lands with one weight row per lane pair:
+// lane l and l + 32 hold row l % 32, columns 4 h + 8 g + [0, 4) (h = l / 32,
+// g = 0..3).  Two v_permlane32_swap per accumulator quad regroup it so that
+// lane l holds columns [0, 16) and lane l + 32 columns [16, 32) of its row:
+// 16 consecutive weights of one block.  The block's 16-entry table q[k] * c'
+// (rounded to 16 bit) is built by the lane pair in registers, 8 entries each,
+// and looked up with byte permutes straight into float32 patterns; the next
+// sub-tile's MFMA chain is issued before this one's VALU work.  The rounded
+// results of two sub-tiles (32 rows x 64 columns) pass through the wave's
+// LDS tile (16-byte chunks XOR-swizzled by row) and leave in whole 128-byte
+// rows, 8 lanes a row: stores that cover a quarter line each ran 30% slower.
+//
+// Tiles are numbered so that the tiles one XCD receives (dispatch is
+// round-robin over the 8 XCDs) walk down the rows of one column slice: the
+// A slice is fetched once per XCD and column slice, and B (rows x r) stays
+// in each XCD's L2.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,19 +51,12 @@ namespace qlora {
 
 namespace {
 
-constexpr int kMergeCols = 256;   // columns per workgroup
-constexpr int kMergeRows = 256;   // rows per workgroup
-constexpr int kTileRows = 32;     // rows per pass
-constexpr int kASlice = 264;      // A slice row stride in elements (256 + 8)
-constexpr int kDStride = 36;      // floats per consumer thread in the delta buffer
+constexpr int kMergeCols = 256;   // columns per workgroup tile
+constexpr int kMergeRows = 256;   // rows per workgroup tile
+constexpr int kASlice = 288;      // A slice row stride in elements (256 + 32)
+constexpr int kMergeWaves = 8;    // one 32-row block per wave
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-template <bool kF16>
-__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b,
-                                           const f32x16_t& c) {
-  return mfma32x32<kF16>(a, b, c);
-}
 
 __device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t* p1) {
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
@@ -56,204 +66,304 @@ __device__ __forceinline__ u32x4_t ld_tr_pair(const uint16_t* p0, const uint16_t
   return u32x4_t{l.x, l.y, h.x, h.y};
 }
 
-// float32 value of x rounded to the 16-bit compute type (nearest even)
+// Table of one row's block: the 16 entries q[k] * c' (float32 product, one
+// rounding to the 16-bit type, as the bulk dequantiser) as byte planes for
+// v_perm lookups.  Lanes l and l + 32 hold the same row and block: lane half
+// h forms entries 8h .. 8h+7 (kq = those levels) and the halves are
+// exchanged with v_permlane32_swap.
 template <bool kF16>
-__device__ __forceinline__ float round16(float x) {
-  return lo16_to_f32<kF16>(pack16x2<kF16>(x, 0.0f));
+__device__ __forceinline__ Nf4Lut merge_lut(float cp, const float kq[8]) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pack16x2<kF16>(__fmul_rn(kq[2 * j], cp), __fmul_rn(kq[2 * j + 1], cp));
+  const uint32_t lo_a = perm(p[1], p[0], 0x06040200u);
+  const uint32_t lo_b = perm(p[3], p[2], 0x06040200u);
+  const uint32_t hi_a = perm(p[1], p[0], 0x07050301u);
+  const uint32_t hi_b = perm(p[3], p[2], 0x07050301u);
+  // permlane32_swap(x, x): first result = lower half's x in every lane,
+  // second = upper half's x in every lane
+  const auto sa = __builtin_amdgcn_permlane32_swap(lo_a, lo_a, false, false);
+  const auto sb = __builtin_amdgcn_permlane32_swap(lo_b, lo_b, false, false);
+  const auto sc = __builtin_amdgcn_permlane32_swap(hi_a, hi_a, false, false);
+  const auto sd = __builtin_amdgcn_permlane32_swap(hi_b, hi_b, false, false);
+  Nf4Lut t;
+  t.lo[0] = sa[0];
+  t.lo[1] = sb[0];
+  t.lo[2] = sa[1];
+  t.lo[3] = sb[1];
+  t.hi[0] = sc[0];
+  t.hi[1] = sd[0];
+  t.hi[2] = sc[1];
+  t.hi[3] = sd[1];
+  return t;
+}
+
+// The 8 codes of word w (element i in bits 4i..4i+3) as the float32 values
+// of their 16-bit table entries.  bf16: the entry's two bytes become the
+// upper half of the float32 pattern (v_perm selector 0x0C gives a zero
+// byte); fp16: the 16-bit pattern is converted.
+template <bool kF16>
+__device__ __forceinline__ void dequant8_f32(const Nf4Lut& t, uint32_t w, float out[8]) {
+  uint32_t elo, ehi, olo, ohi;
+  lut4(t, w & 0x0F0F0F0Fu, elo, ehi);           // elements 0, 2, 4, 6
+  lut4(t, (w >> 4) & 0x0F0F0F0Fu, olo, ohi);    // elements 1, 3, 5, 7
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!kF16) {
+      const uint32_t sel = ((4u + j) << 24) | ((uint32_t)j << 16) | 0x0C0Cu;
+      out[2 * j] = __uint_as_float(perm(ehi, elo, sel));
+      out[2 * j + 1] = __uint_as_float(perm(ohi, olo, sel));
+    } else {
+      const uint32_t sel = 0x0C0C0000u | ((4u + j) << 8) | (uint32_t)j;
+      out[2 * j] = lo16_to_f32<true>(perm(ehi, elo, sel));
+      out[2 * j + 1] = lo16_to_f32<true>(perm(ohi, olo, sel));
+    }
+  }
+}
+
+// Block-constant inputs of one lane's row for the tile's 4 blocks (256
+// columns).  Row and column are clamped into the weight, so every load is
+// unconditional; values of clamped rows or blocks are never stored.
+struct MergeConsts {
+  uint32_t c8[4];   // 8-bit constant code of block b
+  float s2[4];      // its group scale (float32 block constant without DQ)
+};
+
+template <bool kDQ>
+__device__ __forceinline__ void merge_const_loads(const MergeArgs& a, int64_t nc, int64_t k0,
+                                                  MergeConsts& m) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    int64_t col = k0 + 64 * b;
+    col = col < a.cols ? col : a.cols - 64;
+    const int64_t blk = (nc * a.cols + col) >> 6;
+    if (kDQ) {
+      m.c8[b] = a.code8[blk];
+      m.s2[b] = a.s2[blk >> 8];
+    } else {
+      m.c8[b] = 0u;
+      m.s2[b] = a.s2[blk];
+    }
+  }
+}
+
+// Byte offset of the 8-byte code piece (chunk c = tile columns 32 c .. +32,
+// half h) of row `row` in a wave's staging tile of a row block's codes
+// (32 rows x 128 bytes): chunks XOR-swizzled by row bits 1..3 and halves by
+// row bit 4, so 32 lanes reading one chunk of 32 rows hit 64 distinct banks
+// and 8 lanes writing one row's 8 chunks hit distinct banks.
+__device__ __forceinline__ int code_slot(int row, int c, int h) {
+  return row * 128 + ((c ^ ((row >> 1) & 7)) << 4) + ((h ^ ((row >> 4) & 1)) << 3);
 }
 
 }  // namespace
 
-// Loads of one 32-row pass: this thread's codes and block-constant inputs
-// (consumer role) and its B fragments (MFMA role).  The consumer thread owns
-// four 8-column chunks of one row, 64 columns apart (columns kb + 64 w +
-// [0, 8), w = 0..3), i.e. one chunk in each of four consecutive blocks: 8
-// neighbouring threads then write whole 128-byte lines with each store, the
-// four 8-bit constant codes are one 4-byte load and the group scale is
-// shared.  Row and column indices are clamped into the weight, so every
-// load is unconditional (no branch, no serialising wait); values of clamped
-// rows or chunks are never stored.  (The four blocks need not start at a
-// multiple of 4 nor lie in one group of 256, so each has its own loads.)
+// Loads of one wave's 32-row block: B fragments, the codes as whole lines
+// (chunk c = tile columns 32 c .. +32 of rows 8 it + lane / 8) and the block
+// constant inputs.  Rows and columns are clamped into the weight; values of
+// clamped rows and columns are never stored.
 template <int NP>
-struct MergePass {
-  uint32_t cw[4];           // 8 codes of chunk w
-  uint32_t c8[4];           // 8-bit constant code of chunk w's block
-  float s2[4];              // group scale of chunk w's block
+struct MergeRowIn {
   u32x4_t bf[NP];
+  u32x4_t cc[4];
+  MergeConsts m;
 };
 
-struct MergeCtx {
-  const uint16_t* as;
-  float* dl;
-  const float* q;
-  const float* dmine;
-  float mu;
-  int crow, l32, lhi, wave, prow, acol[2];
-  int64_t kb;               // first column of chunk 0
-  int64_t kclamp[4];        // chunk w's first column, clamped into the weight
-  bool wok[4];              // chunk w lies inside the weight
-};
-
-// kDQ false: s2[w] receives chunk w's block constant itself (float32, one
-// per block) and there is no 8-bit code.
 template <int NP, bool kDQ>
-__device__ __forceinline__ void merge_load(const MergeArgs& a, const MergeCtx& c, int64_t n0,
-                                           MergePass<NP>& m) {
-  const int64_t last = a.rows - 1;
-  const int64_t n = n0 + c.crow < last ? n0 + c.crow : last;
-  const int64_t rowe = n * a.cols;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int64_t e0 = rowe + c.kclamp[w];
-    m.cw[w] = *reinterpret_cast<const uint32_t*>(a.codes + e0 / 2);
-    if (kDQ) {
-      m.c8[w] = a.code8[e0 >> 6];
-      m.s2[w] = a.s2[e0 >> 14];
-    } else {
-      m.c8[w] = 0u;
-      m.s2[w] = a.s2[e0 >> 6];
-    }
-  }
-  const int64_t bn = n0 + c.l32 < last ? n0 + c.l32 : last;
+__device__ __forceinline__ void merge_row_issue(const MergeArgs& a, int64_t n0, int64_t k0,
+                                                int lane, MergeRowIn<NP>& in) {
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int64_t n = n0 + l32;
+  const int64_t nc = n < a.rows ? n : a.rows - 1;
 #pragma unroll
   for (int j = 0; j < NP; ++j)
-    m.bf[j] = *reinterpret_cast<const u32x4_t*>(a.B + bn * (16 * NP) + 16 * j + 8 * c.lhi);
+    in.bf[j] = *reinterpret_cast<const u32x4_t*>(a.B + nc * (16 * NP) + 16 * j + 8 * lhi);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    int64_t gn = n0 + 8 * it + (lane >> 3);
+    gn = gn < a.rows ? gn : a.rows - 1;
+    int64_t col = k0 + 32 * (lane & 7);
+    col = col < a.cols ? col : a.cols - 32;
+    in.cc[it] = *reinterpret_cast<const u32x4_t*>(a.codes + ((gn * a.cols + col) >> 1));
+  }
+  merge_const_loads<kDQ>(a, nc, k0, in.m);
 }
 
-// One 32-row pass from `cur`; the loads of the pass after it go to `nxt`
-// first.  The two register sets alternate between passes (no copy, so
-// nothing waits for the loads or for the previous pass's stores).
+// One 32-row block: the 8 sub-tiles of 32 columns, each an MFMA chain over r
+// for s * (B A), the table lookups and the add, out through the wave's
+// staging tile.
 template <int NP, bool kDQ, bool kF16>
-__device__ __forceinline__ void merge_pass(const MergeArgs& a, const MergeCtx& c, int64_t n0,
-                                           const MergePass<NP>& cur, MergePass<NP>& nxt) {
-  merge_load<NP, kDQ>(a, c, n0 + kTileRows, nxt);
-  f32x16_t acc[2];
+__device__ __forceinline__ void merge_row_process(const MergeArgs& a, const uint16_t* as,
+                                                  uint16_t* stg, int64_t n0, int64_t k0,
+                                                  int lane, float mu, const float kq[8],
+                                                  const MergeRowIn<NP>& in) {
+  const int l32 = lane & 31, lhi = lane >> 5;
+  // A fragment of sub-tile s, slice j: rows 16 j + prow (+4), column 32 s + acol
+  const int prow = 8 * lhi + ((lane & 15) >> 2);
+  const int acol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // the codes through the staging tile into 8 bytes per lane and sub-tile
+  // (the wave reads only what it wrote, and its LDS operations complete in
+  // order: no barrier); rows 16..31 (it >= 2) store their halves swapped
+  uint2 cw[8];
+  {
+    unsigned char* sb = reinterpret_cast<unsigned char*>(stg);
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t* p = c.as + (16 * j + c.prow) * kASlice + c.acol[t];
-      acc[t] = mfma32<kF16>(cur.bf[j], ld_tr_pair(p, p + 4 * kASlice), acc[t]);
+    for (int it = 0; it < 4; ++it) {
+      const int row = 8 * it + (lane >> 3);
+      const u32x4_t v = in.cc[it];
+      const u32x4_t w = it >= 2 ? u32x4_t{v[2], v[3], v[0], v[1]} : v;
+      *reinterpret_cast<u32x4_t*>(sb + code_slot(row, lane & 7, 0) - (((row >> 4) & 1) << 3)) = w;
     }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      cw[st] = *reinterpret_cast<const uint2*>(sb + code_slot(l32, st, lhi));
   }
-  // acc[t][e] = (B A)[row 8 (e / 4) + 4 lhi + e % 4][column 64 wave + 32 t + l32];
-  // column col belongs to consumer thread 8 row + (col / 8) % 8, element
-  // 8 (col / 64) + col % 8 of its 32
+  float cps[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int col = 64 * c.wave + 32 * t + c.l32;
-    const int slot = (col >> 3) & 7;
-    const int elem = 8 * (col >> 6) + (col & 7);
+  for (int b = 0; b < 4; ++b)
+    cps[b] = kDQ ? block_constant(in.m.c8[b], in.m.s2[b], mu) : in.m.s2[b];
+  // forced here: every load of the row block completes before its first
+  // store, so no later wait on a load also waits on stores
+  asm volatile("" ::"v"(cps[0]), "v"(cps[1]), "v"(cps[2]), "v"(cps[3]));
+  auto product = [&](int st) {
+    f32x16_t acc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * c.lhi + (e & 3);
-      c.dl[(row * 8 + slot) * kDStride + elem] = __fmul_rn(acc[t][e], a.scale);
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const uint16_t* p = as + (16 * j + prow) * kASlice + 32 * st + acol;
+      acc = mfma32x32<kF16>(ld_tr_pair(p, p + 4 * kASlice), in.bf[j], acc);
     }
-  }
-  __syncthreads();
-  u32x4_t d4[8];
+    return acc;
+  };
+  f32x16_t acc_next = product(0);
+  Nf4Lut lut;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) d4[j] = *reinterpret_cast<const u32x4_t*>(c.dmine + 4 * j);
-  const int64_t n = n0 + c.crow;
-  const bool row_ok = n < a.rows;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float cp = kDQ ? block_constant(cur.c8[w], cur.s2[w], c.mu) : cur.s2[w];
-    u32x4_t o;
+  for (int s = 0; s < 8; ++s) {
+    // the next sub-tile's MFMAs run while this one's VALU work issues
+    const f32x16_t acc = acc_next;
+    if (s < 7) acc_next = product(s + 1);
+    // acc[4 g + e]: row l32, column 8 g + 4 lhi + e.  After the swaps v[i]
+    // is column 16 lhi + i.
+    float v[16];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 8 * w + 2 * e;   // element index within the 32
-      const float lo = round16<kF16>(__fmul_rn(c.q[(cur.cw[w] >> (8 * e)) & 15u], cp));
-      const float hi = round16<kF16>(__fmul_rn(c.q[(cur.cw[w] >> (8 * e + 4)) & 15u], cp));
-      const float dlo = __uint_as_float(d4[i >> 2][i & 3]);
-      const float dhi = __uint_as_float(d4[(i + 1) >> 2][(i + 1) & 3]);
-      o[e] = pack16x2<kF16>(__fadd_rn(lo, dlo), __fadd_rn(hi, dhi));
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]),
+                                                      __float_as_uint(acc[8 + e]), false, false);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[4 + e]),
+                                                      __float_as_uint(acc[12 + e]), false, false);
+      v[e] = __uint_as_float(x[0]);
+      v[4 + e] = __uint_as_float(x[1]);
+      v[8 + e] = __uint_as_float(y[0]);
+      v[12 + e] = __uint_as_float(y[1]);
     }
-    if (row_ok && c.wok[w])
-      *reinterpret_cast<u32x4_t*>(a.out + n * a.cols + c.kb + 64 * w) = o;
+    // sub-tiles 2b and 2b + 1 of a row share block b
+    if ((s & 1) == 0) lut = merge_lut<kF16>(cps[s >> 1], kq);
+    const uint32_t words[2] = {cw[s].x, cw[s].y};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float base[8];
+      dequant8_f32<kF16>(lut, words[w], base);
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * w + 2 * e;
+        o[e] = pack16x2<kF16>(__fadd_rn(base[2 * e], __fmul_rn(v[i], a.scale)),
+                              __fadd_rn(base[2 * e + 1], __fmul_rn(v[i + 1], a.scale)));
+      }
+      // 16-byte chunk 4 (s & 1) + 2 lhi + w of this row in the staging tile
+      const int ch = 4 * (s & 1) + 2 * lhi + w;
+      *reinterpret_cast<u32x4_t*>(stg + l32 * 64 + ((ch ^ (l32 & 7)) << 3)) = o;
+    }
+    if (s & 1) {
+      // the pair of sub-tiles (64 columns) back out in whole 128-byte rows:
+      // 8 lanes per row, 8 rows per store
+      const int ch = lane & 7;
+      const int64_t col = k0 + 32 * (s - 1) + 8 * ch;
+      u32x4_t o[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = 8 * it + (lane >> 3);
+        o[it] = *reinterpret_cast<const u32x4_t*>(stg + row * 64 + ((ch ^ (row & 7)) << 3));
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int64_t gn = n0 + 8 * it + (lane >> 3);
+        if (gn < a.rows && col < a.cols)
+          *reinterpret_cast<u32x4_t*>(a.out + gn * a.cols + col) = o[it];
+      }
+    }
   }
-  __syncthreads();   // the delta buffer is rewritten by the next pass
 }
 
 template <int NP, bool kDQ, bool kF16>
-__global__ __launch_bounds__(256) void nf4_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(64 * kMergeWaves) void nf4_merge_kernel(MergeArgs a, int n_ct, int n_rt) {
   // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int R = 16 * NP;
   __shared__ __attribute__((aligned(16))) uint16_t as[R * kASlice];
-  __shared__ __attribute__((aligned(16))) float dl[256 * kDStride];
-  __shared__ float q[16];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kMergeWaves][32 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  MergeCtx c;
-  c.as = as;
-  c.dl = dl;
-  c.q = q;
-  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  c.l32 = lane & 31;
-  c.lhi = lane >> 5;
-  const int64_t k0 = (int64_t)blockIdx.x * kMergeCols;
-  const int64_t nb = (int64_t)blockIdx.y * kMergeRows;
-  const int64_t ne = nb + kMergeRows < a.rows ? nb + kMergeRows : a.rows;
-  if (tid < 16) q[tid] = a.qt ? kINT4[tid] : kNF4[tid];
-  // the A slice; columns past the weight read a clamped column, and only
-  // feed columns that are never stored
-  for (int i = tid; i < R * 32; i += 256) {
-    const int p = i >> 5;
-    const int ch = i & 31;
-    const int64_t k = k0 + 8 * ch < a.cols ? k0 + 8 * ch : a.cols - 8;
-    *reinterpret_cast<u32x4_t*>(as + p * kASlice + 8 * ch) =
-        *reinterpret_cast<const u32x4_t*>(a.A + (int64_t)p * a.cols + k);
-  }
-  c.mu = kDQ ? a.mu[0] : 0.0f;
-  // consumer role: row crow of the pass, chunks at columns kb + 64 w
-  c.crow = tid >> 3;
-  c.kb = k0 + 8 * (tid & 7);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    c.wok[w] = k0 + 64 * w < a.cols;
-    c.kclamp[w] = (c.wok[w] ? k0 + 64 * w : a.cols - 64) + 8 * (tid & 7);
-  }
-  c.dmine = dl + tid * kDStride;
-  // MFMA role: 32 rows x columns 64 wave + 32 t + [0, 32)
-  c.prow = 8 * c.lhi + ((lane & 15) >> 2);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    c.acol[t] = 64 * c.wave + 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* stg = stage[wave];   // this wave's 32 x 64 staging tile
 
-  MergePass<NP> p0, p1;
-  merge_load<NP, kDQ>(a, c, nb, p0);
-  __syncthreads();   // A slice and table visible
-  if (ne - nb == kMergeRows) {
-    // a whole row group: straight-line passes, so the waits before each
-    // pass count exactly the loads and stores issued since its own loads
+  // tile: XCD-major, then down the rows of one column slice
+  const int pid = blockIdx.x;
+  const int total = n_ct * n_rt;
+  const int xcd = pid & 7;
+  const int base = total >> 3, rem = total & 7;
+  const int qi = __builtin_amdgcn_readfirstlane(xcd * base + (xcd < rem ? xcd : rem) + (pid >> 3));
+  const int ct = qi / n_rt;
+  const int rt = qi - ct * n_rt;
+  const int64_t k0 = (int64_t)ct * kMergeCols;
+  const int64_t nb = (int64_t)rt * kMergeRows;
+
+  // the A slice first (columns past the weight read a clamped column and
+  // only feed sub-tiles that are never stored), then the row block's loads:
+  // the A slice's wait leaves them in flight
+  // levels 8 lhi .. 8 lhi + 7 of the codebook (uniform loads of both halves,
+  // so no vector load of them waits behind the row loads)
+  float kq[8];
 #pragma unroll
-    for (int i = 0; i < kMergeRows / kTileRows; i += 2) {
-      merge_pass<NP, kDQ, kF16>(a, c, nb + i * kTileRows, p0, p1);
-      merge_pass<NP, kDQ, kF16>(a, c, nb + (i + 1) * kTileRows, p1, p0);
-    }
-  } else {
-    for (int64_t n0 = nb; n0 < ne; n0 += 2 * kTileRows) {
-      merge_pass<NP, kDQ, kF16>(a, c, n0, p0, p1);
-      if (n0 + kTileRows >= ne) break;
-      merge_pass<NP, kDQ, kF16>(a, c, n0 + kTileRows, p1, p0);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const float lo = a.qt ? kINT4[j] : kNF4[j];
+    const float hi = a.qt ? kINT4[8 + j] : kNF4[8 + j];
+    kq[j] = (lane >> 5) ? hi : lo;
   }
+  constexpr int kAIters = R * 32 / (64 * kMergeWaves);
+  u32x4_t av[kAIters];
+#pragma unroll
+  for (int t = 0; t < kAIters; ++t) {
+    const int i = tid + t * 64 * kMergeWaves;
+    const int64_t k = k0 + 8 * (i & 31) < a.cols ? k0 + 8 * (i & 31) : a.cols - 8;
+    av[t] = *reinterpret_cast<const u32x4_t*>(a.A + (int64_t)(i >> 5) * a.cols + k);
+  }
+  MergeRowIn<NP> in0;
+  merge_row_issue<NP, kDQ>(a, nb + 32 * wave, k0, lane, in0);
+#pragma unroll
+  for (int t = 0; t < kAIters; ++t) {
+    const int i = tid + t * 64 * kMergeWaves;
+    *reinterpret_cast<u32x4_t*>(as + (i >> 5) * kASlice + 8 * (i & 31)) = av[t];
+  }
+  const float mu = kDQ ? a.mu[0] : 0.0f;
+  __syncthreads();   // A slice visible
+  if (nb + 32 * wave < a.rows)
+    merge_row_process<NP, kDQ, kF16>(a, as, stg, nb + 32 * wave, k0, lane, mu, kq, in0);
 #endif
 }
 
 template <bool kDQ, bool kF16>
 static hipError_t merge_dispatch(const MergeArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.cols + kMergeCols - 1) / kMergeCols),
-                  (unsigned)((a.rows + kMergeRows - 1) / kMergeRows));
+  const int n_ct = (int)((a.cols + kMergeCols - 1) / kMergeCols);
+  const int n_rt = (int)((a.rows + kMergeRows - 1) / kMergeRows);
+  const dim3 grid((unsigned)n_ct * (unsigned)n_rt);
   switch (a.r >> 4) {
 #define QLORA_MERGE_CASE(NP)                                                                  \
   case NP:                                                                                    \
-    hipLaunchKernelGGL((nf4_merge_kernel<NP, kDQ, kF16>), grid, dim3(256), 0, stream, a);     \
+    hipLaunchKernelGGL((nf4_merge_kernel<NP, kDQ, kF16>), grid, dim3(64 * kMergeWaves), 0, stream, a,      \
+                       n_ct, n_rt);                                                           \
     break;
     QLORA_MERGE_CASE(1) QLORA_MERGE_CASE(2) QLORA_MERGE_CASE(3) QLORA_MERGE_CASE(4)
     QLORA_MERGE_CASE(5) QLORA_MERGE_CASE(6) QLORA_MERGE_CASE(7) QLORA_MERGE_CASE(8)
