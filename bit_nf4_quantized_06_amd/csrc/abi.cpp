@@ -87,13 +87,16 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
                                hipStream_t st) {
   uint16_t* Us = ws_ptr<uint16_t>(ws, L.u_off);     // [T, r] bf16(s * U)
   float* P = ws_ptr<float>(ws, L.proj_off);
+  const int n_split = L.gemm_tiles - L.gemm_split;
+  uint32_t* cnt = n_split > 0 ? ws_ptr<uint32_t>(ws, L.split_cnt_off) : nullptr;
   hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs none;
     none.n = 0;
-    e = launch_lora_proj_reduce(
-        ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0, d.f16}, none,
-        st);
+    // the reduction also zeroes the GEMM's arrival counters
+    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv,
+                                           nullptr, 0, d.f16, cnt, n_split},
+                                none, st);
   }
   if (e == hipSuccess) {
     GemmArgs g;
@@ -112,6 +115,9 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
     g.keep = nullptr;
     g.dq = d.dq;
     g.f16 = d.f16;
+    g.split_from = L.gemm_split;
+    g.part = n_split > 0 ? ws_ptr<float>(ws, L.split_part_off) : nullptr;
+    g.cnt = cnt;
     e = timed(QLORA_TIMING_FWD_GEMM, st, [&] { return launch_qlora_fwd_gemm(g, st); });
   }
   return e;
@@ -131,17 +137,20 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
   uint16_t* Gn = ws_ptr<uint16_t>(ws, L.gn_off);    // [T, r] bf16(inv dY B)
   uint16_t* Un = ws_ptr<uint16_t>(ws, L.un_off);    // [T, r] bf16(inv Xa A^T) if not given
   float* P = ws_ptr<float>(ws, L.proj_off);
+  const int n_split = L.gemm_tiles - L.gemm_split;
+  uint32_t* cnt = n_split > 0 ? ws_ptr<uint32_t>(ws, L.split_cnt_off) : nullptr;
 
   // G = dY B (B read in place as [rows, r]); its reduction writes the dX
-  // seed's left operand and dA's, and the same launch transposes A for the
-  // dX seed
+  // seed's left operand and dA's, transposes A for the dX seed in the same
+  // launch, and zeroes the dX GEMM's arrival counters
   hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs tj;
     tj.n = 1;
     tj.job[0] = TransposeJob{A, r, d.cols, At, r};
-    e = launch_lora_proj_reduce(
-        ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0, d.f16}, tj, st);
+    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv,
+                                           nullptr, 0, d.f16, cnt, n_split},
+                                tj, st);
   }
   // U for dB when the forward's U was not kept: recompute inv Xa A^T
   const uint16_t* U = U_saved;
@@ -172,6 +181,9 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
     g.keep = keep;
     g.dq = d.dq;
     g.f16 = d.f16;
+    g.split_from = L.gemm_split;
+    g.part = n_split > 0 ? ws_ptr<float>(ws, L.split_part_off) : nullptr;
+    g.cnt = cnt;
     e = timed(QLORA_TIMING_DX_GEMM, st, [&] { return launch_qlora_dx_gemm(g, st); });
   }
   // dA = s Gn^T Xa and dB = s dY^T U: partials of both in one launch, then
@@ -360,6 +372,15 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
                               const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                               uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
                               void* stream) {
+  return qlora::linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+qlora_status qlora::linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
+                                    const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                                    uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
+                                    void* stream, bool gemm_split) {
   using namespace qlora;
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
@@ -370,7 +391,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
       (U_save && !aligned16(U_save)))
     return QLORA_ERR_ALIGN;
-  const LinearWs L = linear_ws_layout(T, d, r, false);
+  const LinearWs L = linear_ws_layout(T, d, r, false, false, gemm_split);
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;
@@ -407,6 +428,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
       enqueue_fwd_general(w, d, X, X, T, A, B, r, scale, 1.0f, Y, U_save, ws, L, st);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
+
+extern "C" {
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY,
                               int64_t T, const uint16_t* A, const uint16_t* B, int32_t r,

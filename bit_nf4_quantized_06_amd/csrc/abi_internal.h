@@ -35,6 +35,14 @@ struct QuantWs {
 };
 QuantWs quant_ws_layout(const WeightDims& d);
 
+// K-split of the fused GEMM's last tiles.  The fused GEMM runs one 256 x 256
+// tile per CU at a time; when the tile count leaves a last round at most half
+// full, the tiles of that round are each split into two halves of the
+// reduction (kernel units 2 i and 2 i + 1), so they finish in half a round.
+// Returns the first split tile (the tile count when nothing is split).
+constexpr int kGemmCUs = 256;   // compute units of an MI355X
+int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len);
+
 // Workspace layout of the linear forward / backward.
 struct LinearWs {
   int s_proj_x;     // split count of X A^T over cols
@@ -43,12 +51,19 @@ struct LinearWs {
   int s_gemv;       // split count of the skinny forward (0: fused GEMM path)
   size_t proj_off, u_off, gemv_off, gemv_u_off, at_off, g_off, gn_off, un_off, grad_off, grad_b_off;
   size_t xd_off, keep_off;   // lora_dropout: dropped input [T, cols] bf16 and the packed mask
+  // the fused GEMM's K-split (forward: out = rows, reduction = cols;
+  // backward dX: out = cols, reduction = rows): tiles, first split tile, the
+  // float32 partials (2 x 65536 per split tile) and one arrival counter per
+  // split tile
+  int gemm_tiles, gemm_split;
+  size_t split_part_off, split_cnt_off;
   size_t total;
 };
 // With dropout the forward always takes the general path and the layout
 // adds the dropped input and the keep mask.
+// gemm_split false: no K-split (and no space for it) whatever the shape.
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd,
-                          bool dropout = false);
+                          bool dropout = false, bool gemm_split = true);
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
 
@@ -80,5 +95,12 @@ bool adamw_constants(int64_t step, double lr, double beta1, double beta2, double
 
 qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
                                WeightDims* d);
+
+// qlora_linear_fwd, with the fused GEMM's K-split allowed or not (the
+// allocation-free forward turns it off when its partials would not fit).
+qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
+                             void* stream, bool gemm_split);
 
 }  // namespace qlora

@@ -148,6 +148,7 @@ struct GemmCtx {
   uint16_t* A[kAStages];
   uint16_t* B[kBStages];
   int tid, lane, wave, wm, wn, wg, l32, lhi, nsteps;
+  int kstep0;               // first reduction step of this unit (K-split halves)
   int64_t m0, n0, red_len, kblocks;
   float mu;
   // buffer ranges (base, bytes) of the operands read with range checking
@@ -189,7 +190,7 @@ struct CodeRegs {
 // Steps past the end read nothing (scalar offset beyond the range: zeros).
 template <bool kBwd>
 __device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
-  const uint32_t sbase = step < c.nsteps ? (uint32_t)(step * BK * 2) : kOOB;
+  const uint32_t sbase = step < c.nsteps ? (uint32_t)((c.kstep0 + step) * BK * 2) : kOOB;
   const uint32_t row_bytes = (uint32_t)(c.red_len * 2);
 #pragma unroll
   for (int i = 0; i < kActLoads; ++i) {
@@ -211,9 +212,10 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
   // forward: the block moves along the row (+32 B, +1 block per step);
   // backward: it moves down 64 rows (+64 rows of codes and constants)
   const bool in = step < c.nsteps;
-  const int64_t dblk = kBwd ? (int64_t)step * 64 * c.kblocks : (int64_t)step;
-  const uint32_t dcode = kBwd ? (uint32_t)((int64_t)step * 64 * (c.g.cols >> 1)) : (uint32_t)(step * 32);
-  const int64_t n_ok_rows = c.g.rows - (kBwd ? (int64_t)step * 64 : 0);
+  const int64_t ks = (int64_t)c.kstep0 + step;   // reduction step within the whole weight
+  const int64_t dblk = kBwd ? ks * 64 * c.kblocks : ks;
+  const uint32_t dcode = kBwd ? (uint32_t)(ks * 64 * (c.g.cols >> 1)) : (uint32_t)(ks * 32);
+  const int64_t n_ok_rows = c.g.rows - (kBwd ? ks * 64 : 0);
   r.ok = in && c.w_row_ok && (!kBwd || c.wrow < n_ok_rows);
   const uint32_t scode = in ? dcode : kOOB;
   const int64_t blk = c.blk0 + dblk;
@@ -406,8 +408,19 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   const int64_t out_len = kBwd ? g.cols : g.rows;
   const int mt = (int)((g.T + BM - 1) / BM);
   const int nt = (int)((out_len + BN - 1) / BN);
+  // units past split_from are the two reduction halves of the tiles from
+  // split_from on
+  int q = blockIdx.x;
+  int half = -1;
+  if (q >= g.split_from) {
+    const int u = q - g.split_from;
+    q = g.split_from + (u >> 1);
+    half = u & 1;
+  }
+  q = __builtin_amdgcn_readfirstlane(q);
+  half = __builtin_amdgcn_readfirstlane(half);
   int tm, tn;
-  tile_coords(blockIdx.x, mt, nt, tm, tn);
+  tile_coords(q, mt, nt, tm, tn);
   // the divisions in tile_coords run on the vector unit; without this the
   // tile origin, and with it the activation descriptor, would sit in VGPRs
   // and every DMA would be wrapped in a waterfall loop
@@ -415,7 +428,12 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   tn = __builtin_amdgcn_readfirstlane(tn);
   c.m0 = (int64_t)tm * BM;
   c.n0 = (int64_t)tn * BN;
-  c.nsteps = (int)((c.red_len + BK - 1) / BK);
+  {
+    const int all = (int)((c.red_len + BK - 1) / BK);
+    const int first = all >> 1;
+    c.kstep0 = half == 1 ? first : 0;
+    c.nsteps = half < 0 ? all : (half == 0 ? first : all - first);
+  }
   c.kblocks = g.cols >> 6;
   c.mu = kDQ ? g.mu[0] : 0.0f;
   const int64_t rows_here = (g.T - c.m0) < BM ? (g.T - c.m0) : BM;
@@ -498,7 +516,9 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  for (int p0 = 0; p0 < g.r; p0 += 16) {
+  // (the second reduction half of a split tile starts from zero)
+  const int seed_r = half == 1 ? 0 : g.r;
+  for (int p0 = 0; p0 < seed_r; p0 += 16) {
     const int p = p0 + 8 * lhi;
     u32x4_t af[4], bf[2];
 #pragma unroll
@@ -516,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(af[i], bf[j], acc[i][j]);
   }
-  if constexpr (kDrop) {
+  if (kDrop && half != 1) {
     // the keep mask has one nibble per 4 tokens x 1 feature, exactly the 4
     // consecutive rows of one column a lane holds per accumulator group.
     // One batch of 8 byte loads per row block i (indices clamped, so the
@@ -598,6 +618,48 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // banks and each row still reads as 8 distinct 16-byte chunks.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (half >= 0) {
+    // K-split tile: both halves store their float32 accumulators (device
+    // scope, 16 bytes a lane, each store 1 KB contiguous) and count in; the
+    // second to arrive adds the other's (float32 addition of two terms does
+    // not depend on the order) and writes the tile.  Nothing waits for the
+    // other half, so no schedule of the units can stall.
+    // the arrival result goes through the weight stage the epilogue leaves idle
+    uint32_t* sh_last = reinterpret_cast<uint32_t*>(sb1);
+    const int su = q - g.split_from;
+    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+        g.part + ((size_t)su * 2 + half) * 65536, 0, 65536 * 4, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint32_t off = (uint32_t)((((2 * i + j) * 4 + e4) * kThreads + c.tid) * 16);
+          const f32x4_t v = f32x4_t{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1],
+                                    acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), mine, off, 0, 16);
+        }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
+    __syncthreads();
+    if (c.tid == 0)
+      *sh_last = __hip_atomic_fetch_add(g.cnt + su, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == 1u ? 1u : 0u;
+    __syncthreads();
+    if (*sh_last == 0u) return;   // uniform: the other half writes the tile
+    const float* other = g.part + ((size_t)su * 2 + (half ^ 1)) * 65536;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint32_t off = (uint32_t)((((2 * i + j) * 4 + e4) * kThreads + c.tid) * 16);
+          const f32x4_t v = load_partial4(other, off);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[i][j][4 * e4 + k] += v[k];
+        }
+  }
   {
     uint16_t* stg = (c.wave >> 1) == 0 ? sa0 : (c.wave >> 1) == 1 ? sa1
                   : (c.wave >> 1) == 2 ? sa2 : sb0;
@@ -655,16 +717,23 @@ static void launch_fmt(const GemmArgs& a, dim3 grid, hipStream_t stream) {
                        stream, a);
 }
 
+// one unit per tile, two per split tile
+static unsigned num_units(const GemmArgs& a, int64_t out_len) {
+  const unsigned tiles = num_tiles(a.T, out_len);
+  const unsigned from = (unsigned)a.split_from < tiles ? (unsigned)a.split_from : tiles;
+  return from + 2 * (tiles - from);
+}
+
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream) {
-  launch_fmt<false, false>(a, dim3(num_tiles(a.T, a.rows)), stream);
+  launch_fmt<false, false>(a, dim3(num_units(a, a.rows)), stream);
   return hipGetLastError();
 }
 
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.keep)
-    launch_fmt<true, true>(a, dim3(num_tiles(a.T, a.cols)), stream);
+    launch_fmt<true, true>(a, dim3(num_units(a, a.cols)), stream);
   else
-    launch_fmt<true, false>(a, dim3(num_tiles(a.T, a.cols)), stream);
+    launch_fmt<true, false>(a, dim3(num_units(a, a.cols)), stream);
   return hipGetLastError();
 }
 

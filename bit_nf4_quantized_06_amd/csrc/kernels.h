@@ -41,6 +41,14 @@ struct GemmArgs {
   const uint8_t* keep;
   bool dq;                 // double-quantised constants (else s2 = float32 c per block)
   bool f16;                // fp16 compute (else bf16)
+  // K-split of the last tiles: tiles from split_from on run as two units
+  // each, one per half of the reduction; both store their float32 partial
+  // (part: [tile - split_from][2][65536]) and count in (cnt: [tile -
+  // split_from], zero at launch); the second to arrive adds the other's and
+  // writes the tile.  split_from = the tile count: no split.
+  int split_from;
+  float* part;
+  uint32_t* cnt;
 };
 hipError_t launch_qlora_fwd_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_qlora_dx_gemm(const GemmArgs& a, hipStream_t stream);
@@ -154,6 +162,10 @@ struct ProjReduce {
   uint16_t* out_tr;
   int64_t ld_tr;
   bool f16;                // outputs fp16 (else bf16)
+  // also zeroed by this launch: the arrival counters of the fused GEMM that
+  // follows it (NULL / 0: none)
+  uint32_t* zero_cnt;
+  int n_zero;
 };
 hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream);
 

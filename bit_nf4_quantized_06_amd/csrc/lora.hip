@@ -309,6 +309,7 @@ __device__ void transpose_tile(const TransposeJobs& jobs, int b) {
 
 __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, TransposeJobs tj,
                                                                unsigned reduce_blocks) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < a.n_zero) a.zero_cnt[threadIdx.x] = 0u;
   if (blockIdx.x >= reduce_blocks) {
     transpose_tile(tj, (int)(blockIdx.x - reduce_blocks));
     return;

@@ -11,8 +11,11 @@
 // once per device with that device current, and is kept per device.  All
 // calls on one GPU share that GPU's array and it keeps the last call's
 // contents: the forward's kernels fully overwrite the parts they read (split
-// partials, the rounded U), so nothing needs clearing, but calls that overlap
-// on one GPU (two streams at once) race on it.
+// partials, the rounded U; the GEMM's arrival counters are zeroed by the
+// launch before it), so nothing needs clearing, but calls that overlap on
+// one GPU (two streams at once) race on it.  When the fused GEMM's K-split
+// partials would not fit, the forward runs the plain tile schedule (same
+// results up to the float32 summation order of those tiles).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -70,14 +73,17 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t*
   if (s != QLORA_OK) return s;
   if (T == 0)   // an empty batch needs no workspace
     return qlora_linear_fwd(w, X, T, A, B, r, alpha, Y, U_save, nullptr, 0, stream);
-  const size_t need = linear_ws_layout(T, d, r, false).total;
-  if (need > kScratchBytes) return QLORA_ERR_SCRATCH;
+  // the fused GEMM's K-split of its last tiles when its partials fit, else
+  // the plain tile schedule
+  const bool split = linear_ws_layout(T, d, r, false, false, true).total <= kScratchBytes;
+  if (!split && linear_ws_layout(T, d, r, false, false, false).total > kScratchBytes)
+    return QLORA_ERR_SCRATCH;
   s = check_device();
   if (s != QLORA_OK) return s;
   void* ws = nullptr;
   s = scratch_for_current_device(&ws);
   if (s != QLORA_OK) return s;
-  return qlora_linear_fwd(w, X, T, A, B, r, alpha, Y, U_save, ws, kScratchBytes, stream);
+  return linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, kScratchBytes, stream, split);
 }
 
 }  // extern "C"

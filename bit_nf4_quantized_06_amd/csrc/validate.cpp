@@ -139,7 +139,18 @@ QuantWs quant_ws_layout(const WeightDims& d) {
   return q;
 }
 
-LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, bool dropout) {
+int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len) {
+  const int64_t tiles = ((T + 255) / 256) * ((out_len + 255) / 256);
+  const int64_t rem = tiles % kGemmCUs;
+  const int64_t nsteps = (red_len + 63) / 64;
+  // at least one full round before it, a last round at most half full, and
+  // at least 8 reduction steps in each half
+  if (tiles <= kGemmCUs || rem == 0 || 2 * rem > kGemmCUs || nsteps < 16) return (int)tiles;
+  return (int)(tiles - rem);
+}
+
+LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, bool dropout,
+                          bool gemm_split) {
   LinearWs L;
   memset(&L, 0, sizeof(L));
   L.s_proj_x = lora_proj_splits(T, d.cols, r);
@@ -175,6 +186,19 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, b
     off += align_up(2 * (size_t)T * (size_t)d.cols, kWsAlign);
     L.keep_off = off;
     off += align_up(dropout_mask_bytes(T, d.cols), kWsAlign);
+  }
+  if (L.s_gemv == 0) {
+    const int64_t out_len = bwd ? d.cols : d.rows;
+    const int64_t red_len = bwd ? d.rows : d.cols;
+    L.gemm_tiles = (int)(((T + 255) / 256) * ((out_len + 255) / 256));
+    L.gemm_split = gemm_split ? gemm_split_from(T, out_len, red_len) : L.gemm_tiles;
+    const size_t n_split = (size_t)(L.gemm_tiles - L.gemm_split);
+    if (n_split > 0) {
+      L.split_part_off = off;
+      off += align_up(sizeof(float) * n_split * 2 * 65536, kWsAlign);
+      L.split_cnt_off = off;
+      off += align_up(sizeof(uint32_t) * n_split, kWsAlign);
+    }
   }
   L.total = off;
   return L;

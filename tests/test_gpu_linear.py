@@ -20,6 +20,12 @@ CASES = [
     ("r128_T17_N272_K320", 17, 272, 320, 128, 16.0),
     ("r64_T520_N528_K576", 520, 528, 576, 64, 16.0),
     ("r48_T256_N256_K256", 256, 256, 256, 48, 96.0),
+    # more than 256 tiles with a last round at most half full: the forward
+    # (270 tiles, 17 reduction steps) and the dX GEMM (261 tiles, 17 steps)
+    # split their last 14 and 5 tiles into two reduction halves; ragged token
+    # and row tiles
+    ("ksplit_fwd_T2300_N7440_K1088", 2300, 7440, 1088, 16, 16.0),
+    ("ksplit_dx_T2300_N1040_K7424", 2300, 1040, 7424, 16, 16.0),
 ]
 
 
