@@ -35,12 +35,14 @@ struct QuantWs {
 };
 QuantWs quant_ws_layout(const WeightDims& d);
 
-// K-split of the fused GEMM's last tiles.  The fused GEMM runs one 256 x 256
-// tile per CU at a time; when the tile count leaves a last round at most half
+// K-split of the fused GEMM's last tiles.  The fused GEMM runs one tile of
+// 256 tokens x 256 outputs per CU at a time; when the tile count leaves a last round at most half
 // full, the tiles of that round are each split into two halves of the
 // reduction (kernel units 2 i and 2 i + 1), so they finish in half a round.
 // Returns the first split tile (the tile count when nothing is split).
 constexpr int kGemmCUs = 256;   // compute units of an MI355X
+constexpr int kGemmTileTokens = 256;   // fused GEMM tile: tokens
+constexpr int kGemmTileOut = 256;      // fused GEMM tile: output features
 int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len);
 
 // Workspace layout of the linear forward / backward.

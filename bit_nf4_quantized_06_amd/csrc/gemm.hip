@@ -59,13 +59,14 @@
 // receives (dispatch is round-robin over the 8 XCDs) form a compact block
 // of 4 token tiles x 8 column tiles, keeping their shared operand tiles in
 // that XCD's L2.
+#include "abi_internal.h"
 #include "device_common.h"
 #include "kernels.h"
 
 namespace qlora {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
+constexpr int BM = kGemmTileTokens;   // 256 tokens per tile
+constexpr int BN = kGemmTileOut;      // 256 outputs per tile
 constexpr int BK = 64;
 constexpr int kStageElems = BM * BK;           // 16384 bf16 = 32 KB
 constexpr int kAStages = 3;

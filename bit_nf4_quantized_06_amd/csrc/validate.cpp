@@ -140,7 +140,8 @@ QuantWs quant_ws_layout(const WeightDims& d) {
 }
 
 int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len) {
-  const int64_t tiles = ((T + 255) / 256) * ((out_len + 255) / 256);
+  const int64_t tiles = ((T + kGemmTileTokens - 1) / kGemmTileTokens) *
+                        ((out_len + kGemmTileOut - 1) / kGemmTileOut);
   const int64_t rem = tiles % kGemmCUs;
   const int64_t nsteps = (red_len + 63) / 64;
   // at least one full round before it, a last round at most half full, and
@@ -190,7 +191,8 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, b
   if (L.s_gemv == 0) {
     const int64_t out_len = bwd ? d.cols : d.rows;
     const int64_t red_len = bwd ? d.rows : d.cols;
-    L.gemm_tiles = (int)(((T + 255) / 256) * ((out_len + 255) / 256));
+    L.gemm_tiles = (int)(((T + kGemmTileTokens - 1) / kGemmTileTokens) *
+                         ((out_len + kGemmTileOut - 1) / kGemmTileOut));
     L.gemm_split = gemm_split ? gemm_split_from(T, out_len, red_len) : L.gemm_tiles;
     const size_t n_split = (size_t)(L.gemm_tiles - L.gemm_split);
     if (n_split > 0) {
