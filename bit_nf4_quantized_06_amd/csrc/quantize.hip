@@ -19,9 +19,10 @@ typedef double f64x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Quantise: one workgroup per group of 256 blocks (16384 weights, 64 KB of
-// float32).  A wave owns 64 consecutive blocks; per iteration 8 lanes share a
-// block: lane s reads the 16-byte chunks s and s + 8 of the block's 256
-// bytes, so each of the two load instructions covers whole 128-byte lines.
+// float32).  A wave owns 64 consecutive blocks, all loaded up front; per
+// iteration 8 lanes share a block: lane s holds the 16-byte chunks s and
+// s + 8 of the block's 256 bytes, so each load instruction covers whole
+// 128-byte lines.
 // The block absmax is an 8-lane xor butterfly.  The quotient RN32(w / c) is
 // computed as Markstein's corrected product with the correctly rounded
 // reciprocal of c's significand (one IEEE division per block); with
@@ -108,23 +109,32 @@ __global__ __launch_bounds__(256) void nf4_quantize_blocks_kernel(
   const int sub = lane & 7;
   const bool odd = sub & 1;
   float c_keep = 0.0f;
-#pragma unroll 2
+  // All 16 of the lane's loads (the wave's 64 blocks, 16 KB) go out before
+  // any block is coded: 256 bytes per lane in flight, as a plain read stream
+  // needs to approach the HBM rate.  Non-temporal buffer loads over the
+  // wave's blocks; blocks past the end read as 0.
+  f32x4_t x[8][2];
+  {
+    const int64_t nb_here = n_b - blk0 < 64 ? (n_b - blk0 > 0 ? n_b - blk0 : 0) : 64;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(W + blk0 * kBlock), 0, (int)(nb_here * kBlock * 4), 0x00020000);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = (uint32_t)((it * 8 + (lane >> 3)) * kBlock * 4 + (sub + 8 * h) * 16);
+        x[it][h] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 2));
+      }
+  }
+#pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int64_t b = blk0 + it * 8 + (lane >> 3);
     const bool valid = b < n_b;
     float v[8];
-    if (valid) {
-      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(W + b * kBlock) + sub;
-      const f32x4_t x0 = __builtin_nontemporal_load(p);       // elements 4s .. 4s+3
-      const f32x4_t x1 = __builtin_nontemporal_load(p + 8);   // elements 32 + 4s ..
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = x0[e];
-        v[4 + e] = x1[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      v[e] = x[it][0][e];       // elements 4s .. 4s+3
+      v[4 + e] = x[it][1][e];   // elements 32 + 4s ..
     }
     float m = fabsf(v[0]);
 #pragma unroll
