@@ -84,6 +84,9 @@ LINEAR_CASES = [
     ("T520_N528_K576_r64_p05", 520, 528, 576, 64, 16.0, 0.5),
     ("T16_N256_K512_r16_p01", 16, 256, 512, 16, 32.0, 0.1),     # few tokens: general path
     ("T3_N272_K320_r128_p03", 3, 272, 320, 128, 16.0, 0.3),
+    # the dX GEMM splits its last round (261 tiles): the masked seed goes
+    # into the first reduction half only
+    ("T2300_N1040_K7424_r16_p01_ksplit", 2300, 1040, 7424, 16, 16.0, 0.1),
 ]
 
 

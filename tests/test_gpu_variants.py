@@ -193,6 +193,9 @@ LINEAR = [
     ("fp16_dq_skinny_T16_N272_K320_r128", 16, 272, 320, 128, 16.0, True, "fp16", None),
     ("bf16_nodq_skinny_T40_N528_K1024_r64", 40, 528, 1024, 64, 16.0, False, "bf16", None),
     ("fp16_nodq_dropout_T260_N272_K1024_r16", 260, 272, 1024, 16, 32.0, False, "fp16", 0.1),
+    # K-split of the last round in both fused GEMMs (270 and 261 tiles), fp16
+    # and float32 constants
+    ("fp16_nodq_ksplit_T2300_N7440_K7424_r16", 2300, 7440, 7424, 16, 16.0, False, "fp16", None),
 ]
 
 
