@@ -89,7 +89,13 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
   float* P = ws_ptr<float>(ws, L.proj_off);
   const int n_split = L.gemm_tiles - L.gemm_split;
   uint32_t* cnt = n_split > 0 ? ws_ptr<uint32_t>(ws, L.split_cnt_off) : nullptr;
-  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
+  uint16_t* wdq = L.pre_dq ? ws_ptr<uint16_t>(ws, L.wdq_off) : nullptr;
+  hipError_t e = hipSuccess;
+  if (wdq)
+    e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n, wdq,
+                          d.qt, d.dq, d.f16, st);
+  if (e == hipSuccess)
+    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs none;
     none.n = 0;
@@ -115,6 +121,7 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
     g.keep = nullptr;
     g.dq = d.dq;
     g.f16 = d.f16;
+    g.wdq = wdq;
     g.split_from = L.gemm_split;
     g.part = n_split > 0 ? ws_ptr<float>(ws, L.split_part_off) : nullptr;
     g.cnt = cnt;
@@ -139,11 +146,17 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
   float* P = ws_ptr<float>(ws, L.proj_off);
   const int n_split = L.gemm_tiles - L.gemm_split;
   uint32_t* cnt = n_split > 0 ? ws_ptr<uint32_t>(ws, L.split_cnt_off) : nullptr;
+  uint16_t* wdq = L.pre_dq ? ws_ptr<uint16_t>(ws, L.wdq_off) : nullptr;
 
   // G = dY B (B read in place as [rows, r]); its reduction writes the dX
   // seed's left operand and dA's, transposes A for the dX seed in the same
   // launch, and zeroes the dX GEMM's arrival counters
-  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
+  hipError_t e = hipSuccess;
+  if (wdq)
+    e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n, wdq,
+                          d.qt, d.dq, d.f16, st);
+  if (e == hipSuccess)
+    e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs tj;
     tj.n = 1;
@@ -181,6 +194,7 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
     g.keep = keep;
     g.dq = d.dq;
     g.f16 = d.f16;
+    g.wdq = wdq;
     g.split_from = L.gemm_split;
     g.part = n_split > 0 ? ws_ptr<float>(ws, L.split_part_off) : nullptr;
     g.cnt = cnt;
@@ -372,7 +386,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
                               const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                               uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
                               void* stream) {
-  return qlora::linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, ws_bytes, stream, true);
+  return qlora::linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, ws_bytes, stream, true,
+                                true);
 }
 
 }  // extern "C"
@@ -380,7 +395,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int6
 qlora_status qlora::linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
                                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                                     uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
-                                    void* stream, bool gemm_split) {
+                                    void* stream, bool gemm_split, bool pre_dq) {
   using namespace qlora;
   WeightDims d;
   qlora_status s = check_linear_args(w, T, r, alpha, &d);
@@ -391,7 +406,7 @@ qlora_status qlora::linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(ws) ||
       (U_save && !aligned16(U_save)))
     return QLORA_ERR_ALIGN;
-  const LinearWs L = linear_ws_layout(T, d, r, false, false, gemm_split);
+  const LinearWs L = linear_ws_layout(T, d, r, false, false, gemm_split, pre_dq);
   if (ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   s = check_device();
   if (s != QLORA_OK) return s;

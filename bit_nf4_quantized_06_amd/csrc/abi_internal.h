@@ -45,6 +45,16 @@ constexpr int kGemmTileTokens = 256;   // fused GEMM tile: tokens
 constexpr int kGemmTileOut = 256;      // fused GEMM tile: output features
 int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len);
 
+// From this many tokens on, the forward and the backward dequantise the
+// weight once per call into the workspace (16 bit, [rows, cols]) and the
+// fused GEMM fetches it by DMA instead of dequantising each weight tile once
+// per token tile: one streaming pass over the weight against
+// ceil(T / 256) in-kernel decodes.  Below it the GEMM decodes in place.
+constexpr int64_t kPreDqMinTokens = 2048;
+// the 16-bit weight's byte offsets fit the GEMM's 32-bit buffer offsets
+// (fewer than 2^30 weights, at most 2^20 columns)
+bool pre_dq_fits(const WeightDims& d);
+
 // Workspace layout of the linear forward / backward.
 struct LinearWs {
   int s_proj_x;     // split count of X A^T over cols
@@ -59,13 +69,17 @@ struct LinearWs {
   // split tile
   int gemm_tiles, gemm_split;
   size_t split_part_off, split_cnt_off;
+  // the weight dequantised once per call for the fused GEMM (pre_dq)
+  bool pre_dq;
+  size_t wdq_off;
   size_t total;
 };
 // With dropout the forward always takes the general path and the layout
 // adds the dropped input and the keep mask.
-// gemm_split false: no K-split (and no space for it) whatever the shape.
+// gemm_split false: no K-split (and no space for it) whatever the shape;
+// pre_dq false: the GEMM always decodes the weight in place.
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd,
-                          bool dropout = false, bool gemm_split = true);
+                          bool dropout = false, bool gemm_split = true, bool pre_dq = true);
 
 bool linear_dims_ok(int64_t T, int64_t rows, int64_t cols);
 
@@ -98,11 +112,12 @@ bool adamw_constants(int64_t step, double lr, double beta1, double beta2, double
 qlora_status check_linear_args(const qlora_nf4_weight* w, int64_t T, int32_t r, float alpha,
                                WeightDims* d);
 
-// qlora_linear_fwd, with the fused GEMM's K-split allowed or not (the
-// allocation-free forward turns it off when its partials would not fit).
+// qlora_linear_fwd, with the fused GEMM's K-split and the once-per-call
+// dequantisation allowed or not (the allocation-free forward turns off what
+// would not fit its fixed array).
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t T,
                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                              uint16_t* Y, uint16_t* U_save, void* ws, size_t ws_bytes,
-                             void* stream, bool gemm_split);
+                             void* stream, bool gemm_split, bool pre_dq);
 
 }  // namespace qlora

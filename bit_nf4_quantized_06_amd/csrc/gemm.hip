@@ -84,8 +84,11 @@ __device__ __forceinline__ int swz_g(int row) {   // activation / forward weight
 __device__ __forceinline__ int swz_a(int row, int chunk) {
   return row * BK + ((chunk ^ swz_g(row)) << 3);
 }
-__device__ __forceinline__ int swz_bt(int row, int chunk) {   // backward weight tile
-  return row * BN + ((chunk ^ (((row & 3) << 2) | ((row & 3) ^ (((row >> 2) & 1) << 1)))) << 3);
+__device__ __forceinline__ int swz_bt_g(int row) {   // backward weight tile
+  return ((row & 3) << 2) | ((row & 3) ^ (((row >> 2) & 1) << 1));
+}
+__device__ __forceinline__ int swz_bt(int row, int chunk) {
+  return row * BN + ((chunk ^ swz_bt_g(row)) << 3);
 }
 
 __device__ __forceinline__ u32x4_t ld_global16(const uint16_t* p) {
@@ -155,6 +158,11 @@ struct GemmCtx {
   // buffer ranges (base, bytes) of the operands read with range checking
   const uint16_t* act_base;
   uint32_t act_bytes, codes_bytes, code8_bytes, s2_bytes;
+  // weight already dequantised to 16 bit (kPreDq): its range and, in the
+  // backward, the lane offsets of the step's four loads
+  const uint16_t* w_base;
+  uint32_t w_bytes;
+  uint32_t w_voff[4];
   // per-lane byte offsets that do not change with the step
   uint32_t act_voff[2];     // activation DMA, even / odd 8-row block
   uint32_t code_voff;       // this lane's 16 code bytes at step 0
@@ -200,6 +208,34 @@ __device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stag
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.act_base, c.act_bytes),
                                              (lds_void_t*)(stage + blk8 * 512), 16,
                                              c.act_voff[i & 1], soff, 0, 0);
+  }
+}
+
+// Weight DMA of step `step` from a weight already dequantised to 16 bit, in
+// the layout the in-kernel dequantisation writes.  Forward: the same tile
+// shape as the activations (W rows n0 .. n0+255, 64 columns; load i of wave
+// w fills W rows 8 (4 w + i) .. +8, the lane offsets are the activation
+// ones).  Backward: W rows 64 step .. +64 by columns n0 .. n0+255 (512 B a
+// row); load i of wave w fills tile rows 2 (4 w + i) and +1, lane l writes
+// row 2 (4 w + i) + l / 32 at chunk position l % 32 and so fetches chunk
+// (l % 32) ^ swz_bt_g(row), which only depends on i and l.  Rows past the
+// end of W land past w_bytes and read 0 (range check), as do steps past the
+// end.  The host takes this path only for fewer than 2^30 weights and at
+// most 2^20 columns, so every offset stays below 2^31 + 2^29.
+template <bool kBwd>
+__device__ __forceinline__ void issue_wdq(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
+  const bool in = step < c.nsteps;
+  const uint32_t ks = (uint32_t)(c.kstep0 + step);
+  const uint32_t row_bytes = (uint32_t)(c.g.cols * 2);
+#pragma unroll
+  for (int i = 0; i < kActLoads; ++i) {
+    const int blk = c.wave * kActLoads + i;
+    const uint32_t o = kBwd ? (ks * 64 + 2 * (uint32_t)blk) * row_bytes
+                            : ks * (BK * 2) + 8 * (uint32_t)blk * row_bytes;
+    const uint32_t soff = in ? o : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.w_base, c.w_bytes),
+                                             (lds_void_t*)(stage + blk * 512), 16,
+                                             kBwd ? c.w_voff[i] : c.act_voff[i & 1], soff, 0, 0);
   }
 }
 
@@ -376,11 +412,84 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 #endif
 }
 
+// One reduction step when the weight arrives dequantised (kPreDq): both
+// operands come by DMA and the slices hold only MFMAs and their fragment
+// reads.  The weight tile of step+1 goes into the weight stage the previous
+// step read (free since that step's barrier) in slice 0, the activation
+// tile of step+2 in slice 1; the barrier then waits for all but the newest
+// 4 loads (the activation tile of step+2).
+template <int NR, int NM>
+__device__ __forceinline__ void dma_slice_schedule() {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (q < NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+template <bool kBwd, bool kF16, int SA, int SB>
+__device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
+                                              f32x16_t (&acc)[4][2], u32x4_t (&fa)[2][4],
+                                              u32x4_t (&fb)[2][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kReads = kBwd ? 8 : 6;
+  const uint16_t* as = c.A[SA];
+  const uint16_t* bs = c.B[SB];
+  uint16_t* as_next = c.A[(SA + 1) % kAStages];
+  uint16_t* bs_next = c.B[(SB + 1) % kBStages];
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int f = s & 1;
+    if (s == 0) issue_wdq(c, bs_next, step + 1);
+    if (s == 1) issue_act(c, c.A[(SA + 2) % kAStages], step + 2);
+    load_frags(c, as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[f][i], fb[f][j], acc[i][j]);
+    if (s < 2)
+      dma_slice_schedule<kReads, kActLoads>();
+    else
+      dma_slice_schedule<kReads, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[1][i], fb[1][j], acc[i][j]);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  barrier_keep_vmem<kActLoads>();   // stages of step+1 complete and visible
+  u32x4_t ga[4], gb[2];
+  load_frags(c, as_next, bs_next, 0, ga, gb);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[3][j] = mfma32<kF16>(fa[1][3], fb[1][j], acc[3][j]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = ga[i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[0][j] = gb[j];
+#endif
+}
+
+template <bool kBwd, bool kDQ, bool kF16, bool kPreDq, int SA, int SB>
+__device__ __forceinline__ void run_step(const GemmCtx<kBwd>& c, int step, f32x16_t (&acc)[4][2],
+                                         u32x4_t (&fa)[2][4], u32x4_t (&fb)[2][2],
+                                         CodeRegs& cur, CodeRegs& nxt) {
+  if constexpr (kPreDq)
+    gemm_step_dma<kBwd, kF16, SA, SB>(c, step, acc, fa, fb);
+  else
+    gemm_step<kBwd, kDQ, kF16, SA, SB>(c, step, acc, fa, fb, cur, nxt);
+}
+
 // kDrop (backward only): the seed is multiplied element-wise by the
 // lora_dropout keep mask (g.keep) before the main loop.  kDQ: double-
 // quantised block constants (else float32 constants); kF16: fp16 operands,
-// tables and output (else bf16).
-template <bool kBwd, bool kDrop, bool kDQ, bool kF16>
+// tables and output (else bf16); kPreDq: the weight arrives dequantised to
+// 16 bit (g.wdq, [rows, cols]) and is fetched by DMA like the activations
+// (kDQ then unused).
+template <bool kBwd, bool kDrop, bool kDQ, bool kF16, bool kPreDq>
 __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // The body is compiled in the device pass only: the host pass needs just
   // the kernel's signature, and it cannot instantiate the gfx950
@@ -490,6 +599,21 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     c.code_voff = c.w_row_ok ? (uint32_t)((n * g.cols + kc) >> 1) : kOOB;
     c.blk0 = n * (g.cols >> 6) + (kc >> 6);
   }
+  if (kPreDq) {
+    if (!kBwd) {
+      const int64_t wr = (g.rows - c.n0) < BN ? (g.rows - c.n0) : BN;
+      c.w_base = g.wdq + c.n0 * g.cols;
+      c.w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)(wr * g.cols * 2));
+    } else {
+      c.w_base = g.wdq + c.n0;
+      c.w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((g.rows * g.cols - c.n0) * 2));
+#pragma unroll
+      for (int i = 0; i < kActLoads; ++i) {
+        const int ch = (c.lane & 31) ^ swz_bt_g(2 * i + c.lhi);
+        c.w_voff[i] = (uint32_t)((c.lhi * g.cols + 8 * ch) * 2);
+      }
+    }
+  }
   c.act_base = g.act + c.m0 * c.red_len;
   c.act_bytes = (uint32_t)(rows_here * c.red_len * 2);
   c.codes_bytes = (uint32_t)((g.rows * g.cols) >> 1);
@@ -505,9 +629,12 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // prologue barrier's count satisfied)
   CodeRegs ca, cb;   // codes of even / odd steps
   issue_act(c, sa0, 0);
-  issue_codes<kBwd, kDQ>(c, 0, ca);
+  if (kPreDq)
+    issue_wdq(c, sb0, 0);
+  else
+    issue_codes<kBwd, kDQ>(c, 0, ca);
   issue_act(c, sa1, 1);
-  issue_codes<kBwd, kDQ>(c, 1, cb);
+  if (!kPreDq) issue_codes<kBwd, kDQ>(c, 1, cb);
 
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
   f32x16_t acc[4][2];
@@ -580,12 +707,13 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   }
 
   // ---- prologue: step 0's weight tile ----------------------------------------
-  {
+  if (!kPreDq) {
     const Nf4Lut lut = lut_of<kBwd, kDQ, kF16>(c, ca);
 #pragma unroll
     for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, ca, w);
   }
-  barrier_keep_vmem<kVmemPerStep>();   // activation stage 0 complete
+  // activation stage 0 (and the DMA'd weight stage 0) complete
+  barrier_keep_vmem<kPreDq ? kActLoads : kVmemPerStep>();
 
   u32x4_t fa[2][4], fb[2][2];
   load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
@@ -595,18 +723,18 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // the last nsteps % 6 steps
   int step = 0;
   for (; step + 6 <= c.nsteps; step += 6) {
-    gemm_step<kBwd, kDQ, kF16, 0, 0>(c, step, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, kDQ, kF16, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
-    gemm_step<kBwd, kDQ, kF16, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, kDQ, kF16, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
-    gemm_step<kBwd, kDQ, kF16, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
-    gemm_step<kBwd, kDQ, kF16, 2, 1>(c, step + 5, acc, fa, fb, ca, cb);
+    run_step<kBwd, kDQ, kF16, kPreDq, 0, 0>(c, step, acc, fa, fb, cb, ca);
+    run_step<kBwd, kDQ, kF16, kPreDq, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+    run_step<kBwd, kDQ, kF16, kPreDq, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+    run_step<kBwd, kDQ, kF16, kPreDq, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+    run_step<kBwd, kDQ, kF16, kPreDq, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
+    run_step<kBwd, kDQ, kF16, kPreDq, 2, 1>(c, step + 5, acc, fa, fb, ca, cb);
   }
-  if (step < c.nsteps) gemm_step<kBwd, kDQ, kF16, 0, 0>(c, step, acc, fa, fb, cb, ca);
-  if (step + 1 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
-  if (step + 2 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
-  if (step + 3 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
-  if (step + 4 < c.nsteps) gemm_step<kBwd, kDQ, kF16, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
+  if (step < c.nsteps) run_step<kBwd, kDQ, kF16, kPreDq, 0, 0>(c, step, acc, fa, fb, cb, ca);
+  if (step + 1 < c.nsteps) run_step<kBwd, kDQ, kF16, kPreDq, 1, 1>(c, step + 1, acc, fa, fb, ca, cb);
+  if (step + 2 < c.nsteps) run_step<kBwd, kDQ, kF16, kPreDq, 2, 0>(c, step + 2, acc, fa, fb, cb, ca);
+  if (step + 3 < c.nsteps) run_step<kBwd, kDQ, kF16, kPreDq, 0, 1>(c, step + 3, acc, fa, fb, ca, cb);
+  if (step + 4 < c.nsteps) run_step<kBwd, kDQ, kF16, kPreDq, 1, 0>(c, step + 4, acc, fa, fb, cb, ca);
 
   // ---- epilogue: round to 16 bit, stage the wave's 128 x 64 tile in LDS and
   // write whole 128-byte rows with 16-byte stores (16 stores per lane instead
@@ -704,18 +832,24 @@ static unsigned num_tiles(int64_t T, int64_t out_len) {
 
 template <bool kBwd, bool kDrop>
 static void launch_fmt(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.dq && !a.f16)
-    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, false>), grid, dim3(kThreads), 0,
-                       stream, a);
+  if (a.wdq && !a.f16)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, false, true>), grid,
+                       dim3(kThreads), 0, stream, a);
+  else if (a.wdq)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, true, true>), grid, dim3(kThreads),
+                       0, stream, a);
+  else if (a.dq && !a.f16)
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, false, false>), grid,
+                       dim3(kThreads), 0, stream, a);
   else if (a.dq)
-    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, true>), grid, dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, true, true, false>), grid, dim3(kThreads),
+                       0, stream, a);
   else if (!a.f16)
-    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, false>), grid, dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, false, false>), grid,
+                       dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, true>), grid, dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((qlora_gemm_kernel<kBwd, kDrop, false, true, false>), grid,
+                       dim3(kThreads), 0, stream, a);
 }
 
 // one unit per tile, two per split tile

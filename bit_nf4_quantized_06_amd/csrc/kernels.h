@@ -41,6 +41,9 @@ struct GemmArgs {
   const uint8_t* keep;
   bool dq;                 // double-quantised constants (else s2 = float32 c per block)
   bool f16;                // fp16 compute (else bf16)
+  // the weight already dequantised to 16 bit, [rows, cols] (then codes,
+  // code8, s2, mu are not read), or NULL: dequantise in the kernel
+  const uint16_t* wdq;
   // K-split of the last tiles: tiles from split_from on run as two units
   // each, one per half of the reduction; both store their float32 partial
   // (part: [tile - split_from][2][65536]) and count in (cnt: [tile -

@@ -15,7 +15,9 @@
 // launch before it), so nothing needs clearing, but calls that overlap on
 // one GPU (two streams at once) race on it.  When the fused GEMM's K-split
 // partials would not fit, the forward runs the plain tile schedule (same
-// results up to the float32 summation order of those tiles).
+// results up to the float32 summation order of those tiles).  The weight is
+// always decoded inside the GEMM here: its 16-bit copy (2 bytes a weight)
+// would not fit the array for any but small weights.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -75,15 +77,16 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t*
     return qlora_linear_fwd(w, X, T, A, B, r, alpha, Y, U_save, nullptr, 0, stream);
   // the fused GEMM's K-split of its last tiles when its partials fit, else
   // the plain tile schedule
-  const bool split = linear_ws_layout(T, d, r, false, false, true).total <= kScratchBytes;
-  if (!split && linear_ws_layout(T, d, r, false, false, false).total > kScratchBytes)
+  const bool split = linear_ws_layout(T, d, r, false, false, true, false).total <= kScratchBytes;
+  if (!split && linear_ws_layout(T, d, r, false, false, false, false).total > kScratchBytes)
     return QLORA_ERR_SCRATCH;
   s = check_device();
   if (s != QLORA_OK) return s;
   void* ws = nullptr;
   s = scratch_for_current_device(&ws);
   if (s != QLORA_OK) return s;
-  return linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, kScratchBytes, stream, split);
+  return linear_fwd_impl(w, X, T, A, B, r, alpha, Y, U_save, ws, kScratchBytes, stream, split,
+                         false);
 }
 
 }  // extern "C"

@@ -154,8 +154,12 @@ int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len) {
   return (int)(tiles - rem);
 }
 
+bool pre_dq_fits(const WeightDims& d) {
+  return d.n < ((int64_t)1 << 30) && d.cols <= ((int64_t)1 << 20);
+}
+
 LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, bool dropout,
-                          bool gemm_split) {
+                          bool gemm_split, bool pre_dq) {
   LinearWs L;
   memset(&L, 0, sizeof(L));
   L.s_proj_x = lora_proj_splits(T, d.cols, r);
@@ -204,6 +208,11 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, b
       off += align_up(sizeof(float) * n_split * 2 * 65536, kWsAlign);
       L.split_cnt_off = off;
       off += align_up(sizeof(uint32_t) * n_split, kWsAlign);
+    }
+    L.pre_dq = pre_dq && T >= kPreDqMinTokens && pre_dq_fits(d);
+    if (L.pre_dq) {
+      L.wdq_off = off;
+      off += align_up(2 * (size_t)d.n, kWsAlign);
     }
   }
   L.total = off;

@@ -249,7 +249,11 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
  * may then be NULL.  Accumulation is float32 on bf16 MFMA; the packed weight is
  * only read.  For T <= 64 (generation-sized batches, ta-paperlens 落とし穴)
  * the call takes the skinny path, which streams the packed weight once and
- * forms X A^T in the same pass; the workspace size reflects the path.
+ * forms X A^T in the same pass.  From T = 2048 on it dequantises the weight
+ * once into the workspace (2 bytes a weight, fewer than 2^30 weights and at
+ * most 2^20 columns) and the GEMM fetches that copy; in between the GEMM
+ * decodes the packed weight tile by tile.  Both give the same bits; the
+ * workspace size reflects the path.
  */
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
                               const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
@@ -259,13 +263,15 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int6
 /*
  * qlora_linear_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
- * Same arguments, results (the same kernels, bit for bit) and errors as
- * qlora_linear_fwd, without a workspace argument: the workspace is a fixed
- * array of qlora_linear_fwd_noalloc_max_scratch() bytes (32 MiB) that the
- * library holds in device memory on every GPU it runs on, until the process
- * ends.  The call allocates and frees nothing.  QLORA_ERR_SCRATCH (before any
- * device work) when qlora_linear_workspace(T, rows, cols, r, 0) exceeds that
- * size.  All calls on one GPU share its array: calls that overlap on one GPU
+ * Same arguments, results (bit for bit) and errors as qlora_linear_fwd,
+ * without a workspace argument: the workspace is a fixed array of
+ * qlora_linear_fwd_noalloc_max_scratch() bytes (32 MiB) that the library
+ * holds in device memory on every GPU it runs on, until the process ends.
+ * The call allocates and frees nothing.  Its GEMM always decodes the packed
+ * weight tile by tile (no 16-bit copy of the weight), and it drops the
+ * K-split of the GEMM's last tiles when that split's partials would not fit.
+ * QLORA_ERR_SCRATCH (before any device work) when even that workspace exceeds
+ * the array.  All calls on one GPU share its array: calls that overlap on one GPU
  * (on two streams at once) race; calls ordered on one stream do not.  The
  * first call on a device resolves the array's address (hipGetSymbolAddress),
  * which a caller under graph capture should do once before capturing.
@@ -286,7 +292,8 @@ size_t qlora_linear_fwd_noalloc_max_scratch(void);
  * with s = alpha / r and U = X A^T: U_saved (the forward's U_save) when not
  * NULL, else recomputed.  Same shape rules as the forward; for T = 0 dA and
  * dB are set to 0 (sums over no tokens) and X, dY, U_saved, dX and ws may
- * be NULL.
+ * be NULL.  As in the forward, from T = 2048 on the weight is dequantised
+ * once into the workspace for the dX GEMM.
  */
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
                               int64_t T, const uint16_t *A, const uint16_t *B, int32_t r,

@@ -1,7 +1,10 @@
 """The allocation-free forward (qlora_linear_fwd_noalloc) through the C ABI:
 its outputs equal qlora_linear_fwd's (given its own workspace) bit for bit,
 on two calls in a row on one device, the second with a smaller input (the
-shared device array keeps the first call's contents)."""
+shared device array keeps the first call's contents).  The allocation-free
+forward always decodes the weight inside the GEMM; from 2048 tokens on
+qlora_linear_fwd fetches a once-per-call 16-bit copy instead, so the
+2300-token case also checks that both weight paths give the same bits."""
 import ctypes
 
 import numpy as np
@@ -18,8 +21,10 @@ def _ptr(t):
 
 
 @pytest.mark.parametrize("cases", [[(1024, 1024, 2048, 32, 32.0), (16, 528, 1024, 16, 16.0)],
-                                   [(64, 512, 1024, 64, 16.0), (33, 256, 512, 16, 32.0)]],
-                         ids=["general_then_skinny", "skinny_then_smaller"])
+                                   [(64, 512, 1024, 64, 16.0), (33, 256, 512, 16, 32.0)],
+                                   [(2300, 1040, 1088, 16, 16.0), (300, 528, 1024, 32, 32.0)]],
+                         ids=["general_then_skinny", "skinny_then_smaller",
+                              "predq_then_general"])
 def test_noalloc_forward_equals_forward(cases):
     import bit_nf4_quantized_06_amd as q
     from bit_nf4_quantized_06_amd import _lib
