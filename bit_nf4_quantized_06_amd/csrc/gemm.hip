@@ -414,10 +414,14 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 
 // One reduction step when the weight arrives dequantised (kPreDq): both
 // operands come by DMA and the slices hold only MFMAs and their fragment
-// reads.  The weight tile of step+1 goes into the weight stage the previous
-// step read (free since that step's barrier) in slice 0, the activation
-// tile of step+2 in slice 1; the barrier then waits for all but the newest
-// 4 loads (the activation tile of step+2).
+// reads.  Here the three-stage ring (A) holds the weight and the two-stage
+// ring (B) the activations: a weight tile is shared by the 4 token tiles an
+// XCD runs beside it, an activation tile by 8 column tiles, so weight loads
+// miss the L2 more often and get the longer prefetch.  Slice 0 issues the
+// activation tile of step+1 into the activation stage the previous step read
+// (free since that step's barrier), slice 1 the weight tile of step+2; the
+// barrier then waits for all but the newest 4 loads (the weight tile of
+// step+2).
 template <int NR, int NM>
 __device__ __forceinline__ void dma_slice_schedule() {
 #pragma unroll
@@ -434,17 +438,17 @@ __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
                                               u32x4_t (&fb)[2][2]) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kReads = kBwd ? 8 : 6;
-  const uint16_t* as = c.A[SA];
-  const uint16_t* bs = c.B[SB];
-  uint16_t* as_next = c.A[(SA + 1) % kAStages];
-  uint16_t* bs_next = c.B[(SB + 1) % kBStages];
+  const uint16_t* ws = c.A[SA];
+  const uint16_t* xs = c.B[SB];
+  uint16_t* ws_next = c.A[(SA + 1) % kAStages];
+  uint16_t* xs_next = c.B[(SB + 1) % kBStages];
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const int f = s & 1;
-    if (s == 0) issue_wdq(c, bs_next, step + 1);
-    if (s == 1) issue_act(c, c.A[(SA + 2) % kAStages], step + 2);
-    load_frags(c, as, bs, s + 1, fa[f ^ 1], fb[f ^ 1]);
+    if (s == 0) issue_act(c, xs_next, step + 1);
+    if (s == 1) issue_wdq(c, c.A[(SA + 2) % kAStages], step + 2);
+    load_frags(c, xs, ws, s + 1, fa[f ^ 1], fb[f ^ 1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -463,7 +467,7 @@ __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
   __builtin_amdgcn_s_setprio(0);
   barrier_keep_vmem<kActLoads>();   // stages of step+1 complete and visible
   u32x4_t ga[4], gb[2];
-  load_frags(c, as_next, bs_next, 0, ga, gb);
+  load_frags(c, xs_next, ws_next, 0, ga, gb);
 #pragma unroll
   for (int j = 0; j < 2; ++j) acc[3][j] = mfma32<kF16>(fa[1][3], fb[1][j], acc[3][j]);
 #pragma unroll
@@ -628,13 +632,17 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   // (waiting for the seed's operands then drains them too, which leaves the
   // prologue barrier's count satisfied)
   CodeRegs ca, cb;   // codes of even / odd steps
-  issue_act(c, sa0, 0);
-  if (kPreDq)
-    issue_wdq(c, sb0, 0);
-  else
+  if (kPreDq) {
+    // weight ring A, activation ring B (see gemm_step_dma)
+    issue_wdq(c, sa0, 0);
+    issue_act(c, sb0, 0);
+    issue_wdq(c, sa1, 1);
+  } else {
+    issue_act(c, sa0, 0);
     issue_codes<kBwd, kDQ>(c, 0, ca);
-  issue_act(c, sa1, 1);
-  if (!kPreDq) issue_codes<kBwd, kDQ>(c, 1, cb);
+    issue_act(c, sa1, 1);
+    issue_codes<kBwd, kDQ>(c, 1, cb);
+  }
 
   // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
   f32x16_t acc[4][2];
@@ -716,7 +724,10 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   barrier_keep_vmem<kPreDq ? kActLoads : kVmemPerStep>();
 
   u32x4_t fa[2][4], fb[2][2];
-  load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
+  if (kPreDq)
+    load_frags(c, sb0, sa0, 0, fa[0], fb[0]);
+  else
+    load_frags(c, sa0, sb0, 0, fa[0], fb[0]);
 
   // whole groups of 6 steps (the stage cycle) in a loop without exits, so
   // each step's tail and the next step's head share one basic block; then
