@@ -225,67 +225,4 @@ __device__ __forceinline__ f32x16v_t mfma32x32(const u32x4_t& a, const u32x4_t& 
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Last-arriving workgroup of a split reduction.  The workgroups that write
-// partial sums of one output tile each arrive at a 64-bit word in the
-// caller's workspace after their partial stores; the one that completes the
-// count reduces the partials in a fixed order and writes the result, so the
-// reduction needs no dependent kernel launch and stays deterministic.
-//
-// word = (epoch << 32) | arrivals.  Every call of an entry point carries its
-// own non-zero epoch (a process-wide counter on the host), so a word left by
-// any earlier call, or never written, is recognised as stale by its tag and
-// restarted at 1: the workspace needs no zeroing.  The last arriver resets
-// the word to (epoch, 0), so a captured graph, which replays one epoch, also
-// counts from 0 on every replay.
-//
-// Visibility across the XCDs (each has its own L2): the partials are
-// written with device-scope stores and read with device-scope loads (the
-// sc1 scope bit: store_partial / load_partial4 below), which the memory
-// system keeps coherent across the XCDs by themselves, and the arrival is a
-// device-scope atomic.  Each wave waits for its partial stores to complete
-// before the workgroup barrier, the arrival is issued after that barrier,
-// and the last workgroup's loads after its arrival has returned.  No L2-wide
-// write-back or invalidation is needed (agent-scope fences would write back
-// and invalidate the whole L2 of the XCD in every wave, which slowed these
-// kernels several-fold).  Nothing waits for another workgroup, so no
-// schedule of the workgroups can stall.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// four device-scope float32 loads (16 bytes, byte offset `off` < 2^31 from
-// `base`): a buffer load with the sc1 cache-policy bit
-__device__ __forceinline__ f32x4_t load_partial4(const float* base, uint32_t off) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7FFFFFF0, 0x00020000);
-  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
-}
-
-__device__ __forceinline__ bool arrive_last(unsigned long long* word, uint32_t epoch, uint32_t n,
-                                            uint32_t* sh_flag) {
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long nxt;
-    do {
-      nxt = ((uint32_t)(cur >> 32) == epoch) ? cur + 1ull
-                                              : (((unsigned long long)epoch << 32) | 1ull);
-    } while (!__hip_atomic_compare_exchange_weak(word, &cur, nxt, __ATOMIC_RELAXED,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    *sh_flag = ((uint32_t)nxt == n) ? 1u : 0u;
-  }
-  __syncthreads();
-  return *sh_flag != 0u;
-}
-
-// The last arriver, once done with the partials: restart the count.
-__device__ __forceinline__ void arrival_reset(unsigned long long* word, uint32_t epoch) {
-  if (threadIdx.x == 0)
-    __hip_atomic_store(word, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace qlora

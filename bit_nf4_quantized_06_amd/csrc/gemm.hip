@@ -763,22 +763,32 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     // scope, 16 bytes a lane, each store 1 KB contiguous) and count in; the
     // second to arrive adds the other's (float32 addition of two terms does
     // not depend on the order) and writes the tile.  Nothing waits for the
-    // other half, so no schedule of the units can stall.
+    // other half, so no schedule of the units can stall.  Visibility across
+    // the XCDs (each has its own L2): the partials are stored and loaded with
+    // the sc1 (device scope) cache-policy bit, which the memory system keeps
+    // coherent across XCDs, and the arrival is a device-scope atomic issued
+    // after every wave's stores have completed (wait, then barrier); the last
+    // arriver loads only after its atomic has returned.  No L2-wide
+    // write-back or invalidation is needed.
     // the arrival result goes through the weight stage the epilogue leaves idle
     uint32_t* sh_last = reinterpret_cast<uint32_t*>(sb1);
     const int su = q - g.split_from;
+    // (the lane part of each offset in one register, the constant part in
+    // the scalar offset)
     const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
         g.part + ((size_t)su * 2 + half) * 65536, 0, 65536 * 4, 0x00020000);
+    const uint32_t voff = (uint32_t)c.tid * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const uint32_t off = (uint32_t)((((2 * i + j) * 4 + e4) * kThreads + c.tid) * 16);
+          const uint32_t soff = (uint32_t)(((2 * i + j) * 4 + e4) * kThreads * 16);
           const f32x4_t v = f32x4_t{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1],
                                     acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), mine, off, 0, 16);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), mine, voff, soff,
+                                                 16);
         }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
     __syncthreads();
@@ -787,15 +797,17 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
                                         __HIP_MEMORY_SCOPE_AGENT) == 1u ? 1u : 0u;
     __syncthreads();
     if (*sh_last == 0u) return;   // uniform: the other half writes the tile
-    const float* other = g.part + ((size_t)su * 2 + (half ^ 1)) * 65536;
+    const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
+        g.part + ((size_t)su * 2 + (half ^ 1)) * 65536, 0, 65536 * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const uint32_t off = (uint32_t)((((2 * i + j) * 4 + e4) * kThreads + c.tid) * 16);
-          const f32x4_t v = load_partial4(other, off);
+          const uint32_t soff = (uint32_t)(((2 * i + j) * 4 + e4) * kThreads * 16);
+          const f32x4_t v = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(other, voff, soff, 16));
 #pragma unroll
           for (int k = 0; k < 4; ++k) acc[i][j][4 * e4 + k] += v[k];
         }
