@@ -310,10 +310,12 @@ __device__ __forceinline__ void store_w(const GemmCtx<kBwd>& c, uint16_t* bs, co
 
 // MFMA fragments of slice s from stages (as, bs)
 template <bool kBwd>
+// (the two weight fragments first: the slice's first MFMAs use both of them
+// and the first activation fragment, so they can start after 3 of the 6
+// reads, which matters right after the step barrier, when every wave reads
+// at once)
 __device__ __forceinline__ void load_frags(const GemmCtx<kBwd>& c, const uint16_t* as,
                                            const uint16_t* bs, int s, u32x4_t* fa, u32x4_t* fb) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = ld_lds16(as + c.a_frag[s] + 32 * i * BK);
   if (!kBwd) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) fb[j] = ld_lds16(bs + c.b_frag[s] + 32 * j * BK);
@@ -322,6 +324,8 @@ __device__ __forceinline__ void load_frags(const GemmCtx<kBwd>& c, const uint16_
     for (int j = 0; j < 2; ++j)
       fb[j] = ld_lds_tr(bs + c.b_frag[2 * j] + 16 * s * BN, bs + c.b_frag[2 * j + 1] + 16 * s * BN);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = ld_lds16(as + c.a_frag[s] + 32 * i * BK);
 }
 
 // Interleave pattern of one 8-MFMA slice: each MFMA is followed by `V`
@@ -432,6 +436,23 @@ __device__ __forceinline__ void dma_slice_schedule() {
   }
 }
 
+template <int I0, int I1, bool kBwd>
+__device__ __forceinline__ void issue_wdq_part(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
+  const bool in = step < c.nsteps;
+  const uint32_t ks = (uint32_t)(c.kstep0 + step);
+  const uint32_t row_bytes = (uint32_t)(c.g.cols * 2);
+#pragma unroll
+  for (int i = I0; i < I1; ++i) {
+    const int blk = c.wave * kActLoads + i;
+    const uint32_t o = kBwd ? (ks * 64 + 2 * (uint32_t)blk) * row_bytes
+                            : ks * (BK * 2) + 8 * (uint32_t)blk * row_bytes;
+    const uint32_t soff = in ? o : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.w_base, c.w_bytes),
+                                             (lds_void_t*)(stage + blk * 512), 16,
+                                             kBwd ? c.w_voff[i] : c.act_voff[i & 1], soff, 0, 0);
+  }
+}
+
 template <bool kBwd, bool kF16, int SA, int SB>
 __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
                                               f32x16_t (&acc)[4][2], u32x4_t (&fa)[2][4],
@@ -447,20 +468,21 @@ __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
   for (int s = 0; s < 3; ++s) {
     const int f = s & 1;
     if (s == 0) issue_act(c, xs_next, step + 1);
-    if (s == 1) issue_wdq(c, c.A[(SA + 2) % kAStages], step + 2);
+    if (s == 1) issue_wdq_part<0, 2>(c, c.A[(SA + 2) % kAStages], step + 2);
+    if (s == 2) issue_wdq_part<2, 4>(c, c.A[(SA + 2) % kAStages], step + 2);
     load_frags(c, xs, ws, s + 1, fa[f ^ 1], fb[f ^ 1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[f][i], fb[f][j], acc[i][j]);
-    if (s < 2)
+    if (s == 0)
       dma_slice_schedule<kReads, kActLoads>();
     else
-      dma_slice_schedule<kReads, 0>();
+      dma_slice_schedule<kReads, 2>();
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[1][i], fb[1][j], acc[i][j]);
   __builtin_amdgcn_sched_barrier(0);
@@ -469,7 +491,9 @@ __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
   u32x4_t ga[4], gb[2];
   load_frags(c, xs_next, ws_next, 0, ga, gb);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) acc[3][j] = mfma32<kF16>(fa[1][3], fb[1][j], acc[3][j]);
+  for (int i = 2; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(fa[1][i], fb[1][j], acc[i][j]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = ga[i];
 #pragma unroll
