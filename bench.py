@@ -5,8 +5,11 @@ Headline (`value`): a step is the forward (Y, U) and the backward (dX, dA,
 dB) of all seven linears of a 7B-style decoder block (q/k/v/o 4096x4096,
 gate/up 11008x4096, down 4096x11008; NF4 blocks of 64, double quantisation in
 groups of 256), T = 8192 tokens, r = 64, alpha = 16.  The weights are
-quantised once before timing (a load-time cost); every step dequantises them
-on the fly inside the fused GEMMs.  The same line carries the other
+quantised once before timing (a load-time cost); every linear call of every
+step dequantises its weight again: at 2048 tokens and more once per call into
+a 16-bit workspace copy that the GEMM streams by DMA, below that inside the
+GEMM, per 256-token tile (the line also carries the headline workload timed
+with the in-GEMM decode, `block_7b_in_lds_decode`).  The same line carries the other
 workloads: the 4096x4096 attention projection at 4096 tokens, the 65B-style
 block at 2048 tokens (fwd+bwd) and at 16 tokens (forward, skinny path, GB/s),
 the bulk quantize / dequantize of an 8192x22016 weight, and the rows built
@@ -34,6 +37,10 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 
 HEADLINE = "block_7b"            # the training workload with the most flops per step
+# the headline workload again with the weight decoded into LDS inside the GEMM
+# for every 256-token tile (the path below qlora_pre_dequant_min_tokens())
+HEADLINE_LDS = "block_7b_in_lds_decode"
+NEVER = 2 ** 63 - 1
 SMALL_TRAIN = "attn_4096"        # one 4096 x 4096 linear, 4096 tokens
 TRAIN_65B = "block_65b_train"
 DECODE_65B = "block_65b_decode"
@@ -59,7 +66,8 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--only", default=None,
-                    help="comma-separated subset of: block_7b, attn_4096, block_65b_train, "
+                    help="comma-separated subset of: block_7b, block_7b_in_lds_decode, "
+                         "attn_4096, block_65b_train, "
                          "block_65b_decode, bulk, adamw, dropout, variants (profiling runs)")
     return ap.parse_args()
 
@@ -383,7 +391,8 @@ def time_graph(ls, ev, steps):
     return ms
 
 
-def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
+def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False,
+                    traffic_name=None):
     """fwd+bwd TFLOP/s of a training workload and the roofline of its
     dominant fused GEMM (achieved = its algorithmic flops over its event-timed
     duration, summed over the step's launches of it)."""
@@ -401,7 +410,12 @@ def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
     achieved = kfl / (kt["total_ms"] / 1e3) / 1e12
     digest = source_digest("gemm.hip", "device_common.h")
     shapes = sorted({(it["lin"].out_features, it["lin"].in_features) for it in ls.items})
+    from bit_nf4_quantized_06_amd import qlora_pre_dequant_min_tokens
+    path = ("weight dequantised once per call into a 16-bit workspace copy, both GEMM "
+            "operands by DMA" if ls.T >= qlora_pre_dequant_min_tokens() else
+            "weight tiles decoded into LDS inside the GEMM, once per 256-token tile")
     out = {
+        "gemm_weight_path": path,
         "ms_per_step": round(tm["ms_per_step"], 4),
         "TFLOPs": round(fl / (tm["ms_per_step"] / 1e3) / 1e12, 2),
         "mfma_frac": round(fl / (tm["ms_per_step"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -412,7 +426,7 @@ def training_config(name, ev, dev, steps, warmup, warmup_s, keep_weights=False):
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": profiled_traffic(dom, name, digest),
+                     "traffic": profiled_traffic(dom, traffic_name or name, digest),
                      "flops_per_launch": kfl // max(1, kt["launches"]),
                      "avg_launch_ms": round(kt["total_ms"] / max(1, kt["launches"]), 4),
                      "launches_per_step": kt["launches"], "source_digest": digest},
@@ -774,6 +788,18 @@ def main():
     if want(HEADLINE):
         log(f"timing {HEADLINE} fwd+bwd (headline)")
         head = training_config(HEADLINE, ev, dev, args.steps, args.warmup, args.warmup_seconds)
+    if want(HEADLINE_LDS):
+        import bit_nf4_quantized_06_amd as q
+        log(f"timing {HEADLINE} fwd+bwd with the in-LDS weight decode")
+        prev = q.qlora_set_pre_dequant_min_tokens(NEVER)
+        try:
+            r = training_config(HEADLINE, ev, dev, args.steps, args.warmup, args.warmup_seconds,
+                                traffic_name=HEADLINE_LDS)
+        finally:
+            q.qlora_set_pre_dequant_min_tokens(prev)
+        configs[HEADLINE_LDS] = {k: r[k] for k in ("gemm_weight_path", "ms_per_step", "TFLOPs",
+                                                   "mfma_frac", "roofline",
+                                                   "kernels_ms_per_step")}
     if want(SMALL_TRAIN):
         log(f"timing {SMALL_TRAIN} fwd+bwd")
         configs[SMALL_TRAIN] = training_config(SMALL_TRAIN, ev, dev, args.steps, args.warmup,

@@ -70,6 +70,8 @@ SIGNATURES = {
                                           ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double, _P]),
     "qlora_linear_workspace": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_int]),
+    "qlora_set_pre_dequant_min_tokens": (_I64, [_I64]),
+    "qlora_pre_dequant_min_tokens": (_I64, []),
     "qlora_linear_fwd": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float, _P, _P,
                                         _P, _SZ, _P]),
     "qlora_linear_fwd_noalloc": (ctypes.c_int, [_DESC_P, _P, _I64, _P, _P, _I32, ctypes.c_float,

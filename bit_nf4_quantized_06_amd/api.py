@@ -253,6 +253,19 @@ def qlora_linear_workspace(T: int, rows: int, cols: int, r: int, is_bwd: bool) -
     return int(_lib.load().qlora_linear_workspace(T, rows, cols, r, int(bool(is_bwd))))
 
 
+def qlora_set_pre_dequant_min_tokens(min_tokens: int) -> int:
+    """Token count from which qlora_linear_* dequantise the weight once per
+    call into their workspace (process-wide; returns the previous value)."""
+    prev = int(_lib.load().qlora_set_pre_dequant_min_tokens(int(min_tokens)))
+    if prev < 0:
+        raise ValueError("min_tokens must be >= 0")
+    return prev
+
+
+def qlora_pre_dequant_min_tokens() -> int:
+    return int(_lib.load().qlora_pre_dequant_min_tokens())
+
+
 @_stream_scoped
 def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                      alpha: float, Y: torch.Tensor | None = None,

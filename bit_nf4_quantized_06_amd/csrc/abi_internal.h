@@ -45,12 +45,14 @@ constexpr int kGemmTileTokens = 256;   // fused GEMM tile: tokens
 constexpr int kGemmTileOut = 256;      // fused GEMM tile: output features
 int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len);
 
-// From this many tokens on, the forward and the backward dequantise the
-// weight once per call into the workspace (16 bit, [rows, cols]) and the
-// fused GEMM fetches it by DMA instead of dequantising each weight tile once
-// per token tile: one streaming pass over the weight against
-// ceil(T / 256) in-kernel decodes.  Below it the GEMM decodes in place.
+// From pre_dq_min_tokens() tokens on (default kPreDqMinTokens, set with
+// qlora_set_pre_dequant_min_tokens), the forward and the backward dequantise
+// the weight once per call into the workspace (16 bit, [rows, cols]) and the
+// GEMM fetches it by DMA instead of dequantising each weight tile once per
+// token tile: one streaming pass over the weight against ceil(T / 256)
+// in-kernel decodes.  Below it the GEMM decodes in place.
 constexpr int64_t kPreDqMinTokens = 2048;
+int64_t pre_dq_min_tokens();
 // the 16-bit weight's byte offsets fit the GEMM's 32-bit buffer offsets
 // (fewer than 2^30 weights, at most 2^20 columns)
 bool pre_dq_fits(const WeightDims& d);

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "abi_internal.h"
 
 namespace qlora {
@@ -154,6 +156,12 @@ int gemm_split_from(int64_t T, int64_t out_len, int64_t red_len) {
   return (int)(tiles - rem);
 }
 
+namespace {
+std::atomic<int64_t> g_pre_dq_min_tokens{kPreDqMinTokens};
+}  // namespace
+
+int64_t pre_dq_min_tokens() { return g_pre_dq_min_tokens.load(std::memory_order_relaxed); }
+
 bool pre_dq_fits(const WeightDims& d) {
   return d.n < ((int64_t)1 << 30) && d.cols <= ((int64_t)1 << 20);
 }
@@ -209,7 +217,7 @@ LinearWs linear_ws_layout(int64_t T, const WeightDims& d, int32_t r, bool bwd, b
       L.split_cnt_off = off;
       off += align_up(sizeof(uint32_t) * n_split, kWsAlign);
     }
-    L.pre_dq = pre_dq && T >= kPreDqMinTokens && pre_dq_fits(d);
+    L.pre_dq = pre_dq && T >= pre_dq_min_tokens() && pre_dq_fits(d);
     if (L.pre_dq) {
       L.wdq_off = off;
       off += align_up(2 * (size_t)d.n, kWsAlign);
@@ -337,6 +345,13 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
   if (T == 0) return 0;   // an empty batch uses no workspace
   return qlora::linear_ws_layout(T, d, r, is_bwd != 0).total;
 }
+
+int64_t qlora_set_pre_dequant_min_tokens(int64_t min_tokens) {
+  if (min_tokens < 0) return -1;
+  return qlora::g_pre_dq_min_tokens.exchange(min_tokens, std::memory_order_relaxed);
+}
+
+int64_t qlora_pre_dequant_min_tokens(void) { return qlora::pre_dq_min_tokens(); }
 
 size_t qlora_dropout_mask_bytes(int64_t T, int64_t cols) {
   if (!qlora::dropout_dims_ok(T, cols)) return 0;

@@ -232,8 +232,27 @@ qlora_status qlora_adamw_step16(float *param, float *exp_avg, float *exp_avg_sq,
 
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
  * (is_bwd = 1) at T tokens, a [rows, cols] weight and rank r (0 on bad args;
- * also 0 for T = 0, which needs no workspace). */
+ * also 0 for T = 0, which needs no workspace).  The size depends on the
+ * once-per-call dequantisation policy below, read at the time of the query. */
 size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, int is_bwd);
+
+/*
+ * Once-per-call dequantisation policy of the linear layer (process-wide).
+ * Every matmul dequantises the blocks it needs to 16 bit (ta-paperlens
+ * 勾配は実際どこへ行くのか; Ultralytics "So funktioniert QLoRA": dequantise
+ * right before the matmul): for T >= min_tokens (default 2048) the forward
+ * and the backward of qlora_linear_* dequantise the whole weight once per
+ * call into their workspace (2 bytes a weight) and the GEMM streams that
+ * copy; below it (and always in qlora_linear_fwd_noalloc) the GEMM decodes
+ * each weight tile into LDS for every tile of 256 tokens.  Both give the
+ * same bits.  qlora_set_pre_dequant_min_tokens returns the previous value,
+ * or -1 (and changes nothing) for min_tokens < 0; INT64_MAX turns the
+ * once-per-call pass off.  Workspace sizes follow the policy at the time of
+ * the query: a call whose policy changed since leaves QLORA_ERR_WORKSPACE
+ * if its workspace became too small.
+ */
+int64_t qlora_set_pre_dequant_min_tokens(int64_t min_tokens);
+int64_t qlora_pre_dequant_min_tokens(void);
 
 /*
  * Forward of the frozen-NF4 linear layer with a LoRA adapter:
@@ -249,11 +268,11 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
  * may then be NULL.  Accumulation is float32 on bf16 MFMA; the packed weight is
  * only read.  For T <= 64 (generation-sized batches, ta-paperlens 落とし穴)
  * the call takes the skinny path, which streams the packed weight once and
- * forms X A^T in the same pass.  From T = 2048 on it dequantises the weight
- * once into the workspace (2 bytes a weight, fewer than 2^30 weights and at
- * most 2^20 columns) and the GEMM fetches that copy; in between the GEMM
- * decodes the packed weight tile by tile.  Both give the same bits; the
- * workspace size reflects the path.
+ * forms X A^T in the same pass.  From T = qlora_pre_dequant_min_tokens()
+ * on (2048 by default) it dequantises the weight once into the workspace (2
+ * bytes a weight, fewer than 2^30 weights and at most 2^20 columns) and the
+ * GEMM fetches that copy; in between the GEMM decodes the packed weight tile
+ * by tile.  Both give the same bits; the workspace size reflects the path.
  */
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t T,
                               const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
@@ -292,8 +311,8 @@ size_t qlora_linear_fwd_noalloc_max_scratch(void);
  * with s = alpha / r and U = X A^T: U_saved (the forward's U_save) when not
  * NULL, else recomputed.  Same shape rules as the forward; for T = 0 dA and
  * dB are set to 0 (sums over no tokens) and X, dY, U_saved, dX and ws may
- * be NULL.  As in the forward, from T = 2048 on the weight is dequantised
- * once into the workspace for the dX GEMM.
+ * be NULL.  As in the forward, from T = qlora_pre_dequant_min_tokens() on
+ * the weight is dequantised once into the workspace for the dX GEMM.
  */
 qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
                               int64_t T, const uint16_t *A, const uint16_t *B, int32_t r,

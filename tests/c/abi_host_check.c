@@ -51,6 +51,10 @@ int main(void) {
   /* sizes */
   CHECK(qlora_nf4_quantize_workspace(1024, 1024) > 0);
   CHECK(qlora_linear_workspace(512, 1024, 1024, 16, 1) > qlora_linear_workspace(512, 1024, 1024, 16, 0));
+  CHECK(qlora_pre_dequant_min_tokens() == 2048);
+  CHECK(qlora_set_pre_dequant_min_tokens(-5) == -1);
+  CHECK(qlora_linear_workspace(2048, 1024, 1024, 16, 0) >=
+        qlora_linear_workspace(2047, 1024, 1024, 16, 0) + (size_t)2 * 1024 * 1024);
   CHECK(qlora_linear_workspace(512, 1024, 1024, 24, 0) == 0);
   CHECK(qlora_linear_workspace_dropout(512, 1024, 1024, 16, 0) >
         qlora_linear_workspace(512, 1024, 1024, 16, 0));

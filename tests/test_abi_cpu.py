@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_functions_exported_and_bound():
     lib = _lib.load()
     names = _declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -277,6 +277,33 @@ def test_skinny_forward_workspace():
     assert small > 4 * 64 * 8192                      # at least one float32 partial
     assert ws(65, 8192, 8192, 64, 0) < small          # fused GEMM path: no partials
     assert ws(64, 8192, 8192, 64, 1) > 0
+
+
+def test_pre_dequant_policy_and_workspace():
+    """The once-per-call dequantisation policy: default 2048 tokens; from
+    there on the workspace holds a 16-bit copy of the weight (2 bytes a
+    weight, forward and backward); a negative value is rejected; INT64_MAX
+    turns it off; the setter returns the previous value."""
+    lib = _lib.load()
+    ws = lib.qlora_linear_workspace
+    assert lib.qlora_pre_dequant_min_tokens() == 2048
+    rows, cols, r = 1040, 1088, 16
+    below_f, below_b = ws(2047, rows, cols, r, 0), ws(2047, rows, cols, r, 1)
+    at_f, at_b = ws(2048, rows, cols, r, 0), ws(2048, rows, cols, r, 1)
+    assert at_f >= below_f + 2 * rows * cols and at_b >= below_b + 2 * rows * cols
+    try:
+        assert lib.qlora_set_pre_dequant_min_tokens(-1) == -1
+        assert lib.qlora_pre_dequant_min_tokens() == 2048
+        assert lib.qlora_set_pre_dequant_min_tokens(2 ** 63 - 1) == 2048
+        off_f = ws(2048, rows, cols, r, 0)
+        assert off_f < at_f and ws(1 << 20, 16, 64, 16, 1) > 0
+        assert lib.qlora_set_pre_dequant_min_tokens(0) == 2 ** 63 - 1
+        # the skinny forward (T <= 64) never takes the 16-bit copy
+        assert ws(64, rows, cols, r, 0) < ws(65, rows, cols, r, 0) + 2 * rows * cols
+        assert ws(65, rows, cols, r, 0) >= 2 * rows * cols
+    finally:
+        lib.qlora_set_pre_dequant_min_tokens(2048)
+    assert ws(2048, rows, cols, r, 0) == at_f
 
 
 def _drop(p=0.05, seed=1, offset=2):
