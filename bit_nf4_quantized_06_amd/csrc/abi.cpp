@@ -77,6 +77,18 @@ namespace {
 
 using namespace qlora;
 
+// The once-per-call dequantisation of w into wdq, run by the projection's
+// reduce launch.
+void set_dequant(ProjReduce& pr, const qlora_nf4_weight* w, const WeightDims& d, uint16_t* wdq) {
+  pr.dq_codes = w->codes;
+  pr.dq_code8 = w->absmax_code;
+  pr.dq_s2 = w->absmax_scale;
+  pr.dq_mu = w->absmax_offset;
+  pr.dq_words = d.n / 8;
+  pr.dq_dq = d.dq;
+  pr.dq_out = wdq;
+}
+
 // General forward path: U = inv (Xa A^T) by split reduction (U_save =
 // bf16(U), Us = bf16(s U)), then Y = X dequant(W)^T + Us B^T in the fused
 // GEMM.  Xa is X, or under lora_dropout the dropped input (inv = 1 / (1-p)).
@@ -90,19 +102,16 @@ hipError_t enqueue_fwd_general(const qlora_nf4_weight* w, const WeightDims& d, c
   const int n_split = L.gemm_tiles - L.gemm_split;
   uint32_t* cnt = n_split > 0 ? ws_ptr<uint32_t>(ws, L.split_cnt_off) : nullptr;
   uint16_t* wdq = L.pre_dq ? ws_ptr<uint16_t>(ws, L.wdq_off) : nullptr;
-  hipError_t e = hipSuccess;
-  if (wdq)
-    e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n, wdq,
-                          d.qt, d.dq, d.f16, st);
-  if (e == hipSuccess)
-    e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
+  hipError_t e = launch_lora_proj_partial(Xa, A, false, T, d.cols, r, L.s_proj_x, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs none;
     none.n = 0;
-    // the reduction also zeroes the GEMM's arrival counters
-    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv,
-                                           nullptr, 0, d.f16, cnt, n_split},
-                                none, st);
+    // the reduction also zeroes the GEMM's arrival counters and runs the
+    // once-per-call dequantisation
+    ProjReduce pr{P, T, r, L.s_proj_x, U_save, Us, scale * inv, inv, nullptr, 0, d.f16, cnt,
+                  n_split};
+    if (wdq) set_dequant(pr, w, d, wdq);
+    e = launch_lora_proj_reduce(pr, none, st);
   }
   if (e == hipSuccess) {
     GemmArgs g;
@@ -150,20 +159,16 @@ hipError_t enqueue_bwd(const qlora_nf4_weight* w, const WeightDims& d, const uin
 
   // G = dY B (B read in place as [rows, r]); its reduction writes the dX
   // seed's left operand and dA's, transposes A for the dX seed in the same
-  // launch, and zeroes the dX GEMM's arrival counters
-  hipError_t e = hipSuccess;
-  if (wdq)
-    e = launch_dequantize(w->codes, w->absmax_code, w->absmax_scale, w->absmax_offset, d.n, wdq,
-                          d.qt, d.dq, d.f16, st);
-  if (e == hipSuccess)
-    e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
+  // launch, zeroes the dX GEMM's arrival counters and runs the once-per-call
+  // dequantisation
+  hipError_t e = launch_lora_proj_partial(dY, B, true, T, d.rows, r, L.s_proj_dy, P, d.f16, st);
   if (e == hipSuccess) {
     TransposeJobs tj;
     tj.n = 1;
     tj.job[0] = TransposeJob{A, r, d.cols, At, r};
-    e = launch_lora_proj_reduce(ProjReduce{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv,
-                                           nullptr, 0, d.f16, cnt, n_split},
-                                tj, st);
+    ProjReduce pr{P, T, r, L.s_proj_dy, Gn, Gs, scale * inv, inv, nullptr, 0, d.f16, cnt, n_split};
+    if (wdq) set_dequant(pr, w, d, wdq);
+    e = launch_lora_proj_reduce(pr, tj, st);
   }
   // U for dB when the forward's U was not kept: recompute inv Xa A^T
   const uint16_t* U = U_saved;

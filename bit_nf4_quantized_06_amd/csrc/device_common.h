@@ -150,6 +150,50 @@ __device__ __forceinline__ float weight_constant_or_zero(bool ok, uint32_t code8
   return __uint_as_float(__float_as_uint(s2_or_c) & (ok ? 0xFFFFFFFFu : 0u));
 }
 
+// Dequantise chunk `chunk` of a packed weight to 16 bit: 1024 words of 8
+// codes, each of the 256 threads handling 4 words one wave-stride apart so
+// that every load (4 B a lane) and store (16 B a lane) of a wave is
+// contiguous.  The level comes from the table q (16 floats, in LDS), is
+// multiplied by the block constant (decoded, or the stored float32 one
+// without double quantisation) in float32 and rounded once to the 16-bit
+// compute type.  Shared by the standalone dequantiser and the linear layer's
+// once-per-call pass.
+template <bool kDQ, bool kF16>
+__device__ __forceinline__ void dequant_chunk(const uint32_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ code8,
+                                              const float* __restrict__ s2, float mu,
+                                              int64_t n_words, int64_t chunk, const float* q,
+                                              u32x4_t* __restrict__ out) {
+  const int64_t base = chunk * (256 * 4) + threadIdx.x;
+  uint32_t w[4];
+  float cp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + j * 256;
+    w[j] = 0u;
+    cp[j] = 0.0f;
+    if (i < n_words) {
+      w[j] = __builtin_nontemporal_load(codes + i);
+      const int64_t blk = i >> 3;
+      cp[j] = kDQ ? block_constant(code8[blk], s2[blk >> 8], mu) : s2[blk];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + j * 256;
+    if (i < n_words) {
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __fmul_rn(q[(w[j] >> (8 * e)) & 15u], cp[j]);
+        const float b = __fmul_rn(q[(w[j] >> (8 * e + 4)) & 15u], cp[j]);
+        o[e] = pack16x2<kF16>(a, b);
+      }
+      __builtin_nontemporal_store(o, out + i);
+    }
+  }
+}
+
 // 16-entry bf16 lookup table of one block, q[k] * c' rounded once to bf16,
 // split into byte planes for v_perm lookups:
 //   lo[i] byte j = low byte of entry 4i+j, hi[i] byte j = high byte.

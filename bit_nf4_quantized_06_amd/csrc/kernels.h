@@ -169,6 +169,17 @@ struct ProjReduce {
   // follows it (NULL / 0: none)
   uint32_t* zero_cnt;
   int n_zero;
+  // also run by this launch: the linear layer's once-per-call dequantisation
+  // of its NF4 weight to 16 bit (the type of f16) into dq_out [rows, cols]
+  // (NULL: none); dq_words = rows * cols / 8; constants as in the
+  // descriptor, double-quantised (dq_dq) or float32
+  const uint8_t* dq_codes = nullptr;
+  const uint8_t* dq_code8 = nullptr;
+  const float* dq_s2 = nullptr;
+  const float* dq_mu = nullptr;
+  int64_t dq_words = 0;
+  bool dq_dq = false;
+  uint16_t* dq_out = nullptr;
 };
 hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStream_t stream);
 

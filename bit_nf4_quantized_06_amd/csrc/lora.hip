@@ -307,9 +307,38 @@ __device__ void transpose_tile(const TransposeJobs& jobs, int b) {
   }
 }
 
+// One chunk (1024 words of 8 codes) of the once-per-call dequantisation.
+__device__ void dequant_role(const ProjReduce& a, int64_t chunk) {
+  __shared__ float q[16];
+  if (threadIdx.x < 16) q[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.dq_codes);
+  u32x4_t* out = reinterpret_cast<u32x4_t*>(a.dq_out);
+  if (a.dq_dq) {
+    const float mu = a.dq_mu[0];
+    if (a.f16)
+      dequant_chunk<true, true>(codes, a.dq_code8, a.dq_s2, mu, a.dq_words, chunk, q, out);
+    else
+      dequant_chunk<true, false>(codes, a.dq_code8, a.dq_s2, mu, a.dq_words, chunk, q, out);
+  } else {
+    if (a.f16)
+      dequant_chunk<false, true>(codes, a.dq_code8, a.dq_s2, 0.0f, a.dq_words, chunk, q, out);
+    else
+      dequant_chunk<false, false>(codes, a.dq_code8, a.dq_s2, 0.0f, a.dq_words, chunk, q, out);
+  }
+}
+
+// Workgroups [0, reduce_blocks): the split reduction; then `transpose_blocks`
+// transpose tiles; then the dequantisation chunks (a.dq_out set).  The roles
+// are independent, so one launch carries them all.
 __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, TransposeJobs tj,
-                                                               unsigned reduce_blocks) {
+                                                               unsigned reduce_blocks,
+                                                               unsigned transpose_blocks) {
   if (blockIdx.x == 0 && (int)threadIdx.x < a.n_zero) a.zero_cnt[threadIdx.x] = 0u;
+  if (blockIdx.x >= reduce_blocks + transpose_blocks) {
+    dequant_role(a, (int64_t)(blockIdx.x - reduce_blocks - transpose_blocks));
+    return;
+  }
   if (blockIdx.x >= reduce_blocks) {
     transpose_tile(tj, (int)(blockIdx.x - reduce_blocks));
     return;
@@ -364,8 +393,9 @@ hipError_t launch_lora_proj_reduce(const ProjReduce& a, TransposeJobs tj, hipStr
     tj.tiles[i] = (int)(((j.C + 31) / 32) * ((j.ld_out + 31) / 32));
     ttiles += tj.tiles[i];
   }
-  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3(nred + (unsigned)ttiles), dim3(256), 0, stream,
-                     a, tj, nred);
+  const unsigned ndeq = a.dq_out ? (unsigned)((a.dq_words + 1023) / 1024) : 0u;
+  hipLaunchKernelGGL(lora_proj_reduce_kernel, dim3(nred + (unsigned)ttiles + ndeq), dim3(256), 0,
+                     stream, a, tj, nred, (unsigned)ttiles);
   return hipGetLastError();
 }
 

@@ -330,12 +330,8 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Dequantise to bf16: each thread handles 4 words of 8 codes, one wave-stride
-// apart so that every load (4 B per lane) and store (16 B per lane) of a wave
-// is contiguous.  The level (codebook qt) is looked up in shared memory,
-// multiplied by the block constant (decoded, or the stored float32 one
-// without double quantisation) in float32 and rounded once to the 16-bit
-// compute type (bf16, or fp16 with kF16).
+// Dequantise to bf16 (or fp16): one chunk of 1024 words per workgroup
+// (dequant_chunk), levels of codebook qt from an LDS table.
 // ---------------------------------------------------------------------------
 template <bool kDQ, bool kF16>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
@@ -345,35 +341,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
   __shared__ float q[16];
   if (threadIdx.x < 16) q[threadIdx.x] = qt ? kINT4[threadIdx.x] : kNF4[threadIdx.x];
   __syncthreads();
-  const float mu = kDQ ? mu_p[0] : 0.0f;
-  const int64_t base = (int64_t)blockIdx.x * (256 * 4) + threadIdx.x;
-  uint32_t w[4];
-  float cp[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t i = base + j * 256;
-    w[j] = 0u;
-    cp[j] = 0.0f;
-    if (i < n_words) {
-      w[j] = __builtin_nontemporal_load(codes + i);
-      const int64_t blk = i >> 3;
-      cp[j] = kDQ ? block_constant(code8[blk], s2[blk >> 8], mu) : s2[blk];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t i = base + j * 256;
-    if (i < n_words) {
-      u32x4_t o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = __fmul_rn(q[(w[j] >> (8 * e)) & 15u], cp[j]);
-        const float b = __fmul_rn(q[(w[j] >> (8 * e + 4)) & 15u], cp[j]);
-        o[e] = pack16x2<kF16>(a, b);
-      }
-      __builtin_nontemporal_store(o, out + i);
-    }
-  }
+  dequant_chunk<kDQ, kF16>(codes, code8, s2, kDQ ? mu_p[0] : 0.0f, n_words, blockIdx.x, q, out);
 }
 
 // ---------------------------------------------------------------------------

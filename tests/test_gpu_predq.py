@@ -26,6 +26,10 @@ CASES = [
     ("ksplit_dx_T2300_N1040_K7424_r16", 2300, 1040, 7424, 16, 16.0, True, "bf16", None),
     ("fp16_nodq_T2100_N784_K1024_r64", 2100, 784, 1024, 64, 16.0, False, "fp16", None),
     ("dropout_T2300_N1040_K1088_r16_p01", 2300, 1040, 1088, 16, 16.0, True, "bf16", 0.1),
+    # a weight smaller than one tile both ways (16 rows: one partial reduction
+    # step in the backward, 64 columns), and a ragged one just past a tile
+    ("tiny_weight_T2048_N16_K64_r16", 2048, 16, 64, 16, 32.0, True, "bf16", None),
+    ("ragged_T2049_N272_K320_r128", 2049, 272, 320, 128, 16.0, True, "bf16", None),
 ]
 
 
