@@ -29,6 +29,11 @@
 //     keeps W's own row layout in both directions; the backward reads its
 //     operand (reduction = W rows) with ds_read_b64_tr_b16, which hands each
 //     lane 4 consecutive rows of one column.
+// From 2048 tokens on the library dequantises the whole weight once per call
+// (kPreDq): the weight tile then arrives by DMA like the activations, into
+// the same layout the decode writes, and the slices hold only MFMAs and
+// fragment reads; tile, layouts, seed, split and epilogue are shared, so
+// both paths give the same bits.
 // All out-of-range rows and columns are handled by buffer-descriptor range
 // checks (reads past the end return 0), so every 8-MFMA slice is a single
 // basic block.  Within a slice the MFMAs are interleaved with the
@@ -221,14 +226,15 @@ __device__ __forceinline__ void issue_act(const GemmCtx<kBwd>& c, uint16_t* stag
 // (l % 32) ^ swz_bt_g(row), which only depends on i and l.  Rows past the
 // end of W land past w_bytes and read 0 (range check), as do steps past the
 // end.  The host takes this path only for fewer than 2^30 weights and at
-// most 2^20 columns, so every offset stays below 2^31 + 2^29.
-template <bool kBwd>
+// most 2^20 columns, so every offset stays below 2^31 + 2^29.  Loads I0 ..
+// I1 - 1 of the wave's four.
+template <int I0, int I1, bool kBwd>
 __device__ __forceinline__ void issue_wdq(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
   const bool in = step < c.nsteps;
   const uint32_t ks = (uint32_t)(c.kstep0 + step);
   const uint32_t row_bytes = (uint32_t)(c.g.cols * 2);
 #pragma unroll
-  for (int i = 0; i < kActLoads; ++i) {
+  for (int i = I0; i < I1; ++i) {
     const int blk = c.wave * kActLoads + i;
     const uint32_t o = kBwd ? (ks * 64 + 2 * (uint32_t)blk) * row_bytes
                             : ks * (BK * 2) + 8 * (uint32_t)blk * row_bytes;
@@ -308,12 +314,11 @@ __device__ __forceinline__ void store_w(const GemmCtx<kBwd>& c, uint16_t* bs, co
   *reinterpret_cast<u32x4_t*>(bs + c.w_store[w]) = u32x4_t{d[0], d[1], d[2], d[3]};
 }
 
-// MFMA fragments of slice s from stages (as, bs)
+// MFMA fragments of slice s from stages (as, bs); the two weight fragments
+// first: the slice's first MFMAs use both of them and the first activation
+// fragment, so they can start after 3 of the 6 reads, which matters right
+// after the step barrier, when every wave reads at once
 template <bool kBwd>
-// (the two weight fragments first: the slice's first MFMAs use both of them
-// and the first activation fragment, so they can start after 3 of the 6
-// reads, which matters right after the step barrier, when every wave reads
-// at once)
 __device__ __forceinline__ void load_frags(const GemmCtx<kBwd>& c, const uint16_t* as,
                                            const uint16_t* bs, int s, u32x4_t* fa, u32x4_t* fb) {
   if (!kBwd) {
@@ -423,9 +428,9 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
 // XCD runs beside it, an activation tile by 8 column tiles, so weight loads
 // miss the L2 more often and get the longer prefetch.  Slice 0 issues the
 // activation tile of step+1 into the activation stage the previous step read
-// (free since that step's barrier), slice 1 the weight tile of step+2; the
-// barrier then waits for all but the newest 4 loads (the weight tile of
-// step+2).
+// (free since that step's barrier), slices 1 and 2 the weight tile of step+2
+// (two loads each); the barrier, before the step's last four MFMAs, waits
+// for all but the newest 4 loads (the weight tile of step+2).
 template <int NR, int NM>
 __device__ __forceinline__ void dma_slice_schedule() {
 #pragma unroll
@@ -433,23 +438,6 @@ __device__ __forceinline__ void dma_slice_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (q < NM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-  }
-}
-
-template <int I0, int I1, bool kBwd>
-__device__ __forceinline__ void issue_wdq_part(const GemmCtx<kBwd>& c, uint16_t* stage, int step) {
-  const bool in = step < c.nsteps;
-  const uint32_t ks = (uint32_t)(c.kstep0 + step);
-  const uint32_t row_bytes = (uint32_t)(c.g.cols * 2);
-#pragma unroll
-  for (int i = I0; i < I1; ++i) {
-    const int blk = c.wave * kActLoads + i;
-    const uint32_t o = kBwd ? (ks * 64 + 2 * (uint32_t)blk) * row_bytes
-                            : ks * (BK * 2) + 8 * (uint32_t)blk * row_bytes;
-    const uint32_t soff = in ? o : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(c.w_base, c.w_bytes),
-                                             (lds_void_t*)(stage + blk * 512), 16,
-                                             kBwd ? c.w_voff[i] : c.act_voff[i & 1], soff, 0, 0);
   }
 }
 
@@ -468,8 +456,8 @@ __device__ __forceinline__ void gemm_step_dma(const GemmCtx<kBwd>& c, int step,
   for (int s = 0; s < 3; ++s) {
     const int f = s & 1;
     if (s == 0) issue_act(c, xs_next, step + 1);
-    if (s == 1) issue_wdq_part<0, 2>(c, c.A[(SA + 2) % kAStages], step + 2);
-    if (s == 2) issue_wdq_part<2, 4>(c, c.A[(SA + 2) % kAStages], step + 2);
+    if (s == 1) issue_wdq<0, 2>(c, c.A[(SA + 2) % kAStages], step + 2);
+    if (s == 2) issue_wdq<2, 4>(c, c.A[(SA + 2) % kAStages], step + 2);
     load_frags(c, xs, ws, s + 1, fa[f ^ 1], fb[f ^ 1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -658,9 +646,9 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   CodeRegs ca, cb;   // codes of even / odd steps
   if (kPreDq) {
     // weight ring A, activation ring B (see gemm_step_dma)
-    issue_wdq(c, sa0, 0);
+    issue_wdq<0, kActLoads>(c, sa0, 0);
     issue_act(c, sb0, 0);
-    issue_wdq(c, sa1, 1);
+    issue_wdq<0, kActLoads>(c, sa1, 1);
   } else {
     issue_act(c, sa0, 0);
     issue_codes<kBwd, kDQ>(c, 0, ca);
