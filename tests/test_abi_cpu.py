@@ -295,8 +295,8 @@ def test_pre_dequant_policy_and_workspace():
         assert lib.qlora_set_pre_dequant_min_tokens(-1) == -1
         assert lib.qlora_pre_dequant_min_tokens() == 2048
         assert lib.qlora_set_pre_dequant_min_tokens(2 ** 63 - 1) == 2048
-        off_f = ws(2048, rows, cols, r, 0)
-        assert off_f < at_f and ws(1 << 20, 16, 64, 16, 1) > 0
+        off_f, off_b = ws(2048, rows, cols, r, 0), ws(2048, rows, cols, r, 1)
+        assert off_f < at_f and off_b < at_b and ws(1 << 20, 16, 64, 16, 1) > 0
         assert lib.qlora_set_pre_dequant_min_tokens(0) == 2 ** 63 - 1
         # the skinny forward (T <= 64) never takes the 16-bit copy
         assert ws(64, rows, cols, r, 0) < ws(65, rows, cols, r, 0) + 2 * rows * cols
@@ -304,6 +304,13 @@ def test_pre_dequant_policy_and_workspace():
     finally:
         lib.qlora_set_pre_dequant_min_tokens(2048)
     assert ws(2048, rows, cols, r, 0) == at_f
+    # a workspace sized while the pass was off is too small once it is on
+    # again: the calls refuse it before any device work
+    d = ctypes.byref(_desc(rows, cols))
+    assert lib.qlora_linear_fwd(d, FAKE, 2048, FAKE, FAKE, r, 16.0, FAKE, None, FAKE, off_f,
+                                None) == 4
+    assert lib.qlora_linear_bwd(d, FAKE, FAKE, 2048, FAKE, FAKE, r, 16.0, None, FAKE, FAKE, FAKE,
+                                FAKE, off_b, None) == 4
 
 
 def _drop(p=0.05, seed=1, offset=2):
