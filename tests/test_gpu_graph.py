@@ -57,10 +57,19 @@ def _check_replays(name, run, outputs, eager_work):
         torch.cuda.synchronize()
 
 
-def test_general_fwd_bwd_graph():
+# (name, T, N, K): the GEMM decoding in LDS; from 2048 tokens on, the
+# once-per-call dequantisation inside the reduce launch and (7440 rows: 270
+# tiles) the forward GEMM's K-split, whose arrival counters that launch
+# zeroes on every replay
+GENERAL = [("in_lds_T520", 520, 528, 576), ("predq_ksplit_T2300", 2300, 7440, 1088)]
+
+
+@pytest.mark.parametrize("case", GENERAL, ids=[c[0] for c in GENERAL])
+def test_general_fwd_bwd_graph(case):
     q = _api()
-    T, N, K, r, alpha = 520, 528, 576, 64, 16.0
-    print("[graph] general fwd+bwd", flush=True)
+    name, T, N, K = case
+    r, alpha = 64, 16.0
+    print(f"[graph] general fwd+bwd {name}", flush=True)
     inp = linear_case(T, N, K, r, alpha, seed=31)
     wq = q.qlora_nf4_quantize(f32_dev(inp["w"]))
     X, A, B, dY = (bf16_dev(inp[k]) for k in ("x", "a", "b", "dy"))
@@ -78,7 +87,7 @@ def test_general_fwd_bwd_graph():
                            dB=out["dB"], workspace=wsb)
 
     other = torch.randn(1024, 1024, device=dev)
-    _check_replays("general", run, out, lambda: other.mul_(1.0001))
+    _check_replays(f"general {name}", run, out, lambda: other.mul_(1.0001))
 
 
 def test_skinny_forward_graph():
