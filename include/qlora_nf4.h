@@ -249,7 +249,9 @@ size_t qlora_linear_workspace(int64_t T, int64_t rows, int64_t cols, int32_t r, 
  * or -1 (and changes nothing) for min_tokens < 0; INT64_MAX turns the
  * once-per-call pass off.  Workspace sizes follow the policy at the time of
  * the query: a call whose policy changed since leaves QLORA_ERR_WORKSPACE
- * if its workspace became too small.
+ * if its workspace became too small.  The value is one atomic word: a change
+ * made while other threads size or make calls is safe, each of them sees the
+ * old or the new value.
  */
 int64_t qlora_set_pre_dequant_min_tokens(int64_t min_tokens);
 int64_t qlora_pre_dequant_min_tokens(void);
