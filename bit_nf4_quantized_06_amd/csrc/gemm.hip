@@ -34,6 +34,12 @@
 // the same layout the decode writes, and the slices hold only MFMAs and
 // fragment reads; tile, layouts, seed, split and epilogue are shared, so
 // both paths give the same bits.
+// Each tile starts from the LoRA product: the accumulators are seeded with
+// (s L) R^T over the r adapter columns, whose 256 x 64 operand tiles arrive
+// by DMA into the two stages the prologue leaves idle, issued ahead of the
+// first stages' loads, so the seed waits for one memory round trip (loading
+// its fragments from global memory 16 columns at a time took four, about
+// 8 us of every round of tiles).
 // All out-of-range rows and columns are handled by buffer-descriptor range
 // checks (reads past the end return 0), so every 8-MFMA slice is a single
 // basic block.  Within a slice the MFMAs are interleaved with the
@@ -79,7 +85,13 @@ constexpr int kBStages = 2;
 constexpr uint32_t kOOB = 0x80000000u;         // buffer offset that reads as 0
 constexpr int kThreads = 512;                  // 8 waves
 constexpr int kActLoads = 4;                   // activation DMAs per wave and step
-constexpr int kVmemPerStep = kActLoads + 3;    // + codes, 8-bit code, group scale
+// memory loads per reduction step of the in-LDS decode: the activation DMAs,
+// the codes, the group scale (float32 block constant without double
+// quantisation) and, with double quantisation, the 8-bit block code.  The
+// explicit wait counts are built from this, so every one of these loads is
+// issued and used (none may be dropped by the compiler as dead).
+template <bool kDQ>
+constexpr int vmem_per_step() { return kActLoads + (kDQ ? 3 : 2); }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -246,10 +258,8 @@ __device__ __forceinline__ void issue_wdq(const GemmCtx<kBwd>& c, uint16_t* stag
 }
 
 // packed codes and block-constant inputs of this lane's half block at `step`
-// kDQ false: the group-scale slot receives the block's float32 constant and
-// the 8-bit code load stays as an out-of-range dummy (it reads 0), so every
-// step issues the same number of memory operations and the explicit wait
-// counts hold for both formats.
+// (kDQ false: the group-scale slot receives the block's float32 constant and
+// there is no 8-bit code)
 template <bool kBwd, bool kDQ>
 __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, CodeRegs& r) {
   // forward: the block moves along the row (+32 B, +1 block per step);
@@ -264,8 +274,11 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<kBwd>& c, int step, Co
   const int64_t blk = c.blk0 + dblk;
   r.c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                         make_rsrc(c.g.codes, c.codes_bytes), c.code_voff, scode, 0));
-  r.code8 = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(c.g.code8, c.code8_bytes),
-                                                (kDQ && r.ok) ? (uint32_t)blk : kOOB, 0, 0);
+  if constexpr (kDQ)
+    r.code8 = __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(c.g.code8, c.code8_bytes),
+                                                  r.ok ? (uint32_t)blk : kOOB, 0, 0);
+  else
+    r.code8 = 0u;
   r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        make_rsrc(c.g.s2, c.s2_bytes),
                                        r.ok ? scale_offset<kDQ>(blk) : kOOB, 0, 0));
@@ -389,7 +402,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
     // loads, 5 in the others (a sweep of 3..7 found 5..7 alike, about 2 us
     // per step ahead of 4, and 3 behind)
     if (s == 0)
-      slice_schedule<8, kReads, kVmemPerStep>();
+      slice_schedule<8, kReads, vmem_per_step<kDQ>()>();
     else
       slice_schedule<5, kReads, 0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -409,7 +422,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx<kBwd>& c, int step, f32x
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(0);
-  barrier_keep_vmem<kVmemPerStep>();   // stage step+1 complete and visible
+  barrier_keep_vmem<vmem_per_step<kDQ>()>();   // stage step+1 complete and visible
   u32x4_t ga[4], gb[2];
   load_frags(c, as_next, bs_next, 0, ga, gb);
 #pragma unroll
@@ -639,10 +652,46 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
   const int l32 = c.l32, lhi = c.lhi, wm = c.wm;
   const int64_t m0 = c.m0, n0 = c.n0;
 
-  // ---- first loads: the activation stages and codes of steps 0 and 1 go out
-  // before the LoRA seed, so their latency overlaps the seed's own loads
-  // (waiting for the seed's operands then drains them too, which leaves the
-  // prologue barrier's count satisfied)
+  // ---- LoRA seed operands: acc = (s L) R^T over r (L is pre-scaled).  The
+  // 256 x 64 tiles of L (tokens m0 ..) and R (outputs n0 ..) for the first
+  // 64 of the r columns go by DMA into the two stages the prologue leaves
+  // idle (sa2, sb1), in the activation tile layout, ahead of the prologue's
+  // own loads: the seed then costs one memory round trip instead of one per
+  // 16 columns.  Rows past T or out_len lie past the range and read 0; the
+  // columns past r of a row are never read.  (The second reduction half of
+  // a split tile starts from zero and loads nothing.)
+  const int seed_r = half == 1 ? 0 : g.r;
+  uint16_t* const seed_l = sa2;
+  uint16_t* const seed_rt = sb1;
+  const int64_t outs_here = (out_len - c.n0) < BN ? (out_len - c.n0) : BN;
+  uint32_t seed_voff[2];
+  {
+    const int rl = c.lane >> 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = 8 * par + rl;
+      const int ch = (c.lane & 7) ^ swz_g(row);
+      seed_voff[par] = (uint32_t)((rl * g.r + 8 * ch) * 2);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t l_rsrc =
+      make_rsrc(g.lora_l + c.m0 * g.r, (uint32_t)(rows_here * g.r * 2));
+  const __amdgpu_buffer_rsrc_t r_rsrc =
+      make_rsrc(g.lora_r + c.n0 * g.r, (uint32_t)(outs_here * g.r * 2));
+  auto issue_seed = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kActLoads; ++i) {
+      const int blk8 = c.wave * kActLoads + i;
+      const uint32_t soff = (uint32_t)((blk8 * 8 * g.r + c0) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rsrc, (lds_void_t*)(seed_l + blk8 * 512), 16,
+                                               seed_voff[i & 1], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rsrc, (lds_void_t*)(seed_rt + blk8 * 512), 16,
+                                               seed_voff[i & 1], soff, 0, 0);
+    }
+  };
+  if (seed_r > 0) issue_seed(0);
+
+  // ---- first loads: the stages of steps 0 and 1 (and the codes of both)
   CodeRegs ca, cb;   // codes of even / odd steps
   if (kPreDq) {
     // weight ring A, activation ring B (see gemm_step_dma)
@@ -655,8 +704,9 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     issue_act(c, sa1, 1);
     issue_codes<kBwd, kDQ>(c, 1, cb);
   }
+  constexpr int kPrologueLoads = kPreDq ? 3 * kActLoads : 2 * vmem_per_step<kDQ>();
 
-  // ---- LoRA seed: acc = (s L) R^T over r (L is pre-scaled) -----------------
+  // ---- LoRA seed -----------------------------------------------------------
   f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -664,25 +714,36 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // (the second reduction half of a split tile starts from zero)
-  const int seed_r = half == 1 ? 0 : g.r;
-  for (int p0 = 0; p0 < seed_r; p0 += 16) {
-    const int p = p0 + 8 * lhi;
-    u32x4_t af[4], bf[2];
+  {
+    // forward-layout fragment offsets of R (the backward's weight fragments
+    // use another layout)
+    int rfrag[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = m0 + 128 * wm + 32 * i + l32;
-      af[i] = row < g.T ? ld_global16(g.lora_l + row * g.r + p) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int sl = 0; sl < 4; ++sl) rfrag[sl] = swz_a(col0 + l32, 2 * sl + lhi);
+    for (int c0 = 0; c0 < seed_r; c0 += BK) {
+      if (c0 == 0) {
+        barrier_keep_vmem<kPrologueLoads>();   // this wave's seed DMAs landed, and every wave's
+      } else {
+        __syncthreads();                       // every wave done reading the previous columns
+        issue_seed(c0);
+        barrier_keep_vmem<0>();
+      }
+      const int ns = (seed_r - c0) >= BK ? 4 : (seed_r - c0) >> 4;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < ns) {
+          u32x4_t af[4], bf[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) bf[j] = ld_lds16(seed_rt + rfrag[sl] + 32 * j * BK);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) af[i] = ld_lds16(seed_l + c.a_frag[sl] + 32 * i * BK);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(af[i], bf[j], acc[i][j]);
+        }
+      }
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + col0 + 32 * j + l32;
-      bf[j] = col < out_len ? ld_global16(g.lora_r + col * g.r + p) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<kF16>(af[i], bf[j], acc[i][j]);
   }
   if (kDrop && half != 1) {
     // the keep mask has one nibble per 4 tokens x 1 feature, exactly the 4
@@ -733,7 +794,7 @@ __global__ __launch_bounds__(kThreads, 1) void qlora_gemm_kernel(GemmArgs g) {
     for (int w = 0; w < 4; ++w) store_w(c, sb0, lut, ca, w);
   }
   // activation stage 0 (and the DMA'd weight stage 0) complete
-  barrier_keep_vmem<kPreDq ? kActLoads : kVmemPerStep>();
+  barrier_keep_vmem<kPreDq ? kActLoads : vmem_per_step<kDQ>()>();
 
   u32x4_t fa[2][4], fb[2][2];
   if (kPreDq)

@@ -20,6 +20,10 @@ CASES = [
     ("r128_T17_N272_K320", 17, 272, 320, 128, 16.0),
     ("r64_T520_N528_K576", 520, 528, 576, 64, 16.0),
     ("r48_T256_N256_K256", 256, 256, 256, 48, 96.0),
+    # ranks past one 64-column seed tile: a second, partial (80) or whole
+    # (128) tile of the adapter columns
+    ("r80_T300_N528_K320", 300, 528, 320, 80, 16.0),
+    ("r128_T300_N272_K576", 300, 272, 576, 128, 16.0),
     # more than 256 tiles with a last round at most half full: the forward
     # (270 tiles, 17 reduction steps) and the dX GEMM (261 tiles, 17 steps)
     # split their last 14 and 5 tiles into two reduction halves; ragged token
