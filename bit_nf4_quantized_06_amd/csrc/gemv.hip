@@ -117,8 +117,11 @@ __device__ __forceinline__ Nf4Lut make_lut_pair(float cp, const float kq[8]) {
 template <int TG, bool kLora>
 struct GemvStage {
   u32x4_t w[2][kLora ? 4 : 1];   // NF4: 16 code bytes per row group; A: 32 bf16
-  uint32_t c8[2];
-  float s2[2];
+  // block-constant inputs of row group `half` (lanes l and l + 32 hold the
+  // same row of each group, so each half loads one group's and the two
+  // halves exchange them)
+  uint32_t c8;
+  float s2;
   u32x4_t x[TG][4];              // 32 activations per token group
 };
 
@@ -137,8 +140,7 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
       kLora ? rsrc_v(g.A, (uint64_t)g.r * K * 2) : rsrc_v(g.codes, (uint64_t)(g.rows * K) >> 1);
   const __amdgpu_buffer_rsrc_t c8r = rsrc_v(g.code8, (uint64_t)(g.rows * kblocks));
   // without double quantisation the group-scale slot holds each block's
-  // float32 constant; the 8-bit code load then reads nothing (offset out of
-  // range) so both formats issue the same loads
+  // float32 constant and there is no 8-bit code to load
   const __amdgpu_buffer_rsrc_t s2r =
       rsrc_v(g.s2, kDQ ? (uint64_t)((g.rows * kblocks + 255) >> 8) * 4
                        : (uint64_t)(g.rows * kblocks) * 4);
@@ -174,12 +176,18 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
       } else {
         const int64_t blk = row[ng] * kblocks + st;
         s.w[ng][0] = load16(wr, v ? (uint32_t)(blk * 32 + 16 * half) : kOOBv);
-        s.c8[ng] = __builtin_amdgcn_raw_buffer_load_b8(c8r, (kDQ && v) ? (uint32_t)blk : kOOBv,
-                                                       0, 0);
-        s.s2[ng] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(
-                       s2r, v ? scale_offset<kDQ>(blk) : kOOBv, 0, 0));
       }
+    }
+    if (!kLora) {
+      const bool v = ok && row_ok[half];
+      const int64_t blk = row[half] * kblocks + st;
+      if (kDQ)
+        s.c8 = __builtin_amdgcn_raw_buffer_load_b8(c8r, v ? (uint32_t)blk : kOOBv, 0, 0);
+      else
+        s.c8 = 0u;
+      s.s2 = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(s2r, v ? scale_offset<kDQ>(blk) : kOOBv,
+                                                      0, 0));
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -204,6 +212,19 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
     for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
       for (int q = 0; q < 4; ++q) a[tg][q] = act_eo(cur.x[tg][q]);
+    // the block-constant inputs of both row groups: [0] from the lower
+    // half's lanes, [1] from the upper half's
+    uint32_t c8[2] = {0u, 0u};
+    float s2v[2] = {0.0f, 0.0f};
+    if (!kLora) {
+      const auto cx = __builtin_amdgcn_permlane32_swap(cur.c8, cur.c8, false, false);
+      const auto sx = __builtin_amdgcn_permlane32_swap(__float_as_uint(cur.s2),
+                                                       __float_as_uint(cur.s2), false, false);
+      c8[0] = cx[0];
+      c8[1] = cx[1];
+      s2v[0] = __uint_as_float(sx[0]);
+      s2v[1] = __uint_as_float(sx[1]);
+    }
 #pragma unroll
     for (int ng = 0; ng < 2; ++ng) {
       if (kLora) {
@@ -214,7 +235,7 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& g, int64_t n0, int64_t
           for (int tg = 0; tg < TG; ++tg) acc[tg][ng] = mfma32<kF16>(a[tg][q], b, acc[tg][ng]);
         }
       } else {
-        const float cp = weight_constant_or_zero<kDQ>(row_ok[ng], cur.c8[ng], cur.s2[ng], mu);
+        const float cp = weight_constant_or_zero<kDQ>(row_ok[ng], c8[ng], s2v[ng], mu);
         const Nf4Lut lt = make_lut_pair<kF16>(cp, kq);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
