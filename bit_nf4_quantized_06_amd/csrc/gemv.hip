@@ -30,7 +30,9 @@
 //    in LDS in a fixed order and stored as one split partial.
 // 2. qlora_gemv_finish_kernel.  U = sum of the A-tile partials (fixed order),
 //    stored as bf16 and, scaled by s, kept in LDS as bf16; the LoRA term
-//    (s U) B^T comes from MFMA 32x32x16 and Y = bf16(sum_s P + LoRA).
+//    (s U) B^T comes from MFMA 32x32x16 and Y = bf16(sum_s P + LoRA).  B and
+//    the first batch of W partials are requested before U's partials, so
+//    the kernel waits for one round trip where it waited for three.
 #include "abi_internal.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -316,10 +318,19 @@ __global__ __launch_bounds__(256) void qlora_gemv_partial_kernel(GemvArgs g, int
 }
 
 // Grid: ceil(rows / 128); wave w owns rows 128 blockIdx.x + 32 w .. + 31.
-template <int TG, bool kF16>
+// kHalf (T <= 16): only MFMA output rows 0..15 hold tokens, so only the
+// accumulator entries e < 8 are loaded and stored.  The LoRA operand B and
+// the first kBatch split partials are requested before U is reduced, so the
+// three independent load chains share one round trip.
+template <int TG, bool kF16, bool kHalf>
 __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
   // device pass only: the host pass needs just the signature (see the fused GEMM kernel)
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kE = kHalf ? 8 : 16;                          // accumulator entries in use
+  // splits per batch of W-partial and U-partial loads (16 at once with
+  // T <= 16 measured 1% slower on the 65B decode block than 8)
+  constexpr int kBatch = kHalf ? 8 : (TG == 1 ? 4 : 1);
+  constexpr int kUBatch = 8;
   __shared__ __attribute__((aligned(16))) uint16_t us[64 * 128];   // bf16(s U) [t][p]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,10 +339,58 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
   const int64_t N = g.rows, T = g.T;
   const int r = g.r;
   const int splits = g.splits;
+  const int64_t n = (int64_t)blockIdx.x * 128 + 32 * wave + (lane & 31);
+
+  // ---- requests that do not depend on U: B fragments, first partials -----
+  const __amdgpu_buffer_rsrc_t br = rsrc_v(g.B, (uint64_t)N * r * 2);
+  u32x4_t bfr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    bfr[j] = 16 * j < r ? load16(br, n < N ? (uint32_t)((n * r + 16 * j + 8 * half) * 2) : kOOBv)
+                        : u32x4_t{0u, 0u, 0u, 0u};
+  // rows past T are read from row T - 1 (loads stay unconditional) and
+  // never stored; rows past N read row N - 1
+  const int64_t nc = n < N ? n : N - 1;
+  int64_t off[TG][kE];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
+      off[tg][e] = (t < T ? t : T - 1) * N + nc;
+    }
+  float v[TG][kE];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int e = 0; e < kE; ++e) v[tg][e] = 0.0f;
+  auto load_batch = [&](int s0, float (&x)[kBatch][TG][kE]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int sc = s0 + i < splits ? s0 + i : splits - 1;
+      const float* ps = g.P + (int64_t)sc * T * N;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int e = 0; e < kE; ++e) x[i][tg][e] = ps[off[tg][e]];
+    }
+  };
+  // splits past the end read the last split and add 0 (the same sums, in
+  // split order, as one pass over all splits)
+  auto add_batch = [&](int s0, const float (&x)[kBatch][TG][kE]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int e = 0; e < kE; ++e) v[tg][e] += s0 + i < splits ? x[i][tg][e] : 0.0f;
+  };
+  float x0[kBatch][TG][kE];
+  load_batch(0, x0);
 
   // ---- U = sum over splits of the A-tile partials (fixed order) -----------
-  // 4 entries per thread and round, 8 splits per batch of loads; splits past
-  // the end read the last split and add 0.
+  // 4 entries per thread and round, kUBatch splits per batch of loads;
+  // splits past the end read the last split and add 0.
   const int64_t TR = T * r;
   for (int64_t e0 = 0; e0 < TR; e0 += 1024) {
     int64_t ei[4];
@@ -341,16 +400,16 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
       if (ei[j] >= TR) ei[j] = TR - 1;
     }
     float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-      float x[8][4];
+    for (int s0 = 0; s0 < splits; s0 += kUBatch) {
+      float x[kUBatch][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kUBatch; ++i) {
         const int sc = s0 + i < splits ? s0 + i : splits - 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[i][j] = g.PU[(int64_t)sc * TR + ei[j]];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kUBatch; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) u[j] += s0 + i < splits ? x[i][j] : 0.0f;
     }
@@ -366,60 +425,42 @@ __global__ __launch_bounds__(256) void qlora_gemv_finish_kernel(GemvArgs g) {
   }
   __syncthreads();
 
-  // ---- LoRA term (s U) B^T by MFMA, plus the W partials ----------------------
-  const int64_t n = (int64_t)blockIdx.x * 128 + 32 * wave + (lane & 31);
-  const __amdgpu_buffer_rsrc_t br = rsrc_v(g.B, (uint64_t)N * r * 2);
+  // ---- LoRA term (s U) B^T by MFMA -------------------------------------------
   f32x16_t acc[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[tg][e] = 0.0f;
-  for (int p0 = 0; p0 < r; p0 += 16) {
-    const int p = p0 + 8 * half;
-    const u32x4_t b = load16(br, n < N ? (uint32_t)((n * r + p) * 2) : kOOBv);
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      // token rows past T read stale table entries; they only reach output
-      // rows that are never stored
-      const int t = 32 * tg + (lane & 31);
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(us + t * r + p);
-      acc[tg] = mfma32<kF16>(a, b, acc[tg]);
+  for (int j = 0; j < 8; ++j) {
+    if (16 * j < r) {
+      const int p = 16 * j + 8 * half;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        // token rows past T read stale table entries; they only reach output
+        // rows that are never stored
+        const int t = 32 * tg + (lane & 31);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(us + t * r + p);
+        acc[tg] = mfma32<kF16>(a, bfr[j], acc[tg]);
+      }
     }
+  }
+
+  // ---- the W partials, then Y = bf16(sum_s P + LoRA) -------------------------
+  add_batch(0, x0);
+  for (int s0 = kBatch; s0 < splits; s0 += kBatch) {
+    float x[kBatch][TG][kE];
+    load_batch(s0, x);
+    add_batch(s0, x);
   }
   if (n >= N) return;
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    // rows past T are read from row T - 1 (loads stay unconditional) and
-    // never stored
-    int64_t off[16];
+  for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < kE; ++e) {
       const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
-      off[e] = (t < T ? t : T - 1) * N + n;
+      if (t < T) g.Y[t * N + n] = (uint16_t)(pack16x2<kF16>(v[tg][e] + acc[tg][e], 0.0f) & 0xFFFFu);
     }
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
-    for (int s0 = 0; s0 < splits; s0 += 4) {
-      float x[4][16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sc = s0 + i < splits ? s0 + i : splits - 1;
-        const float* ps = g.P + (int64_t)sc * T * N;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[i][e] = ps[off[e]];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] += s0 + i < splits ? x[i][e] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t t = 32 * tg + 8 * (e >> 2) + 4 * half + (e & 3);
-      if (t < T) g.Y[t * N + n] = (uint16_t)(pack16x2<kF16>(v[e] + acc[tg][e], 0.0f) & 0xFFFFu);
-    }
-  }
 #endif
 }
 
@@ -430,7 +471,16 @@ static hipError_t gemv_launch(const GemvArgs& a, dim3 grid, dim3 fgrid, int w_ti
                      w_tiles, per);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((qlora_gemv_finish_kernel<TG, kF16>), fgrid, dim3(256), 0, stream, a);
+  bool half_rows = false;
+  if constexpr (TG == 1) half_rows = a.T <= 16;
+  if constexpr (TG == 1) {
+    if (half_rows)
+      hipLaunchKernelGGL((qlora_gemv_finish_kernel<1, kF16, true>), fgrid, dim3(256), 0, stream,
+                         a);
+  }
+  if (!half_rows)
+    hipLaunchKernelGGL((qlora_gemv_finish_kernel<TG, kF16, false>), fgrid, dim3(256), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
