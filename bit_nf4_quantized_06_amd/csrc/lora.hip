@@ -331,6 +331,29 @@ __device__ void dequant_role(const ProjReduce& a, int64_t chunk) {
 // Workgroups [0, reduce_blocks): the split reduction; then `transpose_blocks`
 // transpose tiles; then the dequantisation chunks (a.dq_out set).  The roles
 // are independent, so one launch carries them all.
+// Fixed-order sum src[0] + src[stride] + ... over `splits` float32 quads:
+// loads go out 8 at a time (splits past the end re-read the last one), so up
+// to 8 splits cost one memory round trip; the padding adds -0, which leaves
+// every sum, signed zeros included, as the plain loop gives it.
+__device__ __forceinline__ f32x4_t sum_splits(const f32x4_t* src, int64_t stride, int splits) {
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    f32x4_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sc = s0 + j < splits ? s0 + j : splits - 1;
+      x[j] = src[(int64_t)sc * stride];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = s0 + j < splits;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += in ? x[j][e] : -0.0f;
+    }
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, TransposeJobs tj,
                                                                unsigned reduce_blocks,
                                                                unsigned transpose_blocks) {
@@ -349,19 +372,7 @@ __global__ __launch_bounds__(256) void lora_proj_reduce_kernel(ProjReduce a, Tra
   const int64_t t = i / a.r;
   const int p = (int)(i - t * a.r);
   f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (t < a.T) {
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.P + i);
-    const int64_t stride = a.T * a.r / 4;
-    int s = 0;
-    for (; s + 8 <= a.splits; s += 8) {
-      f32x4_t x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v += x[j];
-    }
-    for (; s < a.splits; ++s) v += src[(int64_t)s * stride];
-  }
+  if (t < a.T) v = sum_splits(reinterpret_cast<const f32x4_t*>(a.P + i), a.T * a.r / 4, a.splits);
   uint16_t b[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -624,26 +635,17 @@ hipError_t launch_lora_grad_partial(GradJobs jobs, int64_t T, int32_t r, int spl
 __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradJobs jobs, int r, int splits,
                                                                float scale) {
   int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  int jdx = 0;
-  while (jdx < jobs.n && i >= (int64_t)r * jobs.job[jdx].Q) {
-    i -= (int64_t)r * jobs.job[jdx].Q;
-    ++jdx;
-  }
-  if (jdx >= jobs.n) return;
-  const GradJob& jb = jobs.job[jdx];
-  const int64_t stride = (int64_t)r * jb.Q / 4;
-  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(jb.P + i);
-  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= splits; s += 8) {
-    f32x4_t x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(s + j) * stride];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v += x[j];
-  }
-  for (; s < splits; ++s) v += src[(int64_t)s * stride];
-  *reinterpret_cast<f32x4_t*>(jb.out + i) = v * scale;
+  // the job (at most two) by field-wise selects of the kernel arguments: no
+  // dynamically indexed copy of the argument struct in memory
+  const int64_t n0 = (int64_t)r * jobs.job[0].Q;
+  const bool second = i >= n0;
+  if (second) i -= n0;
+  if (second && (jobs.n < 2 || i >= (int64_t)r * jobs.job[1].Q)) return;
+  const int64_t Q = second ? jobs.job[1].Q : jobs.job[0].Q;
+  const float* P = second ? jobs.job[1].P : jobs.job[0].P;
+  float* out = second ? jobs.job[1].out : jobs.job[0].out;
+  const f32x4_t v = sum_splits(reinterpret_cast<const f32x4_t*>(P + i), (int64_t)r * Q / 4, splits);
+  *reinterpret_cast<f32x4_t*>(out + i) = v * scale;
 }
 
 hipError_t launch_lora_grad_reduce(GradJobs jobs, int32_t r, int splits, float scale,
