@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("T1_N16_K64_r16", 1, 16, 64, 16, 16.0),
     ("T16_N1040_K4096_r64", 16, 1040, 4096, 64, 16.0),     # ragged row tile, 4 splits
+    ("T17_N144_K1024_r16", 17, 144, 1024, 16, 16.0),       # first T past the finish's 16-row form
     ("T31_N272_K1088_r32", 31, 272, 1088, 32, 32.0),       # 17 blocks per row
     ("T33_N528_K576_r16", 33, 528, 576, 16, 32.0),         # two token groups
     ("T64_N256_K2048_r128", 64, 256, 2048, 128, 16.0),     # largest skinny T, largest r
