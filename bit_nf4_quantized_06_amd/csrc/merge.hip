@@ -130,20 +130,40 @@ struct MergeConsts {
   float s2[4];      // its group scale (float32 block constant without DQ)
 };
 
+// With double quantisation the tile's 4 blocks of a row are consecutive
+// blocks blk0 .. blk0 + 3: their 8-bit codes are 4 consecutive bytes, read
+// as the (at most) two aligned words that hold them, and they span at most
+// two groups, so two scale loads serve all four (4 loads instead of 8).  The
+// code array is 16-byte aligned and n_b (rows a multiple of 16) a multiple
+// of 16, so every aligned word below n_b lies inside it; blocks past the row
+// read the next row's bytes and feed only columns that are never stored.
 template <bool kDQ>
 __device__ __forceinline__ void merge_const_loads(const MergeArgs& a, int64_t nc, int64_t k0,
                                                   MergeConsts& m) {
+  if (kDQ) {
+    const int64_t n_b = (a.rows * a.cols) >> 6;
+    const int64_t blk0 = (nc * a.cols + k0) >> 6;
+    const int64_t w0 = blk0 & ~(int64_t)3;
+    const int64_t w1 = w0 + 4 < n_b ? w0 + 4 : w0;
+    const uint32_t lo = *reinterpret_cast<const uint32_t*>(a.code8 + w0);
+    const uint32_t hi = *reinterpret_cast<const uint32_t*>(a.code8 + w1);
+    const uint32_t bytes = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(blk0 & 3));
+    const int64_t g0 = blk0 >> 8;
+    const int64_t g1 = (blk0 + 3 < n_b ? blk0 + 3 : n_b - 1) >> 8;
+    const float s2a = a.s2[g0];
+    const float s2b = a.s2[g1];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    int64_t col = k0 + 64 * b;
-    col = col < a.cols ? col : a.cols - 64;
-    const int64_t blk = (nc * a.cols + col) >> 6;
-    if (kDQ) {
-      m.c8[b] = a.code8[blk];
-      m.s2[b] = a.s2[blk >> 8];
-    } else {
+    for (int b = 0; b < 4; ++b) {
+      m.c8[b] = (bytes >> (8 * b)) & 0xFFu;
+      m.s2[b] = ((blk0 + b) >> 8) == g0 ? s2a : s2b;
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int64_t col = k0 + 64 * b;
+      col = col < a.cols ? col : a.cols - 64;
       m.c8[b] = 0u;
-      m.s2[b] = a.s2[blk];
+      m.s2[b] = a.s2[(nc * a.cols + col) >> 6];
     }
   }
 }
