@@ -192,6 +192,10 @@ LINEAR = [
     ("bf16_nodq_T300_N1040_K1088_r16", 300, 1040, 1088, 16, 32.0, False, "bf16", None),
     ("fp16_dq_skinny_T16_N272_K320_r128", 16, 272, 320, 128, 16.0, True, "fp16", None),
     ("bf16_nodq_skinny_T40_N528_K1024_r64", 40, 528, 1024, 64, 16.0, False, "bf16", None),
+    # the skinny finish's 16-row form without double quantisation, and fp16
+    # with two token groups
+    ("bf16_nodq_skinny_T8_N144_K576_r32", 8, 144, 576, 32, 32.0, False, "bf16", None),
+    ("fp16_dq_skinny_T48_N160_K640_r16", 48, 160, 640, 16, 16.0, True, "fp16", None),
     ("fp16_nodq_dropout_T260_N272_K1024_r16", 260, 272, 1024, 16, 32.0, False, "fp16", 0.1),
     # K-split of the last round in both fused GEMMs (270 and 261 tiles), fp16
     # and float32 constants
